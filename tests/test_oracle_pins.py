@@ -1,0 +1,264 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: a
+pure-Python brute force, torch's float64 SDPA, a complex-number RoPE,
+hand-derived closed forms (tests/golden/closed_forms.json) or an invariant
+that the mathematics fixes.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, brute, joint_attention, rope_angles, rope_apply, softmax_probs
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")))
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _as4(x):
+    return np.asarray(x, np.float64)[None, None]
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("B,H,S,D,axes", [
+    (1, 2, 7, 8, (4, 4)),
+    (2, 1, 16, 6, (2, 2, 2)),
+    (1, 1, 3, 128, (16, 56, 56)),
+    (1, 1, 4, 128, (64, 64)),
+    (1, 1, 4, 128, (44, 42, 42)),
+])
+def test_brute_force_matches(B, H, S, D, axes):
+    rng = np.random.default_rng(S * 100 + D)
+    q, k, v = _rand(rng, B, H, S, D), _rand(rng, B, H, S, D), _rand(rng, B, H, S, D)
+    pos = rng.integers(0, 9, size=(S, len(axes)))
+    scale = 0.7 / math.sqrt(D) * 3
+    got = joint_attention(q, k, v, rope_angles(pos, axes, 10000.0), scale=scale)
+    want = np.array(brute.joint_attention(q.tolist(), k.tolist(), v.tolist(), pos.tolist(), axes, 10000.0, scale))
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+def test_brute_force_no_rope_default_scale():
+    rng = np.random.default_rng(5)
+    q, k, v = _rand(rng, 1, 2, 9, 12), _rand(rng, 1, 2, 9, 12), _rand(rng, 1, 2, 9, 5)
+    got = joint_attention(q, k, v)
+    want = np.array(brute.joint_attention(q.tolist(), k.tolist(), v.tolist()))
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+# ---------------------------------------------------------------- library routines
+
+@pytest.mark.parametrize("scale", [None, 0.3])
+def test_attention_matches_torch_sdpa_fp64(scale):
+    rng = np.random.default_rng(11)
+    q, k, v = _rand(rng, 2, 3, 37, 16), _rand(rng, 2, 3, 53, 16), _rand(rng, 2, 3, 53, 8)
+    got = attention(q, k, v, scale=scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=scale).numpy()
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_rope_matches_complex_rotation():
+    rng = np.random.default_rng(12)
+    S, axes = 40, (16, 56, 56)
+    pos = rng.integers(0, 128, size=(S, 3))
+    ang = rope_angles(pos, axes, 10000.0)
+    x = _rand(rng, 2, 3, S, 128)
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * ang)
+    want = np.empty_like(x)
+    want[..., 0::2], want[..., 1::2] = z.real, z.imag
+    assert np.max(np.abs(rope_apply(x, ang) - want)) <= 1e-12
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("case", ["attention_3key", "attention_uniform"])
+def test_golden_attention(case):
+    g = GOLDEN[case]
+    out = attention(_as4(g["q"]), _as4(g["k"]), _as4(g["v"]), scale=g["scale"])[0, 0]
+    assert np.max(np.abs(out - np.array(g["out"]))) <= 1e-12
+    if "probs" in g:
+        p = softmax_probs(_as4(g["q"]), _as4(g["k"]), g["scale"])[0, 0]
+        assert np.max(np.abs(p - np.array(g["probs"]))) <= 1e-15
+
+
+def test_golden_rope_angles():
+    g = GOLDEN["rope_angles"]
+    for c in g["cases"]:
+        ang = rope_angles(np.array([c["pos"]]), c["axes_dim"], g["theta"])
+        assert abs(ang[0, c["pair"]] - c["angle"]) <= 1e-12, c
+
+
+def test_golden_rope_rotation():
+    g = GOLDEN["rope_rotation"]
+    out = rope_apply(np.array([[g["x"]]]), np.array([[g["angle"]]]))
+    assert np.max(np.abs(out[0, 0] - np.array(g["out"]))) <= 1e-15
+
+
+# ---------------------------------------------------------------- invariants
+
+def _joint(rng, S=24, D=32, axes=(8, 12, 12), H=2):
+    q, k, v = _rand(rng, 1, H, S, D), _rand(rng, 1, H, S, D), _rand(rng, 1, H, S, D)
+    pos = rng.integers(0, 20, size=(S, len(axes)))
+    return q, k, v, pos, axes
+
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(20)
+    p = softmax_probs(_rand(rng, 1, 2, 17, 8) * 3, _rand(rng, 1, 2, 29, 8) * 3, 0.9)
+    assert np.max(np.abs(p.sum(-1) - 1.0)) <= 1e-14
+    assert np.all(p >= 0)
+
+
+def test_identical_keys_give_mean_of_v():
+    rng = np.random.default_rng(21)
+    q = _rand(rng, 1, 1, 6, 8)
+    k = np.repeat(_rand(rng, 1, 1, 1, 8), 10, axis=2)
+    v = _rand(rng, 1, 1, 10, 8)
+    out = attention(q, k, v)
+    assert np.max(np.abs(out - v.mean(axis=2, keepdims=True))) <= 1e-14
+    # with RoPE: all tokens at one position (text tokens) rotate identically
+    ang = rope_angles(np.zeros((10, 2), int), (4, 4), 10000.0)
+    out2 = joint_attention(_rand(rng, 1, 1, 10, 8), k, v, ang)
+    assert np.max(np.abs(out2 - v.mean(axis=2, keepdims=True))) <= 1e-14
+
+
+def test_scale_zero_gives_mean_of_v():
+    rng = np.random.default_rng(22)
+    q, k, v, pos, axes = _joint(rng)
+    out = joint_attention(q, k, v, rope_angles(pos, axes, 10000.0), scale=0.0)
+    assert np.max(np.abs(out - v.mean(axis=2, keepdims=True))) <= 1e-14
+
+
+def test_constant_v_gives_constant():
+    rng = np.random.default_rng(23)
+    q, k, v, pos, axes = _joint(rng)
+    v[:] = 0.625
+    out = joint_attention(q, k, v, rope_angles(pos, axes, 10000.0))
+    assert np.max(np.abs(out - 0.625)) <= 1e-14
+
+
+def test_single_token_returns_v():
+    rng = np.random.default_rng(24)
+    q, k, v = _rand(rng, 1, 3, 1, 128), _rand(rng, 1, 3, 1, 128), _rand(rng, 1, 3, 1, 128)
+    ang = rope_angles(np.array([[0, 7, 3]]), (16, 56, 56), 10000.0)
+    assert np.array_equal(joint_attention(q, k, v, ang), v)
+
+
+def test_joint_kv_permutation_leaves_output_unchanged():
+    rng = np.random.default_rng(25)
+    q, k, v = _rand(rng, 1, 2, 9, 16), _rand(rng, 1, 2, 31, 16), _rand(rng, 1, 2, 31, 16)
+    perm = rng.permutation(31)
+    a = attention(q, k, v)
+    b = attention(q, k[:, :, perm], v[:, :, perm])
+    assert np.max(np.abs(a - b)) <= 1e-13
+
+
+def test_token_permutation_with_positions_permutes_output():
+    rng = np.random.default_rng(26)
+    q, k, v, pos, axes = _joint(rng)
+    perm = rng.permutation(q.shape[2])
+    a = joint_attention(q, k, v, rope_angles(pos, axes, 10000.0))
+    b = joint_attention(q[:, :, perm], k[:, :, perm], v[:, :, perm], rope_angles(pos[perm], axes, 10000.0))
+    assert np.max(np.abs(a[:, :, perm] - b)) <= 1e-13
+
+
+def test_shift_invariance_with_overflowing_logits():
+    # adding the same vector c to every key adds q.c to a whole score row;
+    # softmax must not change even when q.c alone would overflow exp
+    rng = np.random.default_rng(27)
+    q, k, v = _rand(rng, 1, 1, 5, 8), _rand(rng, 1, 1, 12, 8), _rand(rng, 1, 1, 12, 8)
+    c = np.sign(q[0, 0].sum(0))[None, None, None, :] * 2000.0
+    a = attention(q, k, v)
+    b = attention(q, k + c, v)
+    assert np.all(np.isfinite(b))
+    assert np.max(np.abs(a - b)) <= 1e-9
+
+
+def test_lse_merge_of_key_halves_equals_whole():
+    rng = np.random.default_rng(28)
+    q, k, v = _rand(rng, 1, 2, 7, 16), _rand(rng, 1, 2, 40, 16), _rand(rng, 1, 2, 40, 16)
+    o, l = attention(q, k, v, return_lse=True)
+    o1, l1 = attention(q, k[:, :, :17], v[:, :, :17], return_lse=True)
+    o2, l2 = attention(q, k[:, :, 17:], v[:, :, 17:], return_lse=True)
+    m = np.maximum(l1, l2)
+    w1, w2 = np.exp(l1 - m)[..., None], np.exp(l2 - m)[..., None]
+    merged = (w1 * o1 + w2 * o2) / (w1 + w2)
+    assert np.max(np.abs(merged - o)) <= 1e-13
+    assert np.max(np.abs(m + np.log(np.exp(l1 - m) + np.exp(l2 - m)) - l)) <= 1e-13
+
+
+def test_linear_in_v():
+    rng = np.random.default_rng(29)
+    q, k = _rand(rng, 1, 1, 6, 8), _rand(rng, 1, 1, 11, 8)
+    v1, v2 = _rand(rng, 1, 1, 11, 8), _rand(rng, 1, 1, 11, 8)
+    a = attention(q, k, 2.5 * v1 - v2)
+    b = 2.5 * attention(q, k, v1) - attention(q, k, v2)
+    assert np.max(np.abs(a - b)) <= 1e-13
+
+
+def test_rope_position_zero_is_identity():
+    rng = np.random.default_rng(30)
+    x = _rand(rng, 1, 2, 5, 128)
+    ang = rope_angles(np.zeros((5, 3), int), (16, 56, 56), 10000.0)
+    assert np.array_equal(rope_apply(x, ang), x)
+
+
+def test_rope_preserves_pair_norms_and_composes():
+    rng = np.random.default_rng(31)
+    x = _rand(rng, 1, 1, 8, 128)
+    pa = rng.integers(0, 100, size=(8, 3))
+    pb = rng.integers(0, 100, size=(8, 3))
+    A, Bn = rope_angles(pa, (16, 56, 56), 10000.0), rope_angles(pb, (16, 56, 56), 10000.0)
+    y = rope_apply(x, A)
+    n0 = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    n1 = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    assert np.max(np.abs(n0 - n1)) <= 1e-12
+    # R(b) R(a) = R(a + b), and R(-a) undoes R(a)
+    assert np.max(np.abs(rope_apply(y, Bn) - rope_apply(x, A + Bn))) <= 1e-11
+    assert np.max(np.abs(rope_apply(y, -A) - x)) <= 1e-12
+    # angles are linear in position, so R(a + b) is the rotation at position pa + pb
+    assert np.max(np.abs(rope_angles(pa + pb, (16, 56, 56), 10000.0) - (A + Bn))) <= 1e-12
+
+
+@pytest.mark.parametrize("axis", [0, 1, 2])
+def test_shifting_all_positions_on_an_axis_leaves_output_unchanged(axis):
+    # <R_m q, R_n k> depends only on n - m
+    rng = np.random.default_rng(32 + axis)
+    q, k, v, pos, axes = _joint(rng, S=20, D=32, axes=(8, 12, 12))
+    shifted = pos.copy()
+    shifted[:, axis] += 37
+    a = joint_attention(q, k, v, rope_angles(pos, axes, 10000.0))
+    b = joint_attention(q, k, v, rope_angles(shifted, axes, 10000.0))
+    assert np.max(np.abs(a - b)) <= 1e-12
+
+
+def test_row_sampling_matches_full():
+    rng = np.random.default_rng(33)
+    q, k, v, pos, axes = _joint(rng, S=30)
+    ang = rope_angles(pos, axes, 10000.0)
+    full = joint_attention(q, k, v, ang)
+    rows = np.array([0, 7, 29, 12])
+    # BLAS may sum a row subset in another order: agree to rounding
+    assert np.max(np.abs(joint_attention(q, k, v, ang, rows=rows) - full[:, :, rows])) <= 1e-14
+
+
+def test_oracle_catches_planted_sign_error():
+    # a plausible mistake (wrong sign on sin) must fail the complex-rotation pin
+    rng = np.random.default_rng(34)
+    x = _rand(rng, 1, 1, 6, 16)
+    ang = rope_angles(rng.integers(1, 9, size=(6, 2)), (8, 8), 10000.0)
+    c, s = np.cos(ang), np.sin(ang)
+    bad = np.empty_like(x)
+    bad[..., 0::2] = x[..., 0::2] * c + x[..., 1::2] * s
+    bad[..., 1::2] = -x[..., 0::2] * s + x[..., 1::2] * c
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * ang)
+    assert np.max(np.abs(bad[..., 0::2] - z.real)) > 1e-3
+    assert np.max(np.abs(rope_apply(x, ang)[..., 0::2] - z.real)) <= 1e-12
