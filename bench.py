@@ -1,0 +1,187 @@
+"""Benchmark: joint self-attention TFLOP/s on one MI355X.
+
+One step = one whole pass of the path over one batch of synthetic input:
+RoPE on K + tile preparation (dit_attn_prepare_kv) and the attention kernel
+with RoPE on Q fused into its prologue (dit_attn_core), i.e. the work of
+dit_attn_forward.  RoPE tables are built once per resolution (outside the
+step), as a DiT reuses them across all blocks and denoising steps.
+
+Prints one JSON line.  `value` is attention TFLOP/s (4 B H S^2 D flop per
+step) over the timed steps; `roofline` prices the attention kernel alone
+against the dense bf16 MFMA peak; `cpu_baseline` times the float64 oracle on
+a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+import dit_workloads as W
+
+METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=16896,H=24,D=128 (1 GPU)"
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux2048", choices=[n for n in W.WORKLOADS if "fp8" not in n])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def bf16_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def cpu_baseline(w, qb, kb, vb, budget_s):
+    """The float64 oracle as it stands, on the first query rows of successive
+    heads until the time budget is spent; TFLOP/s at 4 * rows * S * D flop."""
+    from oracle import joint_attention, rope_angles
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
+    rows_per_head = min(w.S, 2048)
+    rows = np.arange(rows_per_head)
+    t0 = time.perf_counter()
+    done_rows = 0
+    heads = 0
+    for h in range(w.H):
+        sl = slice(h, h + 1)
+        q = W.bf16_bits_to_f32(qb[:, sl]).astype(np.float64)
+        k = W.bf16_bits_to_f32(kb[:, sl]).astype(np.float64)
+        v = W.bf16_bits_to_f32(vb[:, sl]).astype(np.float64)
+        joint_attention(q, k, v, ang, rows=rows)
+        done_rows += rows_per_head
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * done_rows * w.S * w.D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: first {rows_per_head} query rows x {heads} of {w.H} heads vs all {w.S} keys, "
+                      f"float64 numpy (incl. RoPE of the head's K), {dt:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dit_joint_self_amd as dj
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = W.get(args.workload)
+    print(f"[bench] workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D}", file=sys.stderr, flush=True)
+    qb, kb, vb = W.make_bf16_inputs(w)
+    q, k, v = bf16_dev(qb, torch), bf16_dev(kb, torch), bf16_dev(vb, torch)
+    pos = torch.from_numpy(W.positions(w)).to("cuda")
+    cos, sin = dj.dit_rope_tables(pos, w.axes_dim, w.theta)
+    out = torch.empty_like(q)
+    ws_bytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(w.D)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dj.dit_attn_prepare_kv(k, v, cos, sin, ws, ws_bytes, stream=stream)
+        dj.dit_attn_core(q, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        dj.dit_attn_prepare_kv(k, v, cos, sin, ws, ws_bytes, stream=stream)
+        ev[i][1].record(stream)
+        dj.dit_attn_core(q, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes, stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    core_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
+
+    # dit_attn_forward itself (allocating its workspace from the stream pool), for reference.
+    for _ in range(2):
+        dj.dit_attn_forward(q, k, v, cos, sin, out=out, S_txt=w.S_txt, scale=scale)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        dj.dit_attn_forward(q, k, v, cos, sin, out=out, S_txt=w.S_txt, scale=scale)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / K
+
+    # Spot parity of the timed output against the oracle (a few rows of head 0).
+    from oracle import joint_attention, rope_angles
+    rows = np.array([0, 1, w.S_txt - 1, w.S_txt, w.S // 2, w.S - 1])
+    ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
+    ref = joint_attention(W.bf16_bits_to_f32(qb[:, :1]).astype(np.float64),
+                          W.bf16_bits_to_f32(kb[:, :1]).astype(np.float64),
+                          W.bf16_bits_to_f32(vb[:, :1]).astype(np.float64), ang, rows=rows)
+    got_bits = out[:, :1, torch.from_numpy(rows).to("cuda")].cpu().view(torch.int16).numpy().view(np.uint16)
+    spot_err = float(np.abs(W.bf16_bits_to_f32(got_bits) - ref).max())
+
+    flops = w.flops
+    core_avg = float(np.mean(core_ms))
+    prep_avg = float(np.mean(prep_ms))
+    achieved = flops / (core_avg * 1e-3) / 1e12
+    tensor_bytes = w.B * w.H * w.S * w.D * 2
+    prep_bytes = 4 * tensor_bytes + 2 * w.S * (w.D // 2) * 4  # read K, V, cos, sin; write 2 tensors of tiles
+    rec = {
+        "metric": METRIC,
+        "value": flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S_txt": w.S_txt, "S_img": w.S_img, "S": w.S,
+                   "D": w.D, "rope_axes": list(w.axes_dim), "non_causal": True},
+        "pct_of_bf16_peak": 100.0 * flops / (step_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "attn_core_kernel", "achieved": achieved,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": None, "avg_ms": core_avg},
+        "stages_ms": {"prepare_kv": prep_avg, "attn_core": core_avg,
+                      "prepare_kv_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9},
+        "forward_ms": fwd_ms,
+        "wall_s": wall,
+        "spot_parity_max_abs": spot_err,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+"""Thin Python binding of libditattn.so (MI355X / gfx950 joint self-attention).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Functions keep the C names (``dit_attn_forward``, ``dit_rope_tables``,
+``dit_attn_workspace_bytes``, ``dit_attn_prepare_kv``, ``dit_attn_core``) and
+take torch tensors (their device pointers are passed) or plain integers as
+pointers.  A missing library raises ``RuntimeError``: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "LIB_PATH", "DitAttnError", "lib", "lib_loaded", "dit_last_error", "dit_abi_version",
+    "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_kv",
+    "dit_attn_core", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
+    "DIT_ERR_NO_DEVICE", "DIT_ERR_OUT_OF_MEMORY", "DIT_ERR_LAUNCH", "DIT_DTYPE_BF16",
+    "DIT_DTYPE_FP8_E4M3",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
+
+DIT_DTYPE_BF16 = 0
+DIT_DTYPE_FP8_E4M3 = 1
+
+DIT_OK = 0
+DIT_ERR_INVALID_ARG = 1
+DIT_ERR_UNSUPPORTED = 2
+DIT_ERR_NO_DEVICE = 3
+DIT_ERR_OUT_OF_MEMORY = 4
+DIT_ERR_LAUNCH = 5
+
+_STATUS_NAMES = {0: "DIT_OK", 1: "DIT_ERR_INVALID_ARG", 2: "DIT_ERR_UNSUPPORTED", 3: "DIT_ERR_NO_DEVICE",
+                 4: "DIT_ERR_OUT_OF_MEMORY", 5: "DIT_ERR_LAUNCH"}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+# name -> (restype, argtypes); the same set include/dit_attn.h declares.
+_SIGNATURES = {
+    "dit_last_error": (ctypes.c_char_p, []),
+    "dit_abi_version": (_I, []),
+    "dit_rope_tables": (_I, [_P, _I, _I, ctypes.POINTER(ctypes.c_int32), _F, _P, _P, _P]),
+    "dit_attn_forward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "dit_attn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "dit_attn_prepare_kv": (_I, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P]),
+    "dit_attn_core": (_I, [_P, _P, _P, _P, ctypes.c_size_t, _P, _I, _I, _I, _I, _F, _P]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+class DitAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use); raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "or `python dit_joint_self_amd/build.py`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def lib_loaded() -> bool:
+    return _lib is not None
+
+
+def _ptr(x) -> Optional[int]:
+    """Device pointer of a tensor, an int pointer, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int) -> None:
+    if status != DIT_OK:
+        raise DitAttnError(status, dit_last_error())
+
+
+def dit_last_error() -> str:
+    return lib().dit_last_error().decode()
+
+
+def dit_abi_version() -> int:
+    return lib().dit_abi_version()
+
+
+def dit_rope_tables(pos, axes_dim: Sequence[int], theta: float, rope_cos=None, rope_sin=None, stream=None):
+    """cos/sin tables [S, D/2] fp32 from int32 positions [S, n_axes] on the device.
+
+    Allocates the outputs when not given; returns (rope_cos, rope_sin).
+    """
+    import torch
+    S, n_axes = int(pos.shape[0]), int(pos.shape[1])
+    half = sum(int(a) for a in axes_dim) // 2
+    if rope_cos is None:
+        rope_cos = torch.empty((S, half), dtype=torch.float32, device=pos.device)
+    if rope_sin is None:
+        rope_sin = torch.empty((S, half), dtype=torch.float32, device=pos.device)
+    dims = (ctypes.c_int32 * len(axes_dim))(*[int(a) for a in axes_dim])
+    _check(lib().dit_rope_tables(_ptr(pos), S, n_axes, dims, float(theta), _ptr(rope_cos), _ptr(rope_sin),
+                                 _stream(stream)))
+    return rope_cos, rope_sin
+
+
+def dit_attn_forward(q, k, v, rope_cos=None, rope_sin=None, out=None, S_txt: int = 0, S_img: Optional[int] = None,
+                     scale: Optional[float] = None, dtype: int = DIT_DTYPE_BF16, stream=None):
+    """Joint self-attention with RoPE on Q/K: q, k, v bf16 [B, H, S, D] on the device.
+
+    S_img defaults to S - S_txt; scale defaults to 1/sqrt(D).  Returns ``out``.
+    """
+    import torch
+    B, H, S, D = (int(s) for s in q.shape)
+    if S_img is None:
+        S_img = S - S_txt
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().dit_attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(rope_cos), _ptr(rope_sin), _ptr(out),
+                                  B, H, S_txt, S_img, D, float(scale), int(dtype), _stream(stream)))
+    return out
+
+
+def dit_attn_workspace_bytes(B: int, H: int, S: int, D: int) -> int:
+    return int(lib().dit_attn_workspace_bytes(B, H, S, D))
+
+
+def dit_attn_prepare_kv(k, v, rope_cos, rope_sin, workspace, workspace_bytes: Optional[int] = None, stream=None):
+    B, H, S, D = (int(s) for s in k.shape)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().dit_attn_prepare_kv(_ptr(k), _ptr(v), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace),
+                                     int(workspace_bytes), B, H, S, D, _stream(stream)))
+
+
+def dit_attn_core(q, rope_cos, rope_sin, workspace, out, scale: Optional[float] = None,
+                  workspace_bytes: Optional[int] = None, stream=None):
+    B, H, S, D = (int(s) for s in q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().dit_attn_core(_ptr(q), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace), int(workspace_bytes),
+                               _ptr(out), B, H, S, D, float(scale), _stream(stream)))
+    return out

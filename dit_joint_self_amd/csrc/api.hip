@@ -1,0 +1,241 @@
+// api.hip - host side of libditattn.so: argument validation, device checks,
+// workspace management and kernel launches on the caller's stream.
+//
+// Every argument is checked before the first HIP call, so a bad call never
+// touches the device.  Errors are reported as dit_status_t plus a
+// thread-local message; no exception leaves this file.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "dit_attn.h"
+#include "tile_layout.h"
+
+namespace dit {
+hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, const float* sin_t,
+                             void* ws, int BH, int S, hipStream_t stream);
+hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws,
+                            void* out, int BH, int S, float qmul, hipStream_t stream);
+hipError_t launch_rope_tables(const int32_t* pos, int S, int n_axes, const int32_t* axes_dim,
+                              double theta, float* cos_t, float* sin_t, hipStream_t stream);
+int core_block_m();
+}  // namespace dit
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxDevices = 64;
+// Smallest query tile any kernel variant uses; bounds the workgroup count.
+constexpr int kMinBlockM = 128;
+
+thread_local char g_err[512] = "";
+
+dit_status_t fail(dit_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+dit_status_t ok() {
+    g_err[0] = '\0';
+    return DIT_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// Host-only checks shared by the attention entry points.
+dit_status_t check_shape(int B, int H, int S, int D) {
+    if (B < 1 || H < 1) return fail(DIT_ERR_INVALID_ARG, "B and H must be >= 1 (got B=%d H=%d)", B, H);
+    if (S < 1) return fail(DIT_ERR_INVALID_ARG, "S must be >= 1 (got %d)", S);
+    if (D < 1) return fail(DIT_ERR_INVALID_ARG, "D must be >= 1 (got %d)", D);
+    if (D != dit::HEAD_DIM) return fail(DIT_ERR_UNSUPPORTED, "only D = 128 is implemented (got %d)", D);
+    const int64_t wgs = (int64_t)B * H * ((S + kMinBlockM - 1) / kMinBlockM);
+    const int64_t tiles = (int64_t)B * H * dit::num_kv_tiles(S);
+    if (wgs > INT_MAX || tiles > INT_MAX || (int64_t)B * H > 65535)
+        return fail(DIT_ERR_INVALID_ARG, "B*H*S too large for one launch (B=%d H=%d S=%d)", B, H, S);
+    return DIT_OK;
+}
+
+dit_status_t check_rope(const float* c, const float* s) {
+    if ((c == nullptr) != (s == nullptr))
+        return fail(DIT_ERR_INVALID_ARG, "rope_cos and rope_sin must both be NULL or both non-NULL");
+    if (c && (!aligned16(c) || !aligned16(s)))
+        return fail(DIT_ERR_INVALID_ARG, "rope tables must be 16-byte aligned");
+    return DIT_OK;
+}
+
+// Device present and gfx950; the result is cached per device ordinal.
+dit_status_t check_device() {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return fail(DIT_ERR_NO_DEVICE, "no HIP device is visible");
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(DIT_ERR_NO_DEVICE, "hipGetDevice failed");
+    static std::mutex mu;
+    static signed char arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+    if (dev < 0 || dev >= kMaxDevices) return fail(DIT_ERR_NO_DEVICE, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (arch_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(DIT_ERR_NO_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+        arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        if (arch_ok[dev] < 0)
+            return fail(DIT_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev,
+                        prop.gcnArchName);
+        // Keep freed workspace in the stream-ordered pool between calls.
+        hipMemPool_t pool;
+        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+            uint64_t keep = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        }
+    }
+    if (arch_ok[dev] < 0) return fail(DIT_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return DIT_OK;
+}
+
+dit_status_t launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(DIT_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dit_last_error(void) { return g_err; }
+
+int dit_abi_version(void) { return kAbiVersion; }
+
+dit_status_t dit_rope_tables(const int32_t* pos, int S, int n_axes, const int32_t* axes_dim, float theta,
+                             float* rope_cos, float* rope_sin, void* stream) {
+    if (!pos || !axes_dim || !rope_cos || !rope_sin)
+        return fail(DIT_ERR_INVALID_ARG, "pos, axes_dim, rope_cos and rope_sin must be non-NULL");
+    if (S < 1) return fail(DIT_ERR_INVALID_ARG, "S must be >= 1 (got %d)", S);
+    if (n_axes < 1 || n_axes > 4) return fail(DIT_ERR_INVALID_ARG, "n_axes must be 1..4 (got %d)", n_axes);
+    int64_t D = 0;
+    for (int a = 0; a < n_axes; ++a) {
+        if (axes_dim[a] < 2 || (axes_dim[a] & 1))
+            return fail(DIT_ERR_INVALID_ARG, "axes_dim[%d] = %d must be even and >= 2", a, axes_dim[a]);
+        D += axes_dim[a];
+    }
+    if (!(theta > 0.0f) || !std::isfinite(theta))
+        return fail(DIT_ERR_INVALID_ARG, "theta must be finite and > 0");
+    if ((int64_t)S * (D / 2) > (int64_t)INT_MAX * 256)
+        return fail(DIT_ERR_INVALID_ARG, "S * D/2 too large");
+    if (!aligned16(rope_cos) || !aligned16(rope_sin))
+        return fail(DIT_ERR_INVALID_ARG, "rope tables must be 16-byte aligned");
+    if (overlaps(rope_cos, (size_t)S * (D / 2) * 4, rope_sin, (size_t)S * (D / 2) * 4))
+        return fail(DIT_ERR_INVALID_ARG, "rope_cos and rope_sin overlap");
+    dit_status_t st = check_device();
+    if (st != DIT_OK) return st;
+    return launched(dit::launch_rope_tables(pos, S, n_axes, axes_dim, (double)theta, rope_cos, rope_sin,
+                                            static_cast<hipStream_t>(stream)),
+                    "rope_tables_kernel");
+}
+
+size_t dit_attn_workspace_bytes(int B, int H, int S, int D) {
+    if (B < 1 || H < 1 || S < 1 || D != dit::HEAD_DIM) return 0;
+    return (size_t)B * H * (size_t)dit::num_kv_tiles(S) * dit::TILE_BYTES;
+}
+
+dit_status_t dit_attn_prepare_kv(const void* k, const void* v, const float* rope_cos, const float* rope_sin,
+                                 void* workspace, size_t workspace_bytes, int B, int H, int S, int D,
+                                 void* stream) {
+    if (!k || !v || !workspace) return fail(DIT_ERR_INVALID_ARG, "k, v and workspace must be non-NULL");
+    dit_status_t st = check_shape(B, H, S, D);
+    if (st != DIT_OK) return st;
+    if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
+    if (!aligned16(k) || !aligned16(v)) return fail(DIT_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(DIT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t need = dit_attn_workspace_bytes(B, H, S, D);
+    if (workspace_bytes < need)
+        return fail(DIT_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+    const size_t tbytes = (size_t)B * H * S * D * 2;
+    if (overlaps(workspace, need, k, tbytes) || overlaps(workspace, need, v, tbytes))
+        return fail(DIT_ERR_INVALID_ARG, "workspace overlaps k or v");
+    if ((st = check_device()) != DIT_OK) return st;
+    return launched(dit::launch_prepare_kv(k, v, rope_cos, rope_sin, workspace, B * H, S,
+                                           static_cast<hipStream_t>(stream)),
+                    "prepare_kv_kernel");
+}
+
+dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin, const void* workspace,
+                           size_t workspace_bytes, void* out, int B, int H, int S, int D, float scale,
+                           void* stream) {
+    if (!q || !workspace || !out) return fail(DIT_ERR_INVALID_ARG, "q, workspace and out must be non-NULL");
+    dit_status_t st = check_shape(B, H, S, D);
+    if (st != DIT_OK) return st;
+    if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
+    if (!std::isfinite(scale)) return fail(DIT_ERR_INVALID_ARG, "scale must be finite");
+    if (!aligned16(q) || !aligned16(out)) return fail(DIT_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+    const size_t need = dit_attn_workspace_bytes(B, H, S, D);
+    if (workspace_bytes < need)
+        return fail(DIT_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+    const size_t tbytes = (size_t)B * H * S * D * 2;
+    if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, workspace, need))
+        return fail(DIT_ERR_INVALID_ARG, "out overlaps q or the workspace");
+    if ((st = check_device()) != DIT_OK) return st;
+    const float qmul = (float)((double)scale * 1.4426950408889634073599);  // scale * log2(e)
+    return launched(dit::launch_attn_core(q, rope_cos, rope_sin, workspace, out, B * H, S, qmul,
+                                          static_cast<hipStream_t>(stream)),
+                    "attn_core_kernel");
+}
+
+dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const float* rope_cos,
+                              const float* rope_sin, void* out, int B, int H, int S_txt, int S_img, int D,
+                              float scale, dit_dtype_t dtype, void* stream) {
+    if (!q || !k || !v || !out) return fail(DIT_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+    if (S_txt < 0 || S_img < 0)
+        return fail(DIT_ERR_INVALID_ARG, "S_txt and S_img must be >= 0 (got %d, %d)", S_txt, S_img);
+    if ((int64_t)S_txt + S_img > INT_MAX) return fail(DIT_ERR_INVALID_ARG, "S_txt + S_img overflows int");
+    const int S = S_txt + S_img;
+    dit_status_t st = check_shape(B, H, S, D);
+    if (st != DIT_OK) return st;
+    if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
+    if (dtype == DIT_DTYPE_FP8_E4M3)
+        return fail(DIT_ERR_UNSUPPORTED, "fp8 inputs are not taken by dit_attn_forward");
+    if (dtype != DIT_DTYPE_BF16) return fail(DIT_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (!std::isfinite(scale)) return fail(DIT_ERR_INVALID_ARG, "scale must be finite");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(DIT_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    const size_t tbytes = (size_t)B * H * S * D * 2;
+    if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) || overlaps(out, tbytes, v, tbytes))
+        return fail(DIT_ERR_INVALID_ARG, "out overlaps an input");
+    if ((st = check_device()) != DIT_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t need = dit_attn_workspace_bytes(B, H, S, D);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, need, s) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return fail(DIT_ERR_OUT_OF_MEMORY, "hipMallocAsync of %zu workspace bytes failed", need);
+    }
+    hipError_t e = dit::launch_prepare_kv(k, v, rope_cos, rope_sin, ws, B * H, S, s);
+    if (e == hipSuccess) {
+        const float qmul = (float)((double)scale * 1.4426950408889634073599);
+        e = dit::launch_attn_core(q, rope_cos, rope_sin, ws, out, B * H, S, qmul, s);
+    }
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess) return launched(e, "dit_attn_forward kernels");
+    return launched(ef, "hipFreeAsync of the workspace");
+}
+
+}  // extern "C"

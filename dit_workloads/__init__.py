@@ -113,10 +113,21 @@ def draw_qkv_f32(w: Workload):
 
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
-    Inputs here are finite, so no NaN handling."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    bias = ((b >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((b + bias) >> 16).astype(np.uint16)
+    Inputs here are finite, so no NaN handling.  Works in place on slices of
+    a copy so full-size workloads round in a couple of seconds."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    step = 1 << 22
+    for i in range(0, flat.size, step):
+        b = flat[i:i + step].view(np.uint32).copy()
+        bias = b >> 16
+        bias &= np.uint32(1)
+        bias += np.uint32(0x7FFF)
+        b += bias
+        b >>= 16
+        out[i:i + step] = b
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -1,0 +1,143 @@
+/*
+ * dit_attn.h - C ABI of libditattn.so: non-causal joint self-attention of a
+ * diffusion-transformer block on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The xDiT paper ("xDiT: an Inference Engine for Diffusion
+ * Transformers (DiTs) with Massive Parallelism", abstract) names attention over
+ * the long image/video token sequence of a DiT as the cost that grows with
+ * resolution, and the AMD blog "How to Scale Diffusion Inference Across AMD
+ * RDNA 4 GPUs" (section on Ulysses sequence parallelism) describes each GPU
+ * running full-sequence attention for its share of the heads.  For every batch
+ * b and head h this library computes, over the joint sequence of S = S_txt +
+ * S_img tokens (text rows first, then the patchified latent rows):
+ *
+ *     q' = RoPE(q), k' = RoPE(k)                  (interleaved pairs, see below)
+ *     out = softmax(scale * q' k'^T) v            (no mask, every row sees every key)
+ *
+ * The softmax is evaluated in the streaming form of FlashAttention-2 (cited in
+ * the xDiT paper's reference list): exact up to floating-point rounding.
+ *
+ * RoPE.  Pair j of a head vector is the dims (2j, 2j+1), rotated as the complex
+ * number x[2j] + i x[2j+1] times exp(i * phi[s][j]), with cos(phi) and sin(phi)
+ * supplied as fp32 tables of shape [S, D/2].  dit_rope_tables() builds them
+ * from integer token coordinates with per-axis frequencies theta^(-2i/d_a).
+ *
+ * Conventions shared by every entry point.
+ *   - Tensor pointers are DEVICE memory owned by the caller; the library keeps
+ *     no pointer after returning.  Layout is contiguous [B, H, S, D] (bf16),
+ *     16-byte aligned.  `out` must not overlap any input.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued on it; DIT_OK means "enqueued", not "finished".
+ *   - Every argument is validated on the host BEFORE any HIP call; a bad
+ *     argument returns its status and enqueues nothing.  No exception crosses
+ *     the ABI.  dit_last_error() returns a thread-local message for the last
+ *     non-OK status of the calling thread.
+ *   - D must be 128 (DIT_ERR_UNSUPPORTED otherwise).  Index arithmetic is
+ *     64-bit; B*H*ceil(S/256) must fit in a signed 32-bit int.
+ *   - NaN/Inf inputs propagate to the output; they are not trapped.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DIT_DTYPE_BF16 = 0,
+    DIT_DTYPE_FP8_E4M3 = 1
+} dit_dtype_t;
+
+typedef enum {
+    DIT_OK = 0,
+    DIT_ERR_INVALID_ARG = 1,   /* NULL, misaligned, negative or inconsistent argument */
+    DIT_ERR_UNSUPPORTED = 2,   /* valid but not implemented (D != 128, dtype) */
+    DIT_ERR_NO_DEVICE = 3,     /* no usable HIP device */
+    DIT_ERR_OUT_OF_MEMORY = 4, /* workspace allocation failed */
+    DIT_ERR_LAUNCH = 5         /* a HIP call or kernel launch reported an error */
+} dit_status_t;
+
+/* Thread-local message describing the last non-OK status ("" if none). */
+const char* dit_last_error(void);
+
+/* Version of this ABI; bumped when a signature or layout changes. */
+int dit_abi_version(void);
+
+/*
+ * dit_rope_tables - cos/sin tables of multi-axis RoPE.
+ *
+ * The pages name RoPE'd DiTs (FLUX, Wan) but never write RoPE out; the form
+ * used here is the plainest multi-axis reading: the head's D = sum(axes_dim)
+ * dims are split into consecutive per-axis blocks; local pair i of axis a has
+ * frequency theta^(-2i/axes_dim[a]); its angle at token s is
+ * pos[s][a] * frequency.  Angles, cos and sin are evaluated in fp64 on the
+ * device and stored rounded to fp32.
+ *
+ *   pos        device int32 [S, n_axes]: token coordinates (text tokens 0).
+ *   S          number of tokens, >= 1.
+ *   n_axes     1..4.
+ *   axes_dim   HOST int32 [n_axes]: even, positive; sum = D (any even D).
+ *   theta      base frequency, > 0 (10000 for the FLUX/Wan-style shapes).
+ *   rope_cos, rope_sin  device fp32 [S, D/2] outputs, 16-byte aligned.
+ */
+dit_status_t dit_rope_tables(const int32_t* pos, int S, int n_axes, const int32_t* axes_dim,
+                             float theta, float* rope_cos, float* rope_sin, void* stream);
+
+/*
+ * dit_attn_forward - the whole path: RoPE on Q and K, then joint attention.
+ *
+ *   q, k, v    device bf16 [B, H, S, D], S = S_txt + S_img (S_txt, S_img >= 0, S >= 1).
+ *   rope_cos, rope_sin  device fp32 [S, D/2], shared by all (b, h); both NULL
+ *              means no RoPE; exactly one NULL is DIT_ERR_INVALID_ARG.
+ *   out        device bf16 [B, H, S, D], written in full.
+ *   scale      softmax scale (normally 1/sqrt(D)); finite.
+ *   dtype      must be DIT_DTYPE_BF16 (fp8 has its own entry point).
+ *
+ * Rounding: rotated K is rounded to bf16 (RNE); rotated Q is multiplied by
+ * scale*log2(e) in fp32 and rounded to bf16; QK^T and PV accumulate in fp32
+ * on the matrix cores; softmax state is fp32; P is rounded to bf16 for PV;
+ * the output is rounded to bf16 (RNE).
+ *
+ * A workspace of dit_attn_workspace_bytes() is taken from the stream-ordered
+ * allocator (hipMallocAsync/hipFreeAsync on `stream`), so calls on different
+ * streams do not share it.  Allocation failure returns DIT_ERR_OUT_OF_MEMORY.
+ */
+dit_status_t dit_attn_forward(const void* q, const void* k, const void* v,
+                              const float* rope_cos, const float* rope_sin, void* out,
+                              int B, int H, int S_txt, int S_img, int D,
+                              float scale, dit_dtype_t dtype, void* stream);
+
+/*
+ * The two stages of dit_attn_forward, for callers that own the workspace
+ * (for example, to reuse one workspace across layers, or to time the stages).
+ * dit_attn_forward(...) == prepare_kv then core, on one workspace.
+ *
+ * dit_attn_workspace_bytes  bytes needed for B, H, S, D (0 on invalid sizes).
+ *
+ * dit_attn_prepare_kv  rotates K (bf16 RNE) and re-lays K and V out into the
+ *   workspace in the tile order the attention kernel streams.  The workspace
+ *   layout is private to this library and may change between versions.
+ *   workspace: device, 256-byte aligned, >= dit_attn_workspace_bytes(B,H,S,D).
+ *
+ * dit_attn_core  attention of q (rotated and scaled in its prologue) against
+ *   the prepared workspace; rope tables must be the ones given to prepare_kv.
+ */
+size_t dit_attn_workspace_bytes(int B, int H, int S, int D);
+
+dit_status_t dit_attn_prepare_kv(const void* k, const void* v,
+                                 const float* rope_cos, const float* rope_sin,
+                                 void* workspace, size_t workspace_bytes,
+                                 int B, int H, int S, int D, void* stream);
+
+dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin,
+                           const void* workspace, size_t workspace_bytes, void* out,
+                           int B, int H, int S, int D, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

@@ -1,0 +1,132 @@
+"""The C-ABI library without a GPU: it loads, exports what include/dit_attn.h
+declares, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dit_joint_self_amd as dj
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dj.LIB_PATH), reason="libditattn.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", text)))
+
+
+def _no_device():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(dj.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", dj.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (dit_[a-z0-9_]+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+    lib = dj.lib()
+    for name in dj.EXPORTED_SYMBOLS:
+        assert getattr(lib, name) is not None
+    assert dj.dit_abi_version() == 1
+
+
+def test_workspace_bytes():
+    # 64-key tiles of 32 KiB per (batch, head); 0 on unsupported sizes.
+    assert dj.dit_attn_workspace_bytes(1, 24, 16896, 128) == 24 * 264 * 32768
+    assert dj.dit_attn_workspace_bytes(2, 3, 65, 128) == 6 * 2 * 32768
+    assert dj.dit_attn_workspace_bytes(1, 1, 1, 128) == 32768
+    assert dj.dit_attn_workspace_bytes(1, 1, 0, 128) == 0
+    assert dj.dit_attn_workspace_bytes(1, 1, 64, 64) == 0
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, cos=None, sin=None, out=FAKE * 4, B=1, H=2, S_txt=3, S_img=5,
+             D=128, scale=0.1, dtype=0, stream=None)
+    a.update(kw)
+    return dj.lib().dit_attn_forward(a["q"], a["k"], a["v"], a["cos"], a["sin"], a["out"], a["B"], a["H"],
+                                     a["S_txt"], a["S_img"], a["D"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), dj.DIT_ERR_INVALID_ARG),
+    (dict(out=None), dj.DIT_ERR_INVALID_ARG),
+    (dict(cos=FAKE * 5), dj.DIT_ERR_INVALID_ARG),             # exactly one table
+    (dict(sin=FAKE * 5), dj.DIT_ERR_INVALID_ARG),
+    (dict(cos=FAKE * 5 + 4, sin=FAKE * 6), dj.DIT_ERR_INVALID_ARG),  # misaligned table
+    (dict(B=0), dj.DIT_ERR_INVALID_ARG),
+    (dict(H=-1), dj.DIT_ERR_INVALID_ARG),
+    (dict(S_txt=-1), dj.DIT_ERR_INVALID_ARG),
+    (dict(S_txt=0, S_img=0), dj.DIT_ERR_INVALID_ARG),
+    (dict(S_txt=2**31 - 1, S_img=1), dj.DIT_ERR_INVALID_ARG),  # S overflows int
+    (dict(D=64), dj.DIT_ERR_UNSUPPORTED),
+    (dict(D=0), dj.DIT_ERR_INVALID_ARG),
+    (dict(dtype=1), dj.DIT_ERR_UNSUPPORTED),
+    (dict(dtype=7), dj.DIT_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), dj.DIT_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), dj.DIT_ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), dj.DIT_ERR_INVALID_ARG),               # misaligned
+    (dict(out=FAKE), dj.DIT_ERR_INVALID_ARG),                 # out aliases q
+    (dict(out=FAKE * 2 + 256), dj.DIT_ERR_INVALID_ARG),       # out overlaps k
+    (dict(B=70000, H=1), dj.DIT_ERR_INVALID_ARG),             # too many (b, h) for one launch
+    (dict(B=1, H=60000, S_txt=2**20, S_img=0), dj.DIT_ERR_INVALID_ARG),
+])
+def test_forward_rejects_bad_arguments(kw, status):
+    assert _fwd(**kw) == status
+    assert dj.dit_last_error() != ""
+
+
+def test_split_entry_points_reject_bad_arguments():
+    L = dj.lib()
+    need = dj.dit_attn_workspace_bytes(1, 2, 8, 128)
+    ws = 0x10000000
+    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, None, None, ws, need - 1, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, None, None, ws + 16, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, None, None, FAKE, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_kv(FAKE, None, None, None, ws, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, None, None, ws, need, 1, 2, 8, 96, None) == dj.DIT_ERR_UNSUPPORTED
+    assert L.dit_attn_core(FAKE, None, None, ws, need, ws, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, FAKE * 2, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, float("nan"), None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, None, None, ws, need - 1, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+
+
+def test_rope_tables_reject_bad_arguments():
+    L = dj.lib()
+    dims = lambda *d: (ctypes.c_int32 * len(d))(*d)
+    assert L.dit_rope_tables(None, 4, 2, dims(64, 64), 1e4, FAKE, FAKE * 2, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_rope_tables(FAKE, 0, 2, dims(64, 64), 1e4, FAKE, FAKE * 2, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_rope_tables(FAKE, 4, 0, dims(64, 64), 1e4, FAKE, FAKE * 2, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_rope_tables(FAKE, 4, 5, dims(2, 2, 2, 2, 2), 1e4, FAKE, FAKE * 2, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_rope_tables(FAKE, 4, 2, dims(63, 65), 1e4, FAKE, FAKE * 2, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_rope_tables(FAKE, 4, 2, dims(64, 64), 0.0, FAKE, FAKE * 2, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_rope_tables(FAKE, 4, 2, dims(64, 64), 1e4, FAKE + 4, FAKE * 2, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_rope_tables(FAKE, 4, 2, dims(64, 64), 1e4, FAKE, FAKE + 64, None) == dj.DIT_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(not _no_device(), reason="a GPU is visible")
+def test_valid_call_without_device_reports_no_device():
+    assert _fwd() == dj.DIT_ERR_NO_DEVICE
+    assert "device" in dj.dit_last_error()
+    dims = (ctypes.c_int32 * 2)(64, 64)
+    assert dj.lib().dit_rope_tables(FAKE, 4, 2, dims, 1e4, FAKE, FAKE * 2, None) == dj.DIT_ERR_NO_DEVICE
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(dj.DitAttnError) as ei:
+        dj._check(dj.DIT_ERR_UNSUPPORTED)
+    assert "DIT_ERR_UNSUPPORTED" in str(ei.value)

@@ -1,0 +1,203 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Tolerances for bf16 inputs with unit-variance Q/K/V: max |gpu - oracle| <= 1e-2
+and mean |gpu - oracle| <= 1e-3 over the compared outputs, plus a relative
+check mean|diff| / mean|oracle| <= 1%, which an all-zero output fails even at
+long sequences where the absolute gates get loose.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import dit_workloads as W
+from oracle import joint_attention, rope_angles
+from tests.gpu_inputs import bf16_f64, err_stats, from_device_bf16, sample_rows, to_device_bf16
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+REL_MEAN = 1e-2
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _dj():
+    import dit_joint_self_amd as dj
+    return dj  # raises on use if the library is missing: no fallback
+
+
+def _tables(w, device="cuda"):
+    torch = _torch()
+    dj = _dj()
+    pos = torch.from_numpy(W.positions(w)).to(device)
+    return dj.dit_rope_tables(pos, w.axes_dim, w.theta)
+
+
+def _run(w, qb, kb, vb, rope=True, scale=None, split=False):
+    torch = _torch()
+    dj = _dj()
+    q, k, v = to_device_bf16(qb), to_device_bf16(kb), to_device_bf16(vb)
+    cos, sin = _tables(w) if rope else (None, None)
+    if split:
+        nbytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(q)
+        dj.dit_attn_prepare_kv(k, v, cos, sin, ws)
+        dj.dit_attn_core(q, cos, sin, ws, out, scale=scale)
+    else:
+        out = dj.dit_attn_forward(q, k, v, cos, sin, S_txt=w.S_txt, scale=scale)
+    torch.cuda.synchronize()
+    return from_device_bf16(out)
+
+
+def _oracle(w, qb, kb, vb, rope=True, scale=None, rows=None):
+    ang = rope_angles(W.positions(w), w.axes_dim, w.theta) if rope else None
+    return joint_attention(bf16_f64(qb), bf16_f64(kb), bf16_f64(vb), ang, scale=scale, rows=rows)
+
+
+def _assert_close(got, want, tag):
+    e = err_stats(got, want)
+    print(f"[parity] {tag}: {e}", flush=True)
+    assert np.all(np.isfinite(got)), tag
+    assert e["max_abs"] <= MAX_ABS, (tag, e)
+    assert e["mean_abs"] <= MEAN_ABS, (tag, e)
+    assert e["rel_mean"] <= REL_MEAN, (tag, e)
+
+
+# ---------------------------------------------------------------- RoPE tables
+
+@pytest.mark.parametrize("name", ["tiny", "flux1024x768", "flux2048", "video_ulysses4"])
+def test_rope_tables_match_oracle_angles(name):
+    w = W.get(name)
+    cos, sin = _tables(w)
+    ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
+    dc = np.abs(cos.cpu().numpy().astype(np.float64) - np.cos(ang)).max()
+    ds = np.abs(sin.cpu().numpy().astype(np.float64) - np.sin(ang)).max()
+    print(f"[rope] {name}: max|dcos|={dc:.3g} max|dsin|={ds:.3g}", flush=True)
+    # fp64 on both sides, one fp32 rounding on the GPU side: <= 1 ulp of 1.0.
+    assert dc <= 1.2e-7 and ds <= 1.2e-7
+
+
+# ---------------------------------------------------------------- full parity
+
+@pytest.mark.parametrize("name", ["tiny", "flux1024x768"])
+def test_full_parity(name):
+    w = W.get(name)
+    qb, kb, vb = W.make_bf16_inputs(w)
+    got = _run(w, qb, kb, vb)
+    want = _oracle(w, qb, kb, vb)
+    _assert_close(got, want, name)
+
+
+@pytest.mark.parametrize("name,n_random", [("flux2048", 96), ("video_ulysses4", 48)])
+def test_sampled_parity_full_size(name, n_random):
+    """Full-size workloads in the launch configuration the benchmark times;
+    the oracle computes a sample of query rows (each against every key)."""
+    w = W.get(name)
+    qb, kb, vb = W.make_bf16_inputs(w)
+    got = _run(w, qb, kb, vb)
+    assert np.all(np.isfinite(got)), name
+    rows = sample_rows(w.S, w.S_txt, n_random, seed=w.seed)
+    want = _oracle(w, qb, kb, vb, rows=rows)
+    _assert_close(got[:, :, rows], want, f"{name} ({len(rows)} rows x {w.H} heads)")
+
+
+# ---------------------------------------------------------------- edge cases
+
+def _small(S_txt, grid, B=1, H=3, axes=(64, 64), seed=7):
+    return W.Workload("edge", B=B, H=H, D=128, S_txt=S_txt, grid=grid, axes_dim=axes, theta=10000.0, seed=seed)
+
+
+@pytest.mark.parametrize("S_txt,grid,B,H", [
+    (1, (0, 0), 1, 1),        # S = 1: output = V
+    (2, (0, 0), 1, 2),        # text only
+    (0, (7, 9), 1, 2),        # image only, S = 63
+    (0, (8, 8), 2, 2),        # S = 64 exactly one tile
+    (1, (8, 8), 1, 3),        # S = 65, one key in the last tile
+    (5, (4, 31), 2, 3),       # S = 129
+    (13, (12, 20), 1, 2),     # S = 253, ragged query and key tails
+    (64, (16, 16), 2, 2),     # tiny grid with B = 2
+])
+def test_ragged_and_small_shapes(S_txt, grid, B, H):
+    w = _small(S_txt, grid, B=B, H=H, seed=S_txt * 1000 + int(np.prod(grid)))
+    qb, kb, vb = W.make_bf16_inputs(w)
+    for split in (False, True):
+        got = _run(w, qb, kb, vb, split=split)
+        want = _oracle(w, qb, kb, vb)
+        _assert_close(got, want, f"S={w.S} B={B} H={H} split={split}")
+    if w.S == 1:
+        assert np.array_equal(got, bf16_f64(vb))
+
+
+def test_no_rope_three_axis():
+    w = W.get("tiny").with_(grid=(2, 8, 16), axes_dim=(16, 56, 56), H=2)
+    qb, kb, vb = W.make_bf16_inputs(w)
+    _assert_close(_run(w, qb, kb, vb, rope=False), _oracle(w, qb, kb, vb, rope=False), "no-rope")
+
+
+def test_scale_zero_gives_mean_of_v():
+    w = _small(3, (10, 10), H=2)
+    qb, kb, vb = W.make_bf16_inputs(w)
+    got = _run(w, qb, kb, vb, scale=0.0)
+    mean_v = bf16_f64(vb).mean(axis=2, keepdims=True)
+    assert np.abs(got - mean_v).max() <= 2e-3
+
+
+def test_sharp_softmax_and_rising_max():
+    """Large logits (Q x 16) and key norms that grow along the sequence, so the
+    running max is raised many times and exponents span the full range."""
+    w = _small(40, (20, 25), H=2, seed=99)
+    q, k, v = W.draw_qkv_f32(w)
+    growth = np.linspace(0.5, 3.0, w.S, dtype=np.float32)[None, None, :, None]
+    qb, kb, vb = W.bf16_round_bits(q * 16), W.bf16_round_bits(k * growth), W.bf16_round_bits(v)
+    got = _run(w, qb, kb, vb)
+    want = _oracle(w, qb, kb, vb)
+    e = err_stats(got, want)
+    print(f"[parity] sharp: {e}", flush=True)
+    # Peaked rows copy single V rows: errors are a bf16 ulp of |v| (<= 4.5).
+    assert np.all(np.isfinite(got)) and e["max_abs"] <= 4e-2 and e["mean_abs"] <= 2e-3
+
+
+def test_deterministic_and_forward_equals_split():
+    w = W.get("tiny")
+    qb, kb, vb = W.make_bf16_inputs(w)
+    a = _run(w, qb, kb, vb)
+    b = _run(w, qb, kb, vb)
+    c = _run(w, qb, kb, vb, split=True)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_output_bounds_untouched():
+    """NaN-prefilled output is fully written; a canary region right after it is not."""
+    torch = _torch()
+    dj = _dj()
+    w = _small(3, (9, 11), H=3)
+    qb, kb, vb = W.make_bf16_inputs(w)
+    q, k, v = to_device_bf16(qb), to_device_bf16(kb), to_device_bf16(vb)
+    cos, sin = _tables(w)
+    n = q.numel()
+    buf = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    buf[n:] = 7.0
+    out = buf[:n].view(q.shape)
+    dj.dit_attn_forward(q, k, v, cos, sin, out=out, S_txt=w.S_txt)
+    torch.cuda.synchronize()
+    got = from_device_bf16(out)
+    assert np.all(np.isfinite(got))
+    assert torch.all(buf[n:] == 7.0).item()
+    _assert_close(got, _oracle(w, qb, kb, vb), "canary")
+
+
+def test_error_status_on_device():
+    torch = _torch()
+    dj = _dj()
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dj.DitAttnError) as ei:
+        dj.dit_attn_forward(q, q.clone(), q.clone())
+    assert ei.value.status == dj.DIT_ERR_UNSUPPORTED
