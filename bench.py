@@ -25,6 +25,26 @@ import numpy as np
 import dit_workloads as W
 
 METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=16896,H=24,D=128 (1 GPU)"
+
+# HBM bytes per attention-kernel launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+# (scaled by a plain-copy calibration), keyed by the hash of the kernel sources they were
+# taken on and by workload; reported as roofline.traffic only while the sources match.
+KERNEL_SOURCES = ["dit_joint_self_amd/csrc/attn_core.hip", "dit_joint_self_amd/csrc/tile_layout.h",
+                  "dit_joint_self_amd/csrc/bf16_util.h"]
+MEASURED_TRAFFIC = {
+    ("4570db5b9355adc5", "flux2048"): {"read_bytes": 995.0e6, "write_bytes": 103.8e6,
+                                       "profile": "profiles/attn_core_flux2048.md"},
+}
+
+
+def kernel_sources_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 
@@ -37,7 +57,29 @@ def parse():
     ap.add_argument("--workload", default="flux2048", choices=[n for n in W.WORKLOADS if "fp8" not in n])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of attention, time a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(args, torch):
+    """A plain device-to-device copy of known size, run under the same counters
+    as the attention kernel so FETCH_SIZE / WRITE_SIZE can be scaled to bytes."""
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n, "ms": ms,
+                      "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def bf16_dev(bits, torch):
@@ -54,7 +96,7 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = 1
     ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
-    rows_per_head = min(w.S, 2048)
+    rows_per_head = min(w.S, 8192)
     rows = np.arange(rows_per_head)
     t0 = time.perf_counter()
     done_rows = 0
@@ -89,6 +131,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib:
+        copy_calibration(args, torch)
+        return
     w = W.get(args.workload)
     print(f"[bench] workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D}", file=sys.stderr, flush=True)
     qb, kb, vb = W.make_bf16_inputs(w)
@@ -147,6 +192,9 @@ def main():
     spot_err = float(np.abs(W.bf16_bits_to_f32(got_bits) - ref).max())
 
     flops = w.flops
+    src_hash = kernel_sources_hash()
+    meas = MEASURED_TRAFFIC.get((src_hash, w.name))
+    traffic = None if meas is None else meas["read_bytes"] + meas["write_bytes"]
     core_avg = float(np.mean(core_ms))
     prep_avg = float(np.mean(prep_ms))
     achieved = flops / (core_avg * 1e-3) / 1e12
@@ -170,7 +218,8 @@ def main():
         "pct_of_bf16_peak": 100.0 * flops / (step_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "attn_core_kernel", "achieved": achieved,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
-                     "traffic": None, "avg_ms": core_avg},
+                     "traffic": traffic, "traffic_unit": "HBM bytes per launch (read + write)",
+                     "avg_ms": core_avg, "kernel_sources": src_hash},
         "stages_ms": {"prepare_kv": prep_avg, "attn_core": core_avg,
                       "prepare_kv_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9},
         "forward_ms": fwd_ms,

@@ -10,8 +10,9 @@
 // operand of O^T = V^T P^T.  Keys at or past S are written as zeros so the
 // PV product never multiplies a masked probability by garbage.
 //
-// Roofline: HBM bound.  Algorithmic bytes per tile: read 2 x 16 KiB (K, V)
-// + 2 x 16 KiB (cos, sin rows when RoPE is on), write 32 KiB.
+// Roofline: HBM bound.  Algorithmic bytes per tile and head: read 2 x 16 KiB
+// (K, V) + 2 x 16 KiB (cos, sin rows when RoPE is on; shared by all heads),
+// write TILE_BYTES = 35 KiB (the two parts with their row padding).
 
 #include <hip/hip_runtime.h>
 
@@ -44,15 +45,13 @@ __global__ __launch_bounds__(256) void prepare_kv_kernel(
         vtile[x] = w;
     }
 
-    // K part: output chunk x = (row rho, physical chunk p).
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int x = tid + i * 256;
-        const int rho = x >> 4;
-        const int c = (x & 15) ^ (rho & 15);
+    // K part: output chunk x = (row rho, chunk c); chunk 16 of a row is padding.
+    for (int x = tid; x < K_PART_CHUNKS; x += 256) {
+        const int rho = x / K_ROW_CHUNKS;
+        const int c = x - rho * K_ROW_CHUNKS;
         const int key = key0 + kperm(rho);
         uint4 w = make_uint4(0, 0, 0, 0);
-        if (key < S) {
+        if (c < 16 && key < S) {
             w = ksrc[(int64_t)key * 16 + c];
             if (has_rope) {
                 float f[8];
@@ -66,9 +65,10 @@ __global__ __launch_bounds__(256) void prepare_kv_kernel(
 
     __syncthreads();
 
-    // V^T part: logical chunk (d, c) = keys 8c..8c+7 of head dim d.  Lanes run
-    // over d so the 2-byte LDS gathers of one instruction hit one row.
+    // V^T part: chunk (d, c) = keys 8c..8c+7 of head dim d.  Lanes run over d
+    // so the 2-byte LDS gathers of one instruction hit one row.
     const unsigned short* vt16 = reinterpret_cast<const unsigned short*>(vtile);
+    uint4* vdst = dst + K_PART_CHUNKS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int y = tid + i * 256;
@@ -81,8 +81,9 @@ __global__ __launch_bounds__(256) void prepare_kv_kernel(
             const uint32_t hi = vt16[(c * 8 + 2 * e + 1) * 128 + d];
             w[e] = lo | (hi << 16);
         }
-        dst[TILE_CHUNKS / 2 + v_chunk(d, c)] = make_uint4(w[0], w[1], w[2], w[3]);
+        vdst[v_chunk(d, c)] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+    if (tid < HEAD_DIM) vdst[v_chunk(tid, 8)] = make_uint4(0, 0, 0, 0);
 }
 
 hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, const float* sin_t,

@@ -43,10 +43,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_workspace_bytes():
-    # 64-key tiles of 32 KiB per (batch, head); 0 on unsupported sizes.
-    assert dj.dit_attn_workspace_bytes(1, 24, 16896, 128) == 24 * 264 * 32768
-    assert dj.dit_attn_workspace_bytes(2, 3, 65, 128) == 6 * 2 * 32768
-    assert dj.dit_attn_workspace_bytes(1, 1, 1, 128) == 32768
+    # 64-key tiles of 35 KiB (padded K and V^T parts) per (batch, head); 0 on unsupported sizes.
+    assert dj.dit_attn_workspace_bytes(1, 24, 16896, 128) == 24 * 264 * 35840
+    assert dj.dit_attn_workspace_bytes(2, 3, 65, 128) == 6 * 2 * 35840
+    assert dj.dit_attn_workspace_bytes(1, 1, 1, 128) == 35840
     assert dj.dit_attn_workspace_bytes(1, 1, 0, 128) == 0
     assert dj.dit_attn_workspace_bytes(1, 1, 64, 64) == 0
 

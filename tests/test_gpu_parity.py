@@ -62,12 +62,20 @@ def _oracle(w, qb, kb, vb, rope=True, scale=None, rows=None):
     return joint_attention(bf16_f64(qb), bf16_f64(kb), bf16_f64(vb), ang, scale=scale, rows=rows)
 
 
-def _assert_close(got, want, tag):
+def _assert_close(got, want, tag, short=False):
+    """Gates above.  ``short`` sequences (S <= 256) average few V rows, so |O|
+    is O(1) and the bf16 output rounding alone (up to 2^-9 |O|) plus the bf16
+    rounding of P (relative 2^-9 per weight) can exceed 1e-3 on the mean: for
+    them the gates are max(1e-2, 2^-7 max|O|) and max(1e-3, 2^-8 mean|O|)."""
     e = err_stats(got, want)
     print(f"[parity] {tag}: {e}", flush=True)
     assert np.all(np.isfinite(got)), tag
-    assert e["max_abs"] <= MAX_ABS, (tag, e)
-    assert e["mean_abs"] <= MEAN_ABS, (tag, e)
+    max_gate, mean_gate = MAX_ABS, MEAN_ABS
+    if short:
+        max_gate = max(MAX_ABS, 2.0 ** -7 * float(np.abs(want).max()))
+        mean_gate = max(MEAN_ABS, 2.0 ** -8 * float(np.abs(want).mean()))
+    assert e["max_abs"] <= max_gate, (tag, e)
+    assert e["mean_abs"] <= mean_gate, (tag, e)
     assert e["rel_mean"] <= REL_MEAN, (tag, e)
 
 
@@ -131,7 +139,7 @@ def test_ragged_and_small_shapes(S_txt, grid, B, H):
     for split in (False, True):
         got = _run(w, qb, kb, vb, split=split)
         want = _oracle(w, qb, kb, vb)
-        _assert_close(got, want, f"S={w.S} B={B} H={H} split={split}")
+        _assert_close(got, want, f"S={w.S} B={B} H={H} split={split}", short=w.S <= 256)
     if w.S == 1:
         assert np.array_equal(got, bf16_f64(vb))
 
@@ -151,18 +159,53 @@ def test_scale_zero_gives_mean_of_v():
 
 
 def test_sharp_softmax_and_rising_max():
-    """Large logits (Q x 16) and key norms that grow along the sequence, so the
-    running max is raised many times and exponents span the full range."""
+    """Large logits and key norms that grow along the sequence, so the running
+    max is raised many times and exponents span the full range.
+
+    No RoPE, and scale = 0.25 / log2(e): the kernel's scaled Q'' = Q / 4 and
+    K' = K are then exact in bf16, the scores are exact up to fp32 summation,
+    and the only differences from the oracle are the bf16 rounding of P
+    (relative 2^-9 per weight) and of the output (2^-9 |O|), so the gates
+    below are 2^-7 max|V| and 2^-9 mean|V| + 2^-9 mean|O|."""
     w = _small(40, (20, 25), H=2, seed=99)
     q, k, v = W.draw_qkv_f32(w)
     growth = np.linspace(0.5, 3.0, w.S, dtype=np.float32)[None, None, :, None]
-    qb, kb, vb = W.bf16_round_bits(q * 16), W.bf16_round_bits(k * growth), W.bf16_round_bits(v)
-    got = _run(w, qb, kb, vb)
-    want = _oracle(w, qb, kb, vb)
+    qb, kb, vb = W.bf16_round_bits(q * 12), W.bf16_round_bits(k * growth), W.bf16_round_bits(v)
+    scale = 0.25 / math.log2(math.e)
+    got = _run(w, qb, kb, vb, rope=False, scale=scale)
+    want = _oracle(w, qb, kb, vb, rope=False, scale=scale)
     e = err_stats(got, want)
     print(f"[parity] sharp: {e}", flush=True)
-    # Peaked rows copy single V rows: errors are a bf16 ulp of |v| (<= 4.5).
-    assert np.all(np.isfinite(got)) and e["max_abs"] <= 4e-2 and e["mean_abs"] <= 2e-3
+    vabs = np.abs(bf16_f64(vb))
+    assert np.all(np.isfinite(got))
+    assert e["max_abs"] <= 2.0 ** -7 * vabs.max(), e
+    assert e["mean_abs"] <= 2.0 ** -9 * (vabs.mean() + np.abs(want).mean()), e
+
+
+def test_sharp_softmax_with_rope():
+    """Sharper logits (Q x 4) through the whole RoPE path.
+
+    Here the bf16 rounding of the rotated K' and of the scaled Q'' (relative
+    2^-9 each) moves logit (i, j) by at most d_ij = 2^-8 * scale * sum_d
+    |q'_id| |k'_jd| (natural-log units), so row i of the output can move by at
+    most (exp(2 D_i) - 1) max|v| with D_i = max_j d_ij, plus the P rounding
+    (2^-8 max|v|) and the output rounding (2^-9 |O_i|).  The unit-variance
+    gates do not apply at these logit sizes; this per-row bound does."""
+    from oracle import rope_apply
+    w = _small(40, (20, 25), H=2, seed=98)
+    q, k, v = W.draw_qkv_f32(w)
+    qb, kb, vb = W.bf16_round_bits(q * 4), W.bf16_round_bits(k), W.bf16_round_bits(v)
+    got = _run(w, qb, kb, vb)
+    want = _oracle(w, qb, kb, vb)
+    ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
+    qr, kr = np.abs(rope_apply(bf16_f64(qb), ang)), np.abs(rope_apply(bf16_f64(kb), ang))
+    scale = 1.0 / math.sqrt(w.D)
+    D = 2.0 ** -8 * scale * np.einsum("bhid,bhjd->bhij", qr, kr).max(axis=3)
+    vmax = np.abs(bf16_f64(vb)).max()
+    bound = (np.expm1(2 * D) + 2.0 ** -8) * vmax + 2.0 ** -9 * np.abs(want).max(axis=3)
+    err = np.abs(got - want).max(axis=3)
+    print(f"[parity] sharp+rope: max err {err.max():.3g}, min slack {(bound - err).min():.3g}", flush=True)
+    assert np.all(np.isfinite(got)) and np.all(err <= bound)
 
 
 def test_deterministic_and_forward_equals_split():
