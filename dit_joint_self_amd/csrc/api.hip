@@ -21,11 +21,11 @@
 namespace dit {
 hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, const float* sin_t,
                              void* ws, int BH, int S, hipStream_t stream);
-hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws,
+hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
                             void* out, int BH, int S, float qmul, hipStream_t stream);
+size_t core_partial_bytes(int BH, int S);
 hipError_t launch_rope_tables(const int32_t* pos, int S, int n_axes, const int32_t* axes_dim,
                               double theta, float* cos_t, float* sin_t, hipStream_t stream);
-int core_block_m();
 }  // namespace dit
 
 namespace {
@@ -150,9 +150,16 @@ dit_status_t dit_rope_tables(const int32_t* pos, int S, int n_axes, const int32_
                     "rope_tables_kernel");
 }
 
+// Workspace: the K/V tile stream, then (256-byte aligned) the key-range
+// partials of the items that run split.
+static size_t tiles_bytes(int B, int H, int S) {
+    return ((size_t)B * H * (size_t)dit::num_kv_tiles(S) * dit::TILE_BYTES + 255) & ~(size_t)255;
+}
+
 size_t dit_attn_workspace_bytes(int B, int H, int S, int D) {
     if (B < 1 || H < 1 || S < 1 || D != dit::HEAD_DIM) return 0;
-    return (size_t)B * H * (size_t)dit::num_kv_tiles(S) * dit::TILE_BYTES;
+    if (check_shape(B, H, S, D) != DIT_OK) return 0;
+    return tiles_bytes(B, H, S) + dit::core_partial_bytes(B * H, S);
 }
 
 dit_status_t dit_attn_prepare_kv(const void* k, const void* v, const float* rope_cos, const float* rope_sin,
@@ -194,7 +201,8 @@ dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* ro
         return fail(DIT_ERR_INVALID_ARG, "out overlaps q or the workspace");
     if ((st = check_device()) != DIT_OK) return st;
     const float qmul = (float)((double)scale * 1.4426950408889634073599);  // scale * log2(e)
-    return launched(dit::launch_attn_core(q, rope_cos, rope_sin, workspace, out, B * H, S, qmul,
+    void* part = static_cast<char*>(const_cast<void*>(workspace)) + tiles_bytes(B, H, S);
+    return launched(dit::launch_attn_core(q, rope_cos, rope_sin, workspace, part, out, B * H, S, qmul,
                                           static_cast<hipStream_t>(stream)),
                     "attn_core_kernel");
 }
@@ -231,7 +239,8 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const
     hipError_t e = dit::launch_prepare_kv(k, v, rope_cos, rope_sin, ws, B * H, S, s);
     if (e == hipSuccess) {
         const float qmul = (float)((double)scale * 1.4426950408889634073599);
-        e = dit::launch_attn_core(q, rope_cos, rope_sin, ws, out, B * H, S, qmul, s);
+        e = dit::launch_attn_core(q, rope_cos, rope_sin, ws, static_cast<char*>(ws) + tiles_bytes(B, H, S), out,
+                                  B * H, S, qmul, s);
     }
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return launched(e, "dit_attn_forward kernels");

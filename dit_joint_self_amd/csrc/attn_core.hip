@@ -36,6 +36,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "bf16_util.h"
 #include "tile_layout.h"
 
@@ -114,7 +116,7 @@ __device__ __forceinline__ void exp_pack16(const f32x16& sc, bf16x8 (&pf)[2], fl
 constexpr float SUM_LIMIT = 1048576.0f;  // 2^20
 
 template <int QB, bool MASKED>
-__device__ __forceinline__ void attn_tile(const uint4* kt, int j, int S, int n, int hh,
+__device__ __forceinline__ void attn_tile(const uint4* kt, int j, bool first, int S, int n, int hh,
                                           const bf16x8 (&qf)[QB][8], f32x16 (&o)[QB][4],
                                           f32x16 (&negm)[QB], float (&lsum)[QB]) {
     const uint4* vt = kt + K_PART_CHUNKS;
@@ -162,7 +164,7 @@ __device__ __forceinline__ void attn_tile(const uint4* kt, int j, int S, int n, 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         float t0 = 0.0f, t1 = 0.0f;
-        bool slow = (j == 0);
+        bool slow = first;
         if (!slow) {
             exp_pack16(s[qb][0], pf[qb][0], t0);
             exp_pack16(s[qb][1], pf[qb][1], t1);
@@ -175,8 +177,8 @@ __device__ __forceinline__ void attn_tile(const uint4* kt, int j, int S, int n, 
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][1][r]);
             mx = swap_halves_max(mx);
-            const float shift = (j == 0) ? mx : fmaxf(mx, 0.0f);
-            if (j > 0) {
+            const float shift = first ? mx : fmaxf(mx, 0.0f);
+            if (!first) {
                 const float alpha = __builtin_amdgcn_exp2f(-shift);
                 lsum[qb] *= alpha;
 #pragma unroll
@@ -216,24 +218,43 @@ __device__ __forceinline__ void attn_tile(const uint4* kt, int j, int S, int n, 
     }
 }
 
-template <int NW, int QB>
+constexpr int NW = 8;                 // waves per workgroup (two per SIMD)
+constexpr int QB = 1;                 // 32-query blocks per wave
+constexpr int BM = NW * 32 * QB;      // queries per workgroup
+constexpr int MI355X_CUS = 256;       // workgroups resident at once (one per CU)
+
+// Partial results of one key-range workgroup: O (unnormalised, fp32, row-major
+// [BM][128]), then the offset m (base 2) and the weight sum l of each row.
+constexpr int PART_FLOATS = BM * HEAD_DIM + 2 * BM;
+
+// Workgroup x of a launch -> logical index.  Workgroups are dispatched
+// round-robin over the 8 XCDs; give each XCD a contiguous range of logical
+// indices so the workgroups sharing an XCD's L2 stream the same head's K/V.
+__device__ __forceinline__ int xcd_remap(int x, int total) {
+    const int xcd = x & 7, slot = x >> 3;
+    const int per = total >> 3, rem = total & 7;
+    return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+}
+
+// One workgroup = BM queries of one (batch, head) against the key tiles
+// [tb, te).  Items item0 + i / nsplit, key range i % nsplit of nsplit equal
+// ranges.  PARTIAL = false: the whole key range, normalised bf16 output.
+// PARTIAL = true: unnormalised O, m and l of the range to `part`.
+template <bool PARTIAL>
 __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const uint4* __restrict__ q, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
-    const uint4* __restrict__ ws, uint2* __restrict__ out, int S, int ntiles, int nqt,
-    int total_wg, float qmul, int has_rope) {
-    constexpr int BM = NW * 32 * QB;
+    const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ part, int S, int ntiles, int nqt,
+    int item0, int nsplit, float qmul, int has_rope) {
     __shared__ uint4 lds0[TILE_CHUNKS];
     __shared__ uint4 lds1[TILE_CHUNKS];
 
-    // Workgroups are dispatched round-robin over the 8 XCDs.  Give each XCD a
-    // contiguous range of (head, query-tile) items so the workgroups sharing
-    // an XCD's L2 stream the same head's K/V at the same time.
-    const int x = blockIdx.x;
-    const int xcd = x & 7, slot = x >> 3;
-    const int per = total_wg >> 3, rem = total_wg & 7;
-    const int item = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int item = item0 + logical / nsplit;
+    const int f = logical - (logical / nsplit) * nsplit;
     const int64_t bh = item / nqt;
     const int qt = item - (int)bh * nqt;
+    const int tb = (int)((int64_t)f * ntiles / nsplit);
+    const int te = (int)((int64_t)(f + 1) * ntiles / nsplit);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -241,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const int hh = lane >> 5;
 
     const uint4* src = ws + bh * (int64_t)ntiles * TILE_CHUNKS;
-    load_tile_async<NW>(src, lds0, wave, lane);
+    load_tile_async<NW>(src + (int64_t)tb * TILE_CHUNKS, lds0, wave, lane);
 
     // ---- Q prologue: RoPE, fold scale*log2(e), round to bf16, keep resident.
     bf16x8 qf[QB][8];
@@ -253,14 +274,14 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int c = 2 * t + hh;
-            float f[8];
+            float fv[8];
             uint4 w = make_uint4(0, 0, 0, 0);
             if (ok) w = qrow[c];
-            unpack8(w, f);
-            if (has_rope && ok) rotate4(f, cos_t[(int64_t)row * 16 + c], sin_t[(int64_t)row * 16 + c]);
+            unpack8(w, fv);
+            if (has_rope && ok) rotate4(fv, cos_t[(int64_t)row * 16 + c], sin_t[(int64_t)row * 16 + c]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] *= qmul;
-            qf[qb][t] = as_bf16x8(pack8(f));
+            for (int e = 0; e < 8; ++e) fv[e] *= qmul;
+            qf[qb][t] = as_bf16x8(pack8(fv));
         }
     }
 
@@ -276,39 +297,57 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
 
     // Two distinct LDS buffers and a loop unrolled by two: the tile being read
     // and the tile in flight are different objects, so the compiler does not
-    // make the reads wait for the prefetch.  Tiles 0 .. ntiles-2 take the
-    // unmasked path; the last tile always takes the masked one (a no-op mask
-    // when S is a multiple of the tile).
-    const int nfull = ntiles - 1;
-    int j = 0;
-    for (; j + 2 <= nfull; j += 2) {
+    // make the reads wait for the prefetch.  Tiles tb .. te-2 take the
+    // unmasked path; the range's last tile takes the masked one (a no-op mask
+    // unless it is the sequence's ragged last tile).  Tile tb + i lives in
+    // buffer i mod 2.
+    const int last = te - 1;
+    int j = tb;
+    for (; j + 2 <= last; j += 2) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         load_tile_async<NW>(src + (int64_t)(j + 1) * TILE_CHUNKS, lds1, wave, lane);
-        attn_tile<QB, false>(lds0, j, S, n, hh, qf, o, negm, lsum);
+        attn_tile<QB, false>(lds0, j, j == tb, S, n, hh, qf, o, negm, lsum);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         load_tile_async<NW>(src + (int64_t)(j + 2) * TILE_CHUNKS, lds0, wave, lane);
-        attn_tile<QB, false>(lds1, j + 1, S, n, hh, qf, o, negm, lsum);
+        attn_tile<QB, false>(lds1, j + 1, false, S, n, hh, qf, o, negm, lsum);
     }
-    if (j < nfull) {
+    if (j < last) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         load_tile_async<NW>(src + (int64_t)(j + 1) * TILE_CHUNKS, lds1, wave, lane);
-        attn_tile<QB, false>(lds0, j, S, n, hh, qf, o, negm, lsum);
+        attn_tile<QB, false>(lds0, j, j == tb, S, n, hh, qf, o, negm, lsum);
         ++j;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    attn_tile<QB, true>((j & 1) ? lds1 : lds0, j, S, n, hh, qf, o, negm, lsum);
+    attn_tile<QB, true>(((j - tb) & 1) ? lds1 : lds0, j, j == tb, S, n, hh, qf, o, negm, lsum);
 
     // ---- epilogue: lane (n, hh), register r of dim block db holds dim
     // 32 db + 8 (r >> 2) + 4 hh + (r & 3) of query n.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float inv = 1.0f / swap_halves_sum(lsum[qb]);
-        const int row = qt * BM + (wave * QB + qb) * 32 + n;
-        if (row < S) {
+        const float l = swap_halves_sum(lsum[qb]);
+        const int rloc = (wave * QB + qb) * 32 + n;
+        const int row = qt * BM + rloc;
+        if (PARTIAL) {
+            float* pw = part + (int64_t)logical * PART_FLOATS;
+            float4* prow = reinterpret_cast<float4*>(pw + (int64_t)rloc * HEAD_DIM);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16& acc = o[qb][db];
+                    prow[db * 8 + g * 2 + hh] =
+                        make_float4(acc[4 * g + 0], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+                }
+            if (hh == 0) {
+                pw[BM * HEAD_DIM + rloc] = -negm[qb][0];
+                pw[BM * HEAD_DIM + BM + rloc] = l;
+            }
+        } else if (row < S) {
+            const float inv = 1.0f / l;
             uint2* orow = out + (bh * S + row) * 32;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
@@ -323,373 +362,90 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     }
 }
 
-// ===========================================================================
-// Software-pipelined kernel: 4 waves x 64 queries (BM = 256), one wave per
-// SIMD.  Each K/V operand read from LDS feeds two MFMAs (two 32-query blocks),
-// halving LDS traffic per flop against the 32-query-per-wave kernel above.
-// With no second wave on the SIMD to hide latency, the wave overlaps its own
-// work in 32-key steps: step u runs the softmax of step u (VALU) interleaved
-// with S^T = K' Q'^T of step u+1 (MFMA), then O^T += V^T P^T of step u.  The
-// 64-key tiles stream through a ring of three LDS buffers, each tile loaded a
-// full tile-iteration before its first use.
-// ===========================================================================
-
-// Keep a value in the accumulation register file: the resident Q operands
-// live in AGPRs (MFMA reads its A/B operands from either file), which leaves
-// the architectural VGPRs to the scores, weights and softmax state.
-__device__ __forceinline__ bf16x8 pin_to_agpr(bf16x8 v) {
-    typedef int i32x4 __attribute__((ext_vector_type(4)));
-    i32x4 w = __builtin_bit_cast(i32x4, v);
-    asm volatile("" : "=a"(w) : "0"(w));
-    return __builtin_bit_cast(bf16x8, w);
-}
-
-constexpr int PL_NW = 4;
-constexpr int PL_QB = 2;
-// Per-lane, per-step weight sum beyond which the pass is redone with the
-// exact row max (each weight is then <= 2^40, l <= 2^57, far from overflow).
-constexpr float PL_SUM_LIMIT = 1099511627776.0f;  // 2^40
-constexpr int PL_BM = PL_NW * 32 * PL_QB;
-
-// Copy one tile HBM -> LDS: its K part to `kdst`, its V part to `vdst`.
-__device__ __forceinline__ void pl_load_tile(const uint4* __restrict__ src, uint4* kdst, uint4* vdst, int wave,
-                                             int lane) {
-    copy_to_lds_async<PL_NW, K_PART_CHUNKS>(src, kdst, wave, lane);
-    copy_to_lds_async<PL_NW, V_PART_CHUNKS>(src + K_PART_CHUNKS, vdst, wave, lane);
-}
-
-// Scores of key half `kb` (32 keys) of the tile at `kt`: 16 MFMAs, C starts
-// at -m.  Eight K reads, each feeding the two query blocks.
-__device__ __forceinline__ void pl_qk(const uint4* kt, int kb, int n, int hh, const bf16x8 (&qf)[PL_QB][8],
-                                      const f32x16 (&negm)[PL_QB], f32x16 (&sn)[PL_QB]) {
-    bf16x8 a[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) a[t] = as_bf16x8(kt[k_chunk(kb * 32 + n, 2 * t + hh)]);
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int qb = 0; qb < PL_QB; ++qb)
-            sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qf[qb][t], t == 0 ? negm[qb] : sn[qb], 0, 0, 0);
-}
-
-// O^T += V^T P^T over key half `kb` of the tile whose V part is at `vt`: 16 MFMAs.
-__device__ __forceinline__ void pl_pv(const uint4* vt, int kb, int n, int hh, const bf16x8 (&pf)[PL_QB][2],
-                                      f32x16 (&o)[PL_QB][4]) {
-    bf16x8 a[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t2 = i >> 2, db = i & 3;
-        a[i] = as_bf16x8(vt[v_chunk(db * 32 + n, 4 * kb + 2 * t2 + hh)]);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int qb = 0; qb < PL_QB; ++qb)
-            o[qb][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], pf[qb][i >> 2], o[qb][i & 3], 0, 0, 0);
-    // Two reads ahead; then two MFMAs per read.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-        if (i + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
-}
-
-__device__ __forceinline__ void pl_weights(const f32x16 (&sc)[PL_QB], bf16x8 (&pf)[PL_QB][2], float (&tsum)[PL_QB]) {
-#pragma unroll
-    for (int qb = 0; qb < PL_QB; ++qb) {
-        tsum[qb] = 0.0f;
-        exp_pack16(sc[qb], pf[qb], tsum[qb]);
-    }
-}
-
-__device__ __forceinline__ float pl_rowmax(const f32x16& sc) {
-    float mx = sc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    return swap_halves_max(mx);
-}
-
-__device__ __forceinline__ void pl_mask(f32x16 (&sc)[PL_QB], int key0, int S, int hh) {
-    const int base = key0 + 8 * hh;
-#pragma unroll
-    for (int qb = 0; qb < PL_QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (base + 16 * (r >> 3) + (r & 7) >= S) sc[qb][r] = -INFINITY;
-}
-
-// One 32-key step: weights of `sc` interleaved with the scores `sn` of the
-// next step (K part `knext`, key half kbn), then PV of this step (V part
-// `vcur`, key half kb).  With DO_NEXT = false the next scores are not computed.  A
-// lane whose step weights sum past PL_SUM_LIMIT (or are not finite) sets the
-// wave's overflow mask `ovf`.
-template <bool DO_NEXT>
-__device__ __forceinline__ void pl_step(const uint4* vcur, int kb, const uint4* knext, int kbn, int n, int hh,
-                                        const bf16x8 (&qf)[PL_QB][8], const f32x16 (&negm)[PL_QB],
-                                        f32x16 (&sc)[PL_QB], f32x16 (&sn)[PL_QB], f32x16 (&o)[PL_QB][4],
-                                        float (&lsum)[PL_QB], uint64_t& ovf) {
-    bf16x8 pf[PL_QB][2];
-    float tsum[PL_QB];
-    if (DO_NEXT) pl_qk(knext, kbn, n, hh, qf, negm, sn);
-    pl_weights(sc, pf, tsum);
-    if (DO_NEXT) {
-        // Two K reads ahead; then per read two MFMAs, each followed by four
-        // VALU slots (32 exp, 16 packs, 16 dot2 over the step), and the next read.
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            if (t + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-    }
-    ovf |= __builtin_amdgcn_ballot_w64(!(tsum[0] <= PL_SUM_LIMIT) || !(tsum[1] <= PL_SUM_LIMIT));
-    lsum[0] += tsum[0];
-    lsum[1] += tsum[1];
-    pl_pv(vcur, kb, n, hh, pf, o);
-}
-
-// Tile-iteration j (not the last): wait for tile j+1, prefetch tile j+2, then
-// step 2j (weights of sa || scores of tile j keys 32..63 into sb, PV tile j
-// keys 0..31) and step 2j+1 (weights of sb || scores of tile j+1 keys 0..31
-// into sa, PV tile j keys 32..63).  kc/vc: tile j; kn: K part of tile j+1;
-// kl/vl: where tile j+2 goes.
-__device__ __forceinline__ void pl_tile(int j, int L, const uint4* src, const uint4* kc, const uint4* vc,
-                                        const uint4* kn, uint4* kl, uint4* vl, int wave, int lane, int n, int hh,
-                                        const bf16x8 (&qf)[PL_QB][8], const f32x16 (&negm)[PL_QB],
-                                        f32x16 (&sa)[PL_QB], f32x16 (&sb)[PL_QB], f32x16 (&o)[PL_QB][4],
-                                        float (&lsum)[PL_QB], uint64_t& ovf) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 2 <= L) pl_load_tile(src + (int64_t)(j + 2) * TILE_CHUNKS, kl, vl, wave, lane);
-    pl_step<true>(vc, 0, kc, 1, n, hh, qf, negm, sa, sb, o, lsum, ovf);
-    pl_step<true>(vc, 1, kn, 0, n, hh, qf, negm, sb, sa, o, lsum, ovf);
-}
-
-// Exact row max of the scaled scores over all keys (for the rare second
-// attempt): stream every tile's K part through k0/k1 and take QK^T maxima.
-__device__ __forceinline__ void pl_exact_rowmax(const uint4* src, int L, int S, uint4* k0, uint4* k1, int wave,
-                                                int lane, int n, int hh, const bf16x8 (&qf)[PL_QB][8],
-                                                float (&mrow)[PL_QB]) {
-    const f32x16 zero[PL_QB] = {f32x16{}, f32x16{}};
-    mrow[0] = mrow[1] = -INFINITY;
-    for (int j = 0; j <= L; ++j) {
-        uint4* kt = (j & 1) ? k1 : k0;
-        __syncthreads();
-        copy_to_lds_async<PL_NW, K_PART_CHUNKS>(src + (int64_t)j * TILE_CHUNKS, kt, wave, lane);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x16 sc[PL_QB];
-            pl_qk(kt, kb, n, hh, qf, zero, sc);
-            pl_mask(sc, j * KV_TILE + 32 * kb, S, hh);
-#pragma unroll
-            for (int qb = 0; qb < PL_QB; ++qb) mrow[qb] = fmaxf(mrow[qb], pl_rowmax(sc[qb]));
-        }
-    }
-    __syncthreads();
-}
-
-__global__ __launch_bounds__(PL_NW * 64) void attn_fwd_pipelined_kernel(
-    const uint4* __restrict__ q, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
-    const uint4* __restrict__ ws, uint2* __restrict__ out, int S, int ntiles, int nqt, int total_wg, float qmul,
-    int has_rope) {
-    // Ring of three tiles; K parts and V parts in separate regions so that
-    // every operand address is one per-lane base plus an offset below 64 KiB.
-    __shared__ uint4 kb0[K_PART_CHUNKS];
-    __shared__ uint4 kb1[K_PART_CHUNKS];
-    __shared__ uint4 kb2[K_PART_CHUNKS];
-    __shared__ uint4 vb0[V_PART_CHUNKS];
-    __shared__ uint4 vb1[V_PART_CHUNKS];
-    __shared__ uint4 vb2[V_PART_CHUNKS];
-
-    const int x = blockIdx.x;
-    const int xcd = x & 7, slot = x >> 3;
-    const int per = total_wg >> 3, rem = total_wg & 7;
-    const int item = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+// Combine the nsplit key-range partials of each split item (the same streaming
+// softmax merge, exact): M = max m_f, O = sum 2^(m_f - M) O_f / sum 2^(m_f - M) l_f.
+// One workgroup per 16 rows of an item; 16 threads per row, 8 dims each.
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part, uint4* __restrict__ out,
+                                                         int S, int nqt, int item0, int nsplit) {
+    const int item_local = blockIdx.x / (BM / 16);
+    const int rloc = (blockIdx.x % (BM / 16)) * 16 + (threadIdx.x >> 4);
+    const int seg = threadIdx.x & 15;
+    const int item = item0 + item_local;
     const int64_t bh = item / nqt;
-    const int qt = item - (int)bh * nqt;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int n = lane & 31;
-    const int hh = lane >> 5;
-    const int L = ntiles - 1;
-
-    const uint4* src = ws + bh * (int64_t)ntiles * TILE_CHUNKS;
-    pl_load_tile(src, kb0, vb0, wave, lane);
-    if (L >= 1) pl_load_tile(src + TILE_CHUNKS, kb1, vb1, wave, lane);
-
-    // ---- Q prologue: RoPE, fold scale*log2(e), round to bf16, keep resident.
-    bf16x8 qf[PL_QB][8];
-#pragma unroll
-    for (int qb = 0; qb < PL_QB; ++qb) {
-        const int row = qt * PL_BM + (wave * PL_QB + qb) * 32 + n;
-        const bool ok = row < S;
-        const uint4* qrow = q + (bh * S + row) * 16;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int c = 2 * t + hh;
-            float f[8];
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (ok) w = qrow[c];
-            unpack8(w, f);
-            if (has_rope && ok) rotate4(f, cos_t[(int64_t)row * 16 + c], sin_t[(int64_t)row * 16 + c]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] *= qmul;
-            qf[qb][t] = pin_to_agpr(as_bf16x8(pack8(f)));
-        }
+    const int row = (item - (int)bh * nqt) * BM + rloc;
+    if (row >= S) return;
+    const float* p0 = part + (int64_t)item_local * nsplit * PART_FLOATS;
+    float M = -INFINITY;
+    for (int f = 0; f < nsplit; ++f) M = fmaxf(M, p0[(int64_t)f * PART_FLOATS + BM * HEAD_DIM + rloc]);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float L = 0.0f;
+    for (int f = 0; f < nsplit; ++f) {
+        const float* pf = p0 + (int64_t)f * PART_FLOATS;
+        const float w = __builtin_amdgcn_exp2f(pf[BM * HEAD_DIM + rloc] - M);
+        L += w * pf[BM * HEAD_DIM + BM + rloc];
+        const float4* src = reinterpret_cast<const float4*>(pf + (int64_t)rloc * HEAD_DIM + seg * 8);
+        const float4 a = src[0], b = src[1];
+        acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+        acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
     }
-
-    // Softmax offset m (base 2) per query, fixed for a whole pass: the exact
-    // row max of the first 32 keys.  If any weight of a later step exceeds
-    // 2^40 relative to it, the workgroup redoes the pass with the exact row max
-    // over all keys (second attempt), where no weight exceeds 1.
-    f32x16 o[PL_QB][4], negm[PL_QB], sa[PL_QB], sb[PL_QB];
-    float lsum[PL_QB];
-    float mrow[PL_QB] = {0.0f, 0.0f};
-    for (int attempt = 0;; ++attempt) {
+    const float inv = 1.0f / L;
 #pragma unroll
-        for (int qb = 0; qb < PL_QB; ++qb) {
-            negm[qb] = f32x16{} - mrow[qb];
-            lsum[qb] = 0.0f;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) o[qb][db] = f32x16{};
-        }
-        uint64_t ovf = 0;
-        if (attempt > 0) {
-            pl_load_tile(src, kb0, vb0, wave, lane);
-            if (L >= 1) pl_load_tile(src + TILE_CHUNKS, kb1, vb1, wave, lane);
-        }
-
-        // ---- first step's scores (tile 0, keys 0..31).
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        pl_qk(kb0, 0, n, hh, qf, negm, sa);
-        if (S < 32) pl_mask(sa, 0, S, hh);
-        if (attempt == 0) {
-#pragma unroll
-            for (int qb = 0; qb < PL_QB; ++qb) {
-                const float mx = pl_rowmax(sa[qb]);
-                sa[qb] -= mx;
-                negm[qb] -= mx;
-            }
-        }
-
-        // ---- tile-iterations 0 .. L-1, three per trip so each LDS buffer is a
-        // fixed object in each copy (tile j lives in buffer j mod 3).
-        int j = 0;
-        for (; j + 3 <= L; j += 3) {
-            pl_tile(j, L, src, kb0, vb0, kb1, kb2, vb2, wave, lane, n, hh, qf, negm, sa, sb, o, lsum, ovf);
-            pl_tile(j + 1, L, src, kb1, vb1, kb2, kb0, vb0, wave, lane, n, hh, qf, negm, sa, sb, o, lsum, ovf);
-            pl_tile(j + 2, L, src, kb2, vb2, kb0, kb1, vb1, wave, lane, n, hh, qf, negm, sa, sb, o, lsum, ovf);
-        }
-        if (j < L) {
-            pl_tile(j, L, src, kb0, vb0, kb1, kb2, vb2, wave, lane, n, hh, qf, negm, sa, sb, o, lsum, ovf);
-            ++j;
-            if (j < L) {
-                pl_tile(j, L, src, kb1, vb1, kb2, kb0, vb0, wave, lane, n, hh, qf, negm, sa, sb, o, lsum, ovf);
-                ++j;
-            }
-        }
-
-        // ---- last tile L (keys past S masked): step 2L (scores in sa) and 2L+1.
-        {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            const int r3 = L % 3;
-            const uint4* kc = r3 == 0 ? kb0 : (r3 == 1 ? kb1 : kb2);
-            const uint4* vc = r3 == 0 ? vb0 : (r3 == 1 ? vb1 : vb2);
-            const bool ragged = (S & (KV_TILE - 1)) != 0;
-            if (ragged) pl_mask(sa, L * KV_TILE, S, hh);
-            if (L * KV_TILE + 32 < S) {
-                pl_step<true>(vc, 0, kc, 1, n, hh, qf, negm, sa, sb, o, lsum, ovf);
-                if (ragged) pl_mask(sb, L * KV_TILE + 32, S, hh);
-                pl_step<false>(vc, 1, kc, 0, n, hh, qf, negm, sb, sa, o, lsum, ovf);
-            } else {
-                pl_step<false>(vc, 0, kc, 1, n, hh, qf, negm, sa, sb, o, lsum, ovf);
-            }
-        }
-
-        // Attempt 1 uses the exact maxima; it is final whatever its flags say
-        // (non-finite inputs propagate to the output).
-        if (!__syncthreads_or(ovf != 0) || attempt > 0) break;
-        pl_exact_rowmax(src, L, S, kb0, kb1, wave, lane, n, hh, qf, mrow);
-    }
-
-    // ---- epilogue: lane (n, hh), register r of dim block db holds dim
-    // 32 db + 8 (r >> 2) + 4 hh + (r & 3) of query n of block qb.
-#pragma unroll
-    for (int qb = 0; qb < PL_QB; ++qb) {
-        const float inv = 1.0f / swap_halves_sum(lsum[qb]);
-        const int row = qt * PL_BM + (wave * PL_QB + qb) * 32 + n;
-        if (row < S) {
-            uint2* orow = out + (bh * S + row) * 32;
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x16& acc = o[qb][db];
-                    orow[db * 8 + g * 2 + hh] =
-                        make_uint2(pack_bf16x2(acc[4 * g + 0] * inv, acc[4 * g + 1] * inv),
-                                   pack_bf16x2(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv));
-                }
-        }
-    }
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    out[(bh * S + row) * 16 + seg] = pack8(acc);
 }
 
-// Tile configurations (waves per workgroup, 32-query blocks per wave).
-struct CoreConfig {
-    int nw, qb;
+// How one call is laid out over the GPU: `full` items run whole-key-range
+// workgroups in full rounds; the remaining `split` items (fewer than a round)
+// run nsplit key-range workgroups each, merged afterwards.  Depends only on the
+// shape, so the workspace size is known on the host.
+struct CorePlan {
+    int nqt, ntiles, items, full, split, nsplit;
 };
 
-static int core_variant() {
-    static int v = -1;
-    if (v < 0) {
-        const char* e = getenv("DIT_ATTN_CORE_VARIANT");
-        v = e ? atoi(e) : 0;
-        if (v < 0 || v > 2) v = 0;
+static CorePlan core_plan(int BH, int S) {
+    CorePlan p;
+    p.ntiles = (int)num_kv_tiles(S);
+    p.nqt = (S + BM - 1) / BM;
+    p.items = BH * p.nqt;
+    const int rem = p.items % MI355X_CUS;
+    const int f = rem ? std::min(MI355X_CUS / rem, p.ntiles) : 1;
+    if (rem == 0 || f < 2) {
+        p.full = p.items;
+        p.split = 0;
+        p.nsplit = 1;
+    } else {
+        p.full = p.items - rem;
+        p.split = rem;
+        p.nsplit = f;
     }
-    return v;
+    return p;
 }
 
-int core_block_m() { return core_variant() == 1 ? 4 * 32 : 8 * 32; }  // both variants 1 and 2: see launchers
-
-template <int NW, int QB>
-static hipError_t launch_core_t(const void* q, const float* cos_t, const float* sin_t, const void* ws,
-                                void* out, int BH, int S, float qmul, hipStream_t stream) {
-    constexpr int BM = NW * 32 * QB;
-    const int ntiles = (int)num_kv_tiles(S);
-    const int nqt = (S + BM - 1) / BM;
-    const int total = BH * nqt;
-    attn_core_kernel<NW, QB><<<total, NW * 64, 0, stream>>>(
-        static_cast<const uint4*>(q), reinterpret_cast<const float4*>(cos_t),
-        reinterpret_cast<const float4*>(sin_t), static_cast<const uint4*>(ws), static_cast<uint2*>(out),
-        S, ntiles, nqt, total, qmul, cos_t != nullptr);
-    return hipGetLastError();
+size_t core_partial_bytes(int BH, int S) {
+    const CorePlan p = core_plan(BH, S);
+    return (size_t)p.split * p.nsplit * PART_FLOATS * sizeof(float);
 }
 
-static hipError_t launch_pipelined(const void* q, const float* cos_t, const float* sin_t, const void* ws,
-                                   void* out, int BH, int S, float qmul, hipStream_t stream) {
-    const int ntiles = (int)num_kv_tiles(S);
-    const int nqt = (S + PL_BM - 1) / PL_BM;
-    const int total = BH * nqt;
-    attn_fwd_pipelined_kernel<<<total, PL_NW * 64, 0, stream>>>(
-        static_cast<const uint4*>(q), reinterpret_cast<const float4*>(cos_t),
-        reinterpret_cast<const float4*>(sin_t), static_cast<const uint4*>(ws), static_cast<uint2*>(out),
-        S, ntiles, nqt, total, qmul, cos_t != nullptr);
-    return hipGetLastError();
-}
-
-hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws,
+hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
                             void* out, int BH, int S, float qmul, hipStream_t stream) {
-    if (core_variant() == 2) return launch_pipelined(q, cos_t, sin_t, ws, out, BH, S, qmul, stream);
-    if (core_variant() == 1) return launch_core_t<4, 1>(q, cos_t, sin_t, ws, out, BH, S, qmul, stream);
-    return launch_core_t<8, 1>(q, cos_t, sin_t, ws, out, BH, S, qmul, stream);
+    const CorePlan p = core_plan(BH, S);
+    const uint4* wsv = static_cast<const uint4*>(ws);
+    const uint4* qv = static_cast<const uint4*>(q);
+    const float4* cv = reinterpret_cast<const float4*>(cos_t);
+    const float4* sv = reinterpret_cast<const float4*>(sin_t);
+    const int rope = cos_t != nullptr;
+    if (p.full > 0) {
+        attn_core_kernel<false><<<p.full, NW * 64, 0, stream>>>(qv, cv, sv, wsv, static_cast<uint2*>(out), nullptr,
+                                                               S, p.ntiles, p.nqt, 0, 1, qmul, rope);
+    }
+    if (p.split > 0) {
+        float* pt = static_cast<float*>(part);
+        attn_core_kernel<true><<<p.split * p.nsplit, NW * 64, 0, stream>>>(
+            qv, cv, sv, wsv, nullptr, pt, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
+        attn_merge_kernel<<<p.split * (BM / 16), 256, 0, stream>>>(pt, static_cast<uint4*>(out), S, p.nqt, p.full,
+                                                                  p.nsplit);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace dit

@@ -42,11 +42,26 @@ def test_library_exports_every_declared_symbol():
     assert dj.dit_abi_version() == 1
 
 
+def _expected_workspace(B, H, S):
+    """Tile stream (35 KiB per 64-key tile per (batch, head), rounded up to 256 B)
+    plus the key-range partials: items = B*H*ceil(S/256) query tiles; the r = items
+    mod 256 items past the last full round of 256 CUs run split into
+    f = min(256 // r, ntiles) key ranges when f >= 2, each range keeping
+    256 x 128 + 2 x 256 fp32 values."""
+    ntiles = -(-S // 64)
+    tiles = (B * H * ntiles * 35840 + 255) // 256 * 256
+    items = B * H * -(-S // 256)
+    r = items % 256
+    f = min(256 // r, ntiles) if r else 1
+    part = r * f * (256 * 128 + 512) * 4 if (r and f >= 2) else 0
+    return tiles + part
+
+
 def test_workspace_bytes():
-    # 64-key tiles of 35 KiB (padded K and V^T parts) per (batch, head); 0 on unsupported sizes.
-    assert dj.dit_attn_workspace_bytes(1, 24, 16896, 128) == 24 * 264 * 35840
-    assert dj.dit_attn_workspace_bytes(2, 3, 65, 128) == 6 * 2 * 35840
+    assert dj.dit_attn_workspace_bytes(1, 24, 16896, 128) == 24 * 264 * 35840 + 48 * 5 * 33280 * 4
     assert dj.dit_attn_workspace_bytes(1, 1, 1, 128) == 35840
+    for B, H, S in [(1, 24, 16896), (2, 3, 65), (1, 1, 1), (1, 24, 3584), (1, 10, 76112), (1, 2, 320), (3, 7, 999)]:
+        assert dj.dit_attn_workspace_bytes(B, H, S, 128) == _expected_workspace(B, H, S), (B, H, S)
     assert dj.dit_attn_workspace_bytes(1, 1, 0, 128) == 0
     assert dj.dit_attn_workspace_bytes(1, 1, 64, 64) == 0
 
