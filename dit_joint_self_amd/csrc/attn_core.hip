@@ -115,6 +115,9 @@ __device__ __forceinline__ void exp_pack16(const f32x16& sc, bf16x8 (&pf)[2], fl
 // final O / l does not depend on when m moves.
 constexpr float SUM_LIMIT = 1048576.0f;  // 2^20
 
+// MFMA operand ring: LDS reads run RING - 1 MFMA steps ahead of their use.
+constexpr int RING = 4;
+
 template <int QB, bool MASKED>
 __device__ __forceinline__ void attn_tile(const uint4* kt, int j, bool first, int S, int n, int hh,
                                           const bf16x8 (&qf)[QB][8], f32x16 (&o)[QB][4],
@@ -123,24 +126,25 @@ __device__ __forceinline__ void attn_tile(const uint4* kt, int j, bool first, in
 
     // ---- S'^T = K' Q'^T - m for 64 keys x (32 * QB) queries: 16 MFMA steps
     // i = (dim step t = i / 2, key block kb = i % 2).  K operands rotate
-    // through a 3-slot ring read two steps ahead; the scheduling fences keep
-    // the compiler from sinking the reads back to their use.
+    // through a ring read RING - 1 steps ahead; the scheduling fences keep the
+    // compiler from sinking the reads back to their use.
     f32x16 s[QB][2];
     {
-        bf16x8 ring[3];
-        ring[0] = as_bf16x8(kt[k_chunk(n, hh)]);
-        ring[1] = as_bf16x8(kt[k_chunk(32 + n, hh)]);
+        bf16x8 ring[RING];
+#pragma unroll
+        for (int i0 = 0; i0 < RING - 1; ++i0)
+            ring[i0] = as_bf16x8(kt[k_chunk((i0 & 1) * 32 + n, 2 * (i0 >> 1) + hh)]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            if (i + 2 < 16) {
-                const int t2 = (i + 2) >> 1, kb2 = (i + 2) & 1;
-                ring[(i + 2) % 3] = as_bf16x8(kt[k_chunk(kb2 * 32 + n, 2 * t2 + hh)]);
+            if (i + RING - 1 < 16) {
+                const int t2 = (i + RING - 1) >> 1, kb2 = (i + RING - 1) & 1;
+                ring[(i + RING - 1) % RING] = as_bf16x8(kt[k_chunk(kb2 * 32 + n, 2 * t2 + hh)]);
             }
             __builtin_amdgcn_sched_barrier(0);
             const int t = i >> 1, kb = i & 1;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
-                s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % 3], qf[qb][t],
+                s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % RING], qf[qb][t],
                                                                     t == 0 ? negm[qb] : s[qb][kb], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -198,20 +202,21 @@ __device__ __forceinline__ void attn_tile(const uint4* kt, int j, bool first, in
     // steps i = (16-key step u = i / 4, dim block db = i % 4), V^T operands
     // through the same kind of ring.
     {
-        bf16x8 ring[3];
-        ring[0] = as_bf16x8(vt[v_chunk(n, hh)]);
-        ring[1] = as_bf16x8(vt[v_chunk(32 + n, hh)]);
+        bf16x8 ring[RING];
+#pragma unroll
+        for (int i0 = 0; i0 < RING - 1; ++i0)
+            ring[i0] = as_bf16x8(vt[v_chunk((i0 & 3) * 32 + n, 2 * (i0 >> 2) + hh)]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            if (i + 2 < 16) {
-                const int u2 = (i + 2) >> 2, db2 = (i + 2) & 3;
-                ring[(i + 2) % 3] = as_bf16x8(vt[v_chunk(db2 * 32 + n, 2 * u2 + hh)]);
+            if (i + RING - 1 < 16) {
+                const int u2 = (i + RING - 1) >> 2, db2 = (i + RING - 1) & 3;
+                ring[(i + RING - 1) % RING] = as_bf16x8(vt[v_chunk(db2 * 32 + n, 2 * u2 + hh)]);
             }
             __builtin_amdgcn_sched_barrier(0);
             const int u = i >> 2, db = i & 3;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
-                o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % 3], pf[qb][u >> 1][u & 1], o[qb][db],
+                o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % RING], pf[qb][u >> 1][u & 1], o[qb][db],
                                                                     0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
