@@ -29,8 +29,9 @@ METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=16896,H=24,D=128 (1 GPU
 # HBM bytes per attention-kernel launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (scaled by a plain-copy calibration), keyed by the hash of the kernel sources they were
 # taken on and by workload; reported as roofline.traffic only while the sources match.
-KERNEL_SOURCES = ["dit_joint_self_amd/csrc/attn_core.hip", "dit_joint_self_amd/csrc/tile_layout.h",
-                  "dit_joint_self_amd/csrc/bf16_util.h"]
+KERNEL_SOURCES = ["dit_joint_self_amd/csrc/attn_core.hip", "dit_joint_self_amd/csrc/attn_core_fp8.hip",
+                  "dit_joint_self_amd/csrc/attn_common.h", "dit_joint_self_amd/csrc/tile_layout.h",
+                  "dit_joint_self_amd/csrc/bf16_util.h", "dit_joint_self_amd/csrc/fp8_util.h"]
 MEASURED_TRAFFIC = {
     ("4570db5b9355adc5", "flux2048"): {"read_bytes": 995.0e6, "write_bytes": 103.8e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
@@ -46,6 +47,7 @@ def kernel_sources_hash() -> str:
             h.update(fh.read())
     return h.hexdigest()[:16]
 BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+FP8_PEAK_TFLOPS = 5033.2    # 256 CU x 8192 flop/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 
 
@@ -54,7 +56,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="flux2048", choices=[n for n in W.WORKLOADS if "fp8" not in n])
+    ap.add_argument("--workload", default="flux2048", choices=list(W.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -86,9 +88,10 @@ def bf16_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
 
 
-def cpu_baseline(w, qb, kb, vb, budget_s):
+def cpu_baseline(w, f64_head, budget_s):
     """The float64 oracle as it stands, on the first query rows of successive
-    heads until the time budget is spent; TFLOP/s at 4 * rows * S * D flop."""
+    heads until the time budget is spent; TFLOP/s at 4 * rows * S * D flop.
+    ``f64_head(h)`` returns the head's (q, k, v) as float64 [1, 1, S, D]."""
     from oracle import joint_attention, rope_angles
     try:
         from threadpoolctl import threadpool_info
@@ -102,10 +105,7 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
     done_rows = 0
     heads = 0
     for h in range(w.H):
-        sl = slice(h, h + 1)
-        q = W.bf16_bits_to_f32(qb[:, sl]).astype(np.float64)
-        k = W.bf16_bits_to_f32(kb[:, sl]).astype(np.float64)
-        v = W.bf16_bits_to_f32(vb[:, sl]).astype(np.float64)
+        q, k, v = f64_head(h)
         joint_attention(q, k, v, ang, rows=rows)
         done_rows += rows_per_head
         heads += 1
@@ -135,23 +135,41 @@ def main():
         copy_calibration(args, torch)
         return
     w = W.get(args.workload)
-    print(f"[bench] workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D}", file=sys.stderr, flush=True)
-    qb, kb, vb = W.make_bf16_inputs(w)
-    q, k, v = bf16_dev(qb, torch), bf16_dev(kb, torch), bf16_dev(vb, torch)
+    fp8 = w.dtype == "fp8_e4m3"
+    print(f"[bench] workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype}", file=sys.stderr, flush=True)
     pos = torch.from_numpy(W.positions(w)).to("cuda")
     cos, sin = dj.dit_rope_tables(pos, w.axes_dim, w.theta)
-    out = torch.empty_like(q)
-    ws_bytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     scale = 1.0 / math.sqrt(w.D)
     stream = torch.cuda.current_stream()
-
-    def step():
-        dj.dit_attn_prepare_kv(k, v, cos, sin, ws, ws_bytes, stream=stream)
-        dj.dit_attn_core(q, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes, stream=stream)
+    if fp8:
+        from oracle.fp8 import dequantize
+        (q8, sq), (k8, sk), (v8, sv) = [W.fp8_e4m3_quantize(x) for x in W.draw_qkv_f32(w)]
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(c)).to("cuda") for c in (q8, k8, v8))
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+        ws_bytes = dj.dit_attn_workspace_bytes_fp8(w.B, w.H, w.S, w.D)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        prep = lambda: dj.dit_attn_prepare_kv_fp8(k, v, sk, sv, cos, sin, ws, ws_bytes, stream=stream)
+        core = lambda: dj.dit_attn_core_fp8(q, sq, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes,
+                                            stream=stream)
+        forward = lambda: dj.dit_attn_forward_fp8(q, k, v, sq, sk, sv, cos, sin, out=out, S_txt=w.S_txt,
+                                                  scale=scale)
+        f64_head = lambda h: tuple(dequantize(c[:, h:h + 1], s_) for c, s_ in ((q8, sq), (k8, sk), (v8, sv)))
+        peak = FP8_PEAK_TFLOPS
+    else:
+        qb, kb, vb = W.make_bf16_inputs(w)
+        q, k, v = bf16_dev(qb, torch), bf16_dev(kb, torch), bf16_dev(vb, torch)
+        out = torch.empty_like(q)
+        ws_bytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        prep = lambda: dj.dit_attn_prepare_kv(k, v, cos, sin, ws, ws_bytes, stream=stream)
+        core = lambda: dj.dit_attn_core(q, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes, stream=stream)
+        forward = lambda: dj.dit_attn_forward(q, k, v, cos, sin, out=out, S_txt=w.S_txt, scale=scale)
+        f64_head = lambda h: tuple(W.bf16_bits_to_f32(b[:, h:h + 1]).astype(np.float64) for b in (qb, kb, vb))
+        peak = BF16_PEAK_TFLOPS
 
     for _ in range(args.warmup):
-        step()
+        prep()
+        core()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -160,9 +178,9 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
-        dj.dit_attn_prepare_kv(k, v, cos, sin, ws, ws_bytes, stream=stream)
+        prep()
         ev[i][1].record(stream)
-        dj.dit_attn_core(q, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes, stream=stream)
+        core()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -170,13 +188,13 @@ def main():
     core_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
     step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
 
-    # dit_attn_forward itself (allocating its workspace from the stream pool), for reference.
+    # The allocating entry point itself (workspace from the stream pool), for reference.
     for _ in range(2):
-        dj.dit_attn_forward(q, k, v, cos, sin, out=out, S_txt=w.S_txt, scale=scale)
+        forward()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(K):
-        dj.dit_attn_forward(q, k, v, cos, sin, out=out, S_txt=w.S_txt, scale=scale)
+        forward()
     e1.record(stream)
     torch.cuda.synchronize()
     fwd_ms = e0.elapsed_time(e1) / K
@@ -185,9 +203,7 @@ def main():
     from oracle import joint_attention, rope_angles
     rows = np.array([0, 1, w.S_txt - 1, w.S_txt, w.S // 2, w.S - 1])
     ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
-    ref = joint_attention(W.bf16_bits_to_f32(qb[:, :1]).astype(np.float64),
-                          W.bf16_bits_to_f32(kb[:, :1]).astype(np.float64),
-                          W.bf16_bits_to_f32(vb[:, :1]).astype(np.float64), ang, rows=rows)
+    ref = joint_attention(*f64_head(0), ang, rows=rows)
     got_bits = out[:, :1, torch.from_numpy(rows).to("cuda")].cpu().view(torch.int16).numpy().view(np.uint16)
     spot_err = float(np.abs(W.bf16_bits_to_f32(got_bits) - ref).max())
 
@@ -198,7 +214,7 @@ def main():
     core_avg = float(np.mean(core_ms))
     prep_avg = float(np.mean(prep_ms))
     achieved = flops / (core_avg * 1e-3) / 1e12
-    tensor_bytes = w.B * w.H * w.S * w.D * 2
+    tensor_bytes = w.B * w.H * w.S * w.D * (1 if fp8 else 2)
     prep_bytes = 4 * tensor_bytes + 2 * w.S * (w.D // 2) * 4  # read K, V, cos, sin; write 2 tensors of tiles
     rec = {
         "metric": METRIC,
@@ -211,13 +227,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S_txt": w.S_txt, "S_img": w.S_img, "S": w.S,
                    "D": w.D, "rope_axes": list(w.axes_dim), "non_causal": True},
-        "pct_of_bf16_peak": 100.0 * flops / (step_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        "roofline": {"bound": "mfma", "kernel": "attn_core_kernel", "achieved": achieved,
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+        "pct_of_peak": 100.0 * flops / (step_ms * 1e-3) / 1e12 / peak,
+        "roofline": {"bound": "mfma", "kernel": "attn_core_fp8_kernel" if fp8 else "attn_core_kernel",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "traffic_unit": "HBM bytes per launch (read + write)",
                      "avg_ms": core_avg, "kernel_sources": src_hash},
         "stages_ms": {"prepare_kv": prep_avg, "attn_core": core_avg,
@@ -228,7 +244,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, f64_head, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 

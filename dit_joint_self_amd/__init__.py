@@ -16,7 +16,8 @@ from typing import Optional, Sequence
 __all__ = [
     "LIB_PATH", "DitAttnError", "lib", "lib_loaded", "dit_last_error", "dit_abi_version",
     "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_kv",
-    "dit_attn_core", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
+    "dit_attn_core", "dit_attn_workspace_bytes_fp8", "dit_attn_prepare_kv_fp8", "dit_attn_core_fp8",
+    "dit_attn_forward_fp8", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
     "DIT_ERR_NO_DEVICE", "DIT_ERR_OUT_OF_MEMORY", "DIT_ERR_LAUNCH", "DIT_DTYPE_BF16",
     "DIT_DTYPE_FP8_E4M3",
 ]
@@ -49,6 +50,10 @@ _SIGNATURES = {
     "dit_attn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "dit_attn_prepare_kv": (_I, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P]),
     "dit_attn_core": (_I, [_P, _P, _P, _P, ctypes.c_size_t, _P, _I, _I, _I, _I, _F, _P]),
+    "dit_attn_workspace_bytes_fp8": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "dit_attn_prepare_kv_fp8": (_I, [_P, _P, _F, _F, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P]),
+    "dit_attn_core_fp8": (_I, [_P, _F, _P, _P, _P, ctypes.c_size_t, _P, _I, _I, _I, _I, _F, _P]),
+    "dit_attn_forward_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -172,4 +177,55 @@ def dit_attn_core(q, rope_cos, rope_sin, workspace, out, scale: Optional[float] 
         workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib().dit_attn_core(_ptr(q), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace), int(workspace_bytes),
                                _ptr(out), B, H, S, D, float(scale), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------- fp8 (e4m3 codes + per-tensor scales)
+
+def _shape8(t):
+    """[B, H, S, D] of an e4m3 code tensor (uint8 or float8_e4m3fn)."""
+    return tuple(int(x) for x in t.shape)
+
+
+def dit_attn_workspace_bytes_fp8(B: int, H: int, S: int, D: int) -> int:
+    return int(lib().dit_attn_workspace_bytes_fp8(B, H, S, D))
+
+
+def dit_attn_prepare_kv_fp8(k8, v8, k_scale: float, v_scale: float, rope_cos, rope_sin, workspace,
+                            workspace_bytes: Optional[int] = None, stream=None):
+    B, H, S, D = _shape8(k8)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().dit_attn_prepare_kv_fp8(_ptr(k8), _ptr(v8), float(k_scale), float(v_scale), _ptr(rope_cos),
+                                         _ptr(rope_sin), _ptr(workspace), int(workspace_bytes), B, H, S, D,
+                                         _stream(stream)))
+
+
+def dit_attn_core_fp8(q8, q_scale: float, rope_cos, rope_sin, workspace, out, scale: Optional[float] = None,
+                      workspace_bytes: Optional[int] = None, stream=None):
+    B, H, S, D = _shape8(q8)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().dit_attn_core_fp8(_ptr(q8), float(q_scale), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace),
+                                   int(workspace_bytes), _ptr(out), B, H, S, D, float(scale), _stream(stream)))
+    return out
+
+
+def dit_attn_forward_fp8(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float, rope_cos=None, rope_sin=None,
+                         out=None, S_txt: int = 0, S_img: Optional[int] = None, scale: Optional[float] = None,
+                         stream=None):
+    """Joint self-attention on e4m3 codes [B, H, S, D] with per-tensor scales; bf16 output."""
+    import torch
+    B, H, S, D = _shape8(q8)
+    if S_img is None:
+        S_img = S - S_txt
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=q8.device)
+    _check(lib().dit_attn_forward_fp8(_ptr(q8), _ptr(k8), _ptr(v8), float(q_scale), float(k_scale), float(v_scale),
+                                      _ptr(rope_cos), _ptr(rope_sin), _ptr(out), B, H, S_txt, S_img, D,
+                                      float(scale), _stream(stream)))
     return out

@@ -24,6 +24,11 @@ hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, c
 hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
                             void* out, int BH, int S, float qmul, hipStream_t stream);
 size_t core_partial_bytes(int BH, int S);
+hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_t, const float* sin_t, void* ws,
+                                 int BH, int S, float k_scale, float v_scale, hipStream_t stream);
+hipError_t launch_attn_core_fp8(const void* q, float q_scale, const float* cos_t, const float* sin_t, const void* ws,
+                                void* part, void* out, int BH, int S, float qmul, hipStream_t stream);
+size_t core_fp8_partial_bytes(int BH, int S);
 hipError_t launch_rope_tables(const int32_t* pos, int S, int n_axes, const int32_t* axes_dim,
                               double theta, float* cos_t, float* sin_t, hipStream_t stream);
 }  // namespace dit
@@ -207,6 +212,112 @@ dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* ro
                     "attn_core_kernel");
 }
 
+// ---------------------------------------------------------------- fp8
+
+static size_t fp8_tiles_bytes(int B, int H, int S) {
+    return (dit::F8_HEADER_BYTES + (size_t)B * H * (size_t)dit::num_kv_tiles(S) * dit::F8_TILE_BYTES + 255) &
+           ~(size_t)255;
+}
+
+static dit_status_t check_scale(float s, const char* name) {
+    if (!(s > 0.0f) || !std::isfinite(s)) return fail(DIT_ERR_INVALID_ARG, "%s must be finite and > 0", name);
+    return DIT_OK;
+}
+
+size_t dit_attn_workspace_bytes_fp8(int B, int H, int S, int D) {
+    if (B < 1 || H < 1 || S < 1 || D != dit::HEAD_DIM) return 0;
+    if (check_shape(B, H, S, D) != DIT_OK) return 0;
+    return fp8_tiles_bytes(B, H, S) + dit::core_fp8_partial_bytes(B * H, S);
+}
+
+dit_status_t dit_attn_prepare_kv_fp8(const void* k8, const void* v8, float k_scale, float v_scale,
+                                     const float* rope_cos, const float* rope_sin, void* workspace,
+                                     size_t workspace_bytes, int B, int H, int S, int D, void* stream) {
+    if (!k8 || !v8 || !workspace) return fail(DIT_ERR_INVALID_ARG, "k8, v8 and workspace must be non-NULL");
+    dit_status_t st = check_shape(B, H, S, D);
+    if (st != DIT_OK) return st;
+    if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
+    if ((st = check_scale(k_scale, "k_scale")) != DIT_OK || (st = check_scale(v_scale, "v_scale")) != DIT_OK)
+        return st;
+    if (!aligned16(k8) || !aligned16(v8)) return fail(DIT_ERR_INVALID_ARG, "k8 and v8 must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(DIT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t need = dit_attn_workspace_bytes_fp8(B, H, S, D);
+    if (workspace_bytes < need)
+        return fail(DIT_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+    const size_t tbytes = (size_t)B * H * S * D;
+    if (overlaps(workspace, need, k8, tbytes) || overlaps(workspace, need, v8, tbytes))
+        return fail(DIT_ERR_INVALID_ARG, "workspace overlaps k8 or v8");
+    if ((st = check_device()) != DIT_OK) return st;
+    return launched(dit::launch_prepare_kv_fp8(k8, v8, rope_cos, rope_sin, workspace, B * H, S, k_scale, v_scale,
+                                               static_cast<hipStream_t>(stream)),
+                    "prepare_kv_fp8_kernel");
+}
+
+dit_status_t dit_attn_core_fp8(const void* q8, float q_scale, const float* rope_cos, const float* rope_sin,
+                               const void* workspace, size_t workspace_bytes, void* out, int B, int H, int S, int D,
+                               float scale, void* stream) {
+    if (!q8 || !workspace || !out) return fail(DIT_ERR_INVALID_ARG, "q8, workspace and out must be non-NULL");
+    dit_status_t st = check_shape(B, H, S, D);
+    if (st != DIT_OK) return st;
+    if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
+    if ((st = check_scale(q_scale, "q_scale")) != DIT_OK) return st;
+    if (!std::isfinite(scale)) return fail(DIT_ERR_INVALID_ARG, "scale must be finite");
+    if (!aligned16(q8) || !aligned16(out)) return fail(DIT_ERR_INVALID_ARG, "q8 and out must be 16-byte aligned");
+    const size_t need = dit_attn_workspace_bytes_fp8(B, H, S, D);
+    if (workspace_bytes < need)
+        return fail(DIT_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+    const size_t obytes = (size_t)B * H * S * D * 2;
+    if (overlaps(out, obytes, q8, (size_t)B * H * S * D) || overlaps(out, obytes, workspace, need))
+        return fail(DIT_ERR_INVALID_ARG, "out overlaps q8 or the workspace");
+    if ((st = check_device()) != DIT_OK) return st;
+    const float qmul = (float)((double)scale * 1.4426950408889634073599);
+    void* part = static_cast<char*>(const_cast<void*>(workspace)) + fp8_tiles_bytes(B, H, S);
+    return launched(dit::launch_attn_core_fp8(q8, q_scale, rope_cos, rope_sin, workspace, part, out, B * H, S, qmul,
+                                              static_cast<hipStream_t>(stream)),
+                    "attn_core_fp8_kernel");
+}
+
+dit_status_t dit_attn_forward_fp8(const void* q8, const void* k8, const void* v8, float q_scale, float k_scale,
+                                  float v_scale, const float* rope_cos, const float* rope_sin, void* out, int B,
+                                  int H, int S_txt, int S_img, int D, float scale, void* stream) {
+    if (!q8 || !k8 || !v8 || !out) return fail(DIT_ERR_INVALID_ARG, "q8, k8, v8 and out must be non-NULL");
+    if (S_txt < 0 || S_img < 0)
+        return fail(DIT_ERR_INVALID_ARG, "S_txt and S_img must be >= 0 (got %d, %d)", S_txt, S_img);
+    if ((int64_t)S_txt + S_img > INT_MAX) return fail(DIT_ERR_INVALID_ARG, "S_txt + S_img overflows int");
+    const int S = S_txt + S_img;
+    dit_status_t st = check_shape(B, H, S, D);
+    if (st != DIT_OK) return st;
+    if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
+    if ((st = check_scale(q_scale, "q_scale")) != DIT_OK || (st = check_scale(k_scale, "k_scale")) != DIT_OK ||
+        (st = check_scale(v_scale, "v_scale")) != DIT_OK)
+        return st;
+    if (!std::isfinite(scale)) return fail(DIT_ERR_INVALID_ARG, "scale must be finite");
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(out))
+        return fail(DIT_ERR_INVALID_ARG, "q8, k8, v8 and out must be 16-byte aligned");
+    const size_t ibytes = (size_t)B * H * S * D, obytes = ibytes * 2;
+    if (overlaps(out, obytes, q8, ibytes) || overlaps(out, obytes, k8, ibytes) || overlaps(out, obytes, v8, ibytes))
+        return fail(DIT_ERR_INVALID_ARG, "out overlaps an input");
+    if ((st = check_device()) != DIT_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t need = dit_attn_workspace_bytes_fp8(B, H, S, D);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, need, s) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return fail(DIT_ERR_OUT_OF_MEMORY, "hipMallocAsync of %zu workspace bytes failed", need);
+    }
+    hipError_t e = dit::launch_prepare_kv_fp8(k8, v8, rope_cos, rope_sin, ws, B * H, S, k_scale, v_scale, s);
+    if (e == hipSuccess) {
+        const float qmul = (float)((double)scale * 1.4426950408889634073599);
+        e = dit::launch_attn_core_fp8(q8, q_scale, rope_cos, rope_sin, ws, static_cast<char*>(ws) + fp8_tiles_bytes(B, H, S),
+                                      out, B * H, S, qmul, s);
+    }
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess) return launched(e, "dit_attn_forward_fp8 kernels");
+    return launched(ef, "hipFreeAsync of the workspace");
+}
+
 dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const float* rope_cos,
                               const float* rope_sin, void* out, int B, int H, int S_txt, int S_img, int D,
                               float scale, dit_dtype_t dtype, void* stream) {
@@ -219,7 +330,7 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const
     if (st != DIT_OK) return st;
     if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
     if (dtype == DIT_DTYPE_FP8_E4M3)
-        return fail(DIT_ERR_UNSUPPORTED, "fp8 inputs are not taken by dit_attn_forward");
+        return fail(DIT_ERR_UNSUPPORTED, "fp8 inputs go through dit_attn_forward_fp8 (it takes their scales)");
     if (dtype != DIT_DTYPE_BF16) return fail(DIT_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
     if (!std::isfinite(scale)) return fail(DIT_ERR_INVALID_ARG, "scale must be finite");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))

@@ -1,0 +1,105 @@
+// attn_common.h - pieces shared by the bf16 and fp8 attention kernels:
+// workgroup shape, launch plan, key-range partial format, XCD-aware workgroup
+// order, direct-to-LDS copies and the half-wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "tile_layout.h"
+
+namespace dit {
+
+constexpr int NW = 8;                 // waves per workgroup (two per SIMD)
+constexpr int QB = 1;                 // 32-query blocks per wave
+constexpr int BM = NW * 32 * QB;      // queries per workgroup
+constexpr int MI355X_CUS = 256;       // workgroups resident at once (one per CU)
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));   // one 32x32 MFMA accumulator
+
+// Materialise an accumulator here, with every lane active.  An MFMA reads its
+// operands from all 64 lanes; if the compiler sank the last products into a
+// branch taken by only some lanes (the store guard row < S of the epilogue),
+// the inactive lanes' operand rows would be lost.  The empty volatile asm
+// reads and writes the value, so every product feeding it stays before it.
+__device__ __forceinline__ void settle(f32x16& x) { asm volatile("" : "+v"(x)); }
+
+// Partial results of one key-range workgroup: O (unnormalised, fp32, row-major
+// [BM][128]), then the offset m (base 2) and the weight sum l of each row.
+constexpr int PART_FLOATS = BM * HEAD_DIM + 2 * BM;
+
+// Workgroup x of a launch -> logical index.  Workgroups are dispatched
+// round-robin over the 8 XCDs; give each XCD a contiguous range of logical
+// indices so the workgroups sharing an XCD's L2 stream the same head's K/V.
+__device__ __forceinline__ int xcd_remap(int x, int total) {
+    const int xcd = x & 7, slot = x >> 3;
+    const int per = total >> 3, rem = total & 7;
+    return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+}
+
+__device__ __forceinline__ float swap_halves_max(float x) {
+    // v_permlane32_swap exchanges lanes 0-31 of one operand with lanes 32-63 of
+    // the other; with both operands = x, the two results hold x of this lane
+    // and of lane ^ 32 (in some order).
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float swap_halves_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Copy `chunks` 16-byte chunks (a multiple of 64) HBM -> LDS: wave w copies
+// the 1 KiB pieces w, w + NW, ...; each lane moves 16 bytes per piece.
+template <int NW, int CHUNKS>
+__device__ __forceinline__ void copy_to_lds_async(const uint4* __restrict__ src, uint4* lds_dst, int wave,
+                                                  int lane) {
+    static_assert(CHUNKS % 64 == 0, "whole 1 KiB pieces");
+#pragma unroll
+    for (int i = 0; i < (CHUNKS / 64 + NW - 1) / NW; ++i) {
+        const int piece = i * NW + wave;
+        if (piece < CHUNKS / 64) {
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(src + piece * 64 + lane),
+                (__attribute__((address_space(3))) void*)(lds_dst + piece * 64), 16, 0, 0);
+        }
+    }
+}
+
+// How one call is laid out over the GPU: `full` items run whole-key-range
+// workgroups in full rounds; the remaining `split` items (fewer than a round)
+// run nsplit key-range workgroups each, merged afterwards.  Depends only on the
+// shape, so the workspace size is known on the host.
+struct CorePlan {
+    int nqt, ntiles, items, full, split, nsplit;
+};
+
+inline CorePlan core_plan(int BH, int S) {
+    CorePlan p;
+    p.ntiles = (int)num_kv_tiles(S);
+    p.nqt = (S + BM - 1) / BM;
+    p.items = BH * p.nqt;
+    const int rem = p.items % MI355X_CUS;
+    const int f = rem ? std::min(MI355X_CUS / rem, p.ntiles) : 1;
+    if (rem == 0 || f < 2) {
+        p.full = p.items;
+        p.split = 0;
+        p.nsplit = 1;
+    } else {
+        p.full = p.items - rem;
+        p.split = rem;
+        p.nsplit = f;
+    }
+    return p;
+}
+
+inline size_t core_partial_bytes_for(const CorePlan& p) {
+    return (size_t)p.split * p.nsplit * PART_FLOATS * sizeof(float);
+}
+
+hipError_t launch_merge(const float* part, void* out, int S, int nqt, int item0, int nsplit, int split_items,
+                        hipStream_t stream);
+
+}  // namespace dit

@@ -36,47 +36,15 @@
 
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
-
+#include "attn_common.h"
 #include "bf16_util.h"
 #include "tile_layout.h"
 
 namespace dit {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
-
-__device__ __forceinline__ float swap_halves_max(float x) {
-    // v_permlane32_swap exchanges lanes 0-31 of one operand with lanes 32-63 of
-    // the other; with both operands = x, the two results hold x of this lane
-    // and of lane ^ 32 (in some order).
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float swap_halves_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Copy `chunks` 16-byte chunks (a multiple of 64) HBM -> LDS: wave w copies
-// the 1 KiB pieces w, w + NW, ...; each lane moves 16 bytes per piece.
-template <int NW, int CHUNKS>
-__device__ __forceinline__ void copy_to_lds_async(const uint4* __restrict__ src, uint4* lds_dst, int wave,
-                                                  int lane) {
-    static_assert(CHUNKS % 64 == 0, "whole 1 KiB pieces");
-#pragma unroll
-    for (int i = 0; i < (CHUNKS / 64 + NW - 1) / NW; ++i) {
-        const int piece = i * NW + wave;
-        if (piece < CHUNKS / 64) {
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(src + piece * 64 + lane),
-                (__attribute__((address_space(3))) void*)(lds_dst + piece * 64), 16, 0, 0);
-        }
-    }
-}
 
 template <int NW>
 __device__ __forceinline__ void load_tile_async(const uint4* __restrict__ src, uint4* lds_dst,
@@ -223,24 +191,6 @@ __device__ __forceinline__ void attn_tile(const uint4* kt, int j, bool first, in
     }
 }
 
-constexpr int NW = 8;                 // waves per workgroup (two per SIMD)
-constexpr int QB = 1;                 // 32-query blocks per wave
-constexpr int BM = NW * 32 * QB;      // queries per workgroup
-constexpr int MI355X_CUS = 256;       // workgroups resident at once (one per CU)
-
-// Partial results of one key-range workgroup: O (unnormalised, fp32, row-major
-// [BM][128]), then the offset m (base 2) and the weight sum l of each row.
-constexpr int PART_FLOATS = BM * HEAD_DIM + 2 * BM;
-
-// Workgroup x of a launch -> logical index.  Workgroups are dispatched
-// round-robin over the 8 XCDs; give each XCD a contiguous range of logical
-// indices so the workgroups sharing an XCD's L2 stream the same head's K/V.
-__device__ __forceinline__ int xcd_remap(int x, int total) {
-    const int xcd = x & 7, slot = x >> 3;
-    const int per = total >> 3, rem = total & 7;
-    return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
-}
-
 // One workgroup = BM queries of one (batch, head) against the key tiles
 // [tb, te).  Items item0 + i / nsplit, key range i % nsplit of nsplit equal
 // ranges.  PARTIAL = false: the whole key range, normalised bf16 output.
@@ -328,6 +278,10 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     attn_tile<QB, true>(((j - tb) & 1) ? lds1 : lds0, j, j == tb, S, n, hh, qf, o, negm, lsum);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) settle(o[qb][db]);
 
     // ---- epilogue: lane (n, hh), register r of dim block db holds dim
     // 32 db + 8 (r >> 2) + 4 hh + (r & 3) of query n.
@@ -399,37 +353,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     out[(bh * S + row) * 16 + seg] = pack8(acc);
 }
 
-// How one call is laid out over the GPU: `full` items run whole-key-range
-// workgroups in full rounds; the remaining `split` items (fewer than a round)
-// run nsplit key-range workgroups each, merged afterwards.  Depends only on the
-// shape, so the workspace size is known on the host.
-struct CorePlan {
-    int nqt, ntiles, items, full, split, nsplit;
-};
-
-static CorePlan core_plan(int BH, int S) {
-    CorePlan p;
-    p.ntiles = (int)num_kv_tiles(S);
-    p.nqt = (S + BM - 1) / BM;
-    p.items = BH * p.nqt;
-    const int rem = p.items % MI355X_CUS;
-    const int f = rem ? std::min(MI355X_CUS / rem, p.ntiles) : 1;
-    if (rem == 0 || f < 2) {
-        p.full = p.items;
-        p.split = 0;
-        p.nsplit = 1;
-    } else {
-        p.full = p.items - rem;
-        p.split = rem;
-        p.nsplit = f;
-    }
-    return p;
+hipError_t launch_merge(const float* part, void* out, int S, int nqt, int item0, int nsplit, int split_items,
+                        hipStream_t stream) {
+    attn_merge_kernel<<<split_items * (BM / 16), 256, 0, stream>>>(part, static_cast<uint4*>(out), S, nqt, item0,
+                                                                   nsplit);
+    return hipGetLastError();
 }
 
-size_t core_partial_bytes(int BH, int S) {
-    const CorePlan p = core_plan(BH, S);
-    return (size_t)p.split * p.nsplit * PART_FLOATS * sizeof(float);
-}
+size_t core_partial_bytes(int BH, int S) { return core_partial_bytes_for(core_plan(BH, S)); }
 
 hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
                             void* out, int BH, int S, float qmul, hipStream_t stream) {
@@ -447,8 +378,7 @@ hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_
         float* pt = static_cast<float*>(part);
         attn_core_kernel<true><<<p.split * p.nsplit, NW * 64, 0, stream>>>(
             qv, cv, sv, wsv, nullptr, pt, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
-        attn_merge_kernel<<<p.split * (BM / 16), 256, 0, stream>>>(pt, static_cast<uint4*>(out), S, p.nqt, p.full,
-                                                                  p.nsplit);
+        launch_merge(pt, out, S, p.nqt, p.full, p.nsplit, p.split, stream);
     }
     return hipGetLastError();
 }

@@ -1,0 +1,280 @@
+// attn_core_fp8.hip - joint self-attention with fp8 (OCP e4m3) Q/K/V and
+// per-tensor scales on gfx950's v_mfma_scale_f32_32x32x64_f8f6f4.
+//
+// The same computation as attn_core.hip (non-causal softmax(scale q' k'^T) v
+// over the whole joint sequence, RoPE on Q and K; xDiT paper abstract and the
+// AMD RDNA 4 xDiT blog's fp8 attention backend), on fp8 operands:
+//
+//   * K' was re-quantised after RoPE by prepare_kv_fp8 (step sk, in the
+//     workspace header); V keeps its codes (step v_scale).
+//   * Q prologue: dequantise (x q_scale), RoPE in fp32, multiply by
+//     scale*log2(e)*sk*2^-e and re-quantise, where 2^e is the power of two that
+//     keeps the largest possible code within 448.  The QK^T MFMA applies 2^e
+//     through its E8M0 B-operand scale, so its fp32 result is the base-2 score.
+//   * Weights p' = 2^(s - m + 4) = 16 p are rounded to e4m3 for the PV MFMA;
+//     m is the row max of the range's first tile and moves (with O and l
+//     rescaled) only when a lane's step weights sum past 16 * 24, which keeps
+//     every p' below 448.  l sums the fp32 p'; O = O_acc * v_scale / l.
+//
+// Work per workgroup, tile stream, split plan and merge are the bf16 kernel's
+// (attn_common.h).  Per 64-key tile a wave issues 4 QK^T and 4 PV MFMAs of
+// 32x32x64 (2 * 32 * 32 * 64 flop each).  Roofline: MFMA bound (fp8 peak).
+
+#include <hip/hip_runtime.h>
+
+#include "attn_common.h"
+#include "bf16_util.h"
+#include "fp8_util.h"
+#include "tile_layout.h"
+
+namespace dit {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float F8_SUM_LIMIT = 384.0f;  // 16 * 24: every p' of the step is then < 448
+constexpr int E8M0_ONE = 127;           // E8M0 scale code of 2^0
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c, int scale_b) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, E8M0_ONE, 0, scale_b);
+}
+
+__device__ __forceinline__ i32x8 lds_read32(const uint4* p) {
+    const uint4 lo = p[0], hi = p[1];
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// exp2 of a lane's 32 scores (two key blocks), packed to e4m3 in the PV B
+// operand order (byte j = key block j/16, register j%16); fp32 sum of p'.
+__device__ __forceinline__ void f8_weights(const f32x16 (&s)[2], i32x8& pf, float& sum) {
+    float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const f32x16& sc = s[w >> 2];
+        const int r = (w & 3) * 4;
+        const float a = __builtin_amdgcn_exp2f(sc[r]), b = __builtin_amdgcn_exp2f(sc[r + 1]);
+        const float c = __builtin_amdgcn_exp2f(sc[r + 2]), d = __builtin_amdgcn_exp2f(sc[r + 3]);
+        t0 += a + b;
+        t1 += c + d;
+        pf[w] = (int)f32x4_to_fp8(fminf(a, E4M3_MAX), fminf(b, E4M3_MAX), fminf(c, E4M3_MAX), fminf(d, E4M3_MAX));
+    }
+    sum = t0 + t1;
+}
+
+template <bool MASKED>
+__device__ __forceinline__ void f8_tile(const uint4* kt, int j, bool first, int S, int n, int hh, int qscale,
+                                        const i32x8 (&qf)[2], f32x16 (&o)[4], f32x16& negm, float& lsum) {
+    const uint4* vt = kt + F8_K_PART_CHUNKS;
+
+    // ---- S'^T = K' Q''^T * 2^e - m + 4: per key block kb, two 64-dim steps.
+    f32x16 s[2];
+    {
+        i32x8 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kb = i >> 1, kk = i & 1;
+            a[i] = lds_read32(kt + (kb * 32 + n) * F8_K_ROW_CHUNKS + kk * 4 + hh * 2);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kb = i >> 1, kk = i & 1;
+            s[kb] = mfma_f8(a[i], qf[kk], kk == 0 ? negm : s[kb], qscale);
+        }
+    }
+
+    if (MASKED) {
+        const int base = j * KV_TILE + 8 * hh;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (base + 32 * kb + 16 * (r >> 3) + (r & 7) >= S) s[kb][r] = -INFINITY;
+    }
+
+    i32x8 pf;
+    float tsum = 0.0f;
+    bool slow = first;
+    if (!slow) {
+        f8_weights(s, pf, tsum);
+        slow = __builtin_amdgcn_ballot_w64(!(tsum <= F8_SUM_LIMIT)) != 0;
+    }
+    if (slow) {
+        // Exact row max of this tile becomes the offset: p' <= 16 afterwards.
+        float mx = s[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        mx = swap_halves_max(mx);
+        const float shift = first ? mx - 4.0f : fmaxf(mx - 4.0f, 0.0f);
+        if (!first) {
+            const float alpha = __builtin_amdgcn_exp2f(-shift);
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        }
+        s[0] -= shift;
+        s[1] -= shift;
+        negm -= shift;
+        f8_weights(s, pf, tsum);
+    }
+    lsum += tsum;
+
+    // ---- O^T += V^T P'^T: four 32-dim blocks, 64 keys each.
+    {
+        i32x8 a[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) a[db] = lds_read32(vt + (db * 32 + n) * F8_V_ROW_CHUNKS + hh * 2);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] = mfma_f8(a[db], pf, o[db], E8M0_ONE);
+    }
+}
+
+template <bool PARTIAL>
+__global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
+    const uint4* __restrict__ q, float q_scale, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
+    const uint8_t* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ part, int S, int ntiles, int nqt,
+    int item0, int nsplit, float qmul, int has_rope) {
+    __shared__ uint4 lds0[F8_TILE_CHUNKS];
+    __shared__ uint4 lds1[F8_TILE_CHUNKS];
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int item = item0 + logical / nsplit;
+    const int f = logical - (logical / nsplit) * nsplit;
+    const int64_t bh = item / nqt;
+    const int qt = item - (int)bh * nqt;
+    const int tb = (int)((int64_t)f * ntiles / nsplit);
+    const int te = (int)((int64_t)(f + 1) * ntiles / nsplit);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 31;
+    const int hh = lane >> 5;
+
+    const float sk = reinterpret_cast<const float*>(ws)[0];
+    const float sv = reinterpret_cast<const float*>(ws)[1];
+    const uint4* src = reinterpret_cast<const uint4*>(ws + F8_HEADER_BYTES) + bh * (int64_t)ntiles * F8_TILE_CHUNKS;
+    copy_to_lds_async<NW, F8_TILE_CHUNKS>(src + (int64_t)tb * F8_TILE_CHUNKS, lds0, wave, lane);
+
+    // ---- Q prologue.  Largest |q'| is 448 q_scale (times sqrt(2) with RoPE);
+    // choose e so that it maps to at most 448 after the factor qmul * sk.
+    const float qbound = E4M3_MAX * q_scale * (has_rope ? 1.41421356237309515f : 1.0f) * qmul * sk;
+    const int e = qbound > 0.0f ? min(max((int)ceilf(log2f(qbound / E4M3_MAX)), -126), 126) : 0;
+    const float qfac = qmul * sk * ldexpf(1.0f, -e);
+    const int qscale = E8M0_ONE + e;
+    i32x8 qf[2];
+    {
+        const int row = qt * BM + wave * 32 + n;
+        const bool ok = row < S;
+        const uint4* qrow = q + (bh * S + row) * 8;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // dims 64 kk + 32 hh + 16 h .. +15: chunk c of the row
+                const int c = kk * 4 + hh * 2 + h;
+                uint4 w = make_uint4(0, 0, 0, 0);
+                if (ok) w = qrow[c];
+                float fv[16];
+                fp8x4_to_f32(w.x, fv);
+                fp8x4_to_f32(w.y, fv + 4);
+                fp8x4_to_f32(w.z, fv + 8);
+                fp8x4_to_f32(w.w, fv + 12);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    float t[8];
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) t[x] = fv[8 * g + x] * q_scale;
+                    if (has_rope && ok)
+                        rotate4(t, cos_t[(int64_t)row * 16 + 2 * c + g], sin_t[(int64_t)row * 16 + 2 * c + g]);
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) fv[8 * g + x] = clamp_e4m3(t[x] * qfac);
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    qf[kk][4 * h + x] = (int)f32x4_to_fp8(fv[4 * x], fv[4 * x + 1], fv[4 * x + 2], fv[4 * x + 3]);
+            }
+        }
+    }
+
+    f32x16 o[4], negm = f32x16{};
+    float lsum = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+
+    const int last = te - 1;
+    int j = tb;
+    for (; j + 2 <= last; j += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        copy_to_lds_async<NW, F8_TILE_CHUNKS>(src + (int64_t)(j + 1) * F8_TILE_CHUNKS, lds1, wave, lane);
+        f8_tile<false>(lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        copy_to_lds_async<NW, F8_TILE_CHUNKS>(src + (int64_t)(j + 2) * F8_TILE_CHUNKS, lds0, wave, lane);
+        f8_tile<false>(lds1, j + 1, false, S, n, hh, qscale, qf, o, negm, lsum);
+    }
+    if (j < last) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        copy_to_lds_async<NW, F8_TILE_CHUNKS>(src + (int64_t)(j + 1) * F8_TILE_CHUNKS, lds1, wave, lane);
+        f8_tile<false>(lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
+        ++j;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f8_tile<true>(((j - tb) & 1) ? lds1 : lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) settle(o[db]);
+
+    // ---- epilogue (as in the bf16 kernel), O scaled by the V step.
+    const float l = swap_halves_sum(lsum);
+    const int rloc = wave * 32 + n;
+    const int row = qt * BM + rloc;
+    if (PARTIAL) {
+        float* pw = part + (int64_t)logical * PART_FLOATS;
+        float4* prow = reinterpret_cast<float4*>(pw + (int64_t)rloc * HEAD_DIM);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                prow[db * 8 + g * 2 + hh] = make_float4(o[db][4 * g] * sv, o[db][4 * g + 1] * sv,
+                                                        o[db][4 * g + 2] * sv, o[db][4 * g + 3] * sv);
+        if (hh == 0) {
+            pw[BM * HEAD_DIM + rloc] = -negm[0];
+            pw[BM * HEAD_DIM + BM + rloc] = l;
+        }
+    } else if (row < S) {
+        const float inv = sv / l;
+        uint2* orow = out + (bh * S + row) * 32;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                orow[db * 8 + g * 2 + hh] = make_uint2(pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                                       pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+    }
+}
+
+size_t core_fp8_partial_bytes(int BH, int S) { return core_partial_bytes_for(core_plan(BH, S)); }
+
+hipError_t launch_attn_core_fp8(const void* q, float q_scale, const float* cos_t, const float* sin_t, const void* ws,
+                                void* part, void* out, int BH, int S, float qmul, hipStream_t stream) {
+    const CorePlan p = core_plan(BH, S);
+    const uint4* qv = static_cast<const uint4*>(q);
+    const uint8_t* wsv = static_cast<const uint8_t*>(ws);
+    const float4* cv = reinterpret_cast<const float4*>(cos_t);
+    const float4* sv = reinterpret_cast<const float4*>(sin_t);
+    const int rope = cos_t != nullptr;
+    if (p.full > 0)
+        attn_core_fp8_kernel<false><<<p.full, NW * 64, 0, stream>>>(qv, q_scale, cv, sv, wsv, static_cast<uint2*>(out),
+                                                                   nullptr, S, p.ntiles, p.nqt, 0, 1, qmul, rope);
+    if (p.split > 0) {
+        float* pt = static_cast<float*>(part);
+        attn_core_fp8_kernel<true><<<p.split * p.nsplit, NW * 64, 0, stream>>>(
+            qv, q_scale, cv, sv, wsv, nullptr, pt, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
+        launch_merge(pt, out, S, p.nqt, p.full, p.nsplit, p.split, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dit

@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include "bf16_util.h"
+#include "fp8_util.h"
 #include "tile_layout.h"
 
 namespace dit {
@@ -84,6 +85,110 @@ __global__ __launch_bounds__(256) void prepare_kv_kernel(
         vdst[v_chunk(d, c)] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     if (tid < HEAD_DIM) vdst[v_chunk(tid, 8)] = make_uint4(0, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// fp8 tiles (scaled-e4m3 path).  K codes are dequantised (x k_scale), rotated
+// in fp32 and re-quantised with step sk = k_scale * sqrt(2) when RoPE is on (a
+// rotation grows a component by at most sqrt(2) of the pair's largest, so the
+// codes stay within +-448), else copied.  V codes are only re-laid out (V^T,
+// keys in f8_vkey order).  Block (0, 0) stores {sk, v_scale} in the header.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prepare_kv_fp8_kernel(
+    const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
+    uint8_t* __restrict__ ws, int S, int ntiles, int has_rope, float k_scale, float v_scale) {
+    __shared__ uint4 vtile[KV_TILE * 8];  // 64 keys x 128 e4m3 codes, key-major
+
+    const int tile = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int key0 = tile * KV_TILE;
+    const float sk = has_rope ? k_scale * 1.41421356237309515f : k_scale;
+    if (tile == 0 && bh == 0 && tid == 0) {
+        reinterpret_cast<float*>(ws)[0] = sk;
+        reinterpret_cast<float*>(ws)[1] = v_scale;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(ws + F8_HEADER_BYTES) + (bh * ntiles + tile) * (int64_t)F8_TILE_CHUNKS;
+    const uint4* ksrc = k + bh * (int64_t)S * 8;
+    const uint4* vsrc = v + bh * (int64_t)S * 8;
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int x = tid + i * 256;
+        const int key = key0 + (x >> 3);
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (key < S) w = vsrc[(int64_t)key * 8 + (x & 7)];
+        vtile[x] = w;
+    }
+
+    // K part: chunk x = (row rho, chunk c) holds dims 16c..16c+15; c = 8 is padding.
+    const float inv_sk = 1.0f / sk;
+    for (int x = tid; x < F8_K_PART_CHUNKS; x += 256) {
+        const int rho = x / F8_K_ROW_CHUNKS;
+        const int c = x - rho * F8_K_ROW_CHUNKS;
+        const int key = key0 + kperm(rho);
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (c < 8 && key < S) {
+            w = ksrc[(int64_t)key * 8 + c];
+            if (has_rope) {
+                float f[16];
+                fp8x4_to_f32(w.x, f);
+                fp8x4_to_f32(w.y, f + 4);
+                fp8x4_to_f32(w.z, f + 8);
+                fp8x4_to_f32(w.w, f + 12);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float g[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) g[e] = f[8 * h + e] * k_scale;
+                    rotate4(g, cos_t[(int64_t)key * 16 + 2 * c + h], sin_t[(int64_t)key * 16 + 2 * c + h]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[8 * h + e] = clamp_e4m3(g[e] * inv_sk);
+                }
+                w = make_uint4(f32x4_to_fp8(f[0], f[1], f[2], f[3]), f32x4_to_fp8(f[4], f[5], f[6], f[7]),
+                               f32x4_to_fp8(f[8], f[9], f[10], f[11]), f32x4_to_fp8(f[12], f[13], f[14], f[15]));
+            }
+        }
+        dst[x] = w;
+    }
+
+    __syncthreads();
+
+    // V^T part: chunk (d, c) holds bytes 16c..16c+15 of row d, i.e. keys
+    // f8_vkey(hh, j) for byte 32 hh + j; c = 4 is padding.  Lanes run over d.
+    const uint8_t* vt8 = reinterpret_cast<const uint8_t*>(vtile);
+    uint4* vdst = dst + F8_K_PART_CHUNKS;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int y = tid + i * 256;
+        const int d = y & 127;
+        const int c = y >> 7;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int p = 16 * c + 4 * e + b;
+                acc |= (uint32_t)vt8[f8_vkey(p >> 5, p & 31) * 128 + d] << (8 * b);
+            }
+            w[e] = acc;
+        }
+        vdst[d * F8_V_ROW_CHUNKS + c] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    if (tid < HEAD_DIM) vdst[tid * F8_V_ROW_CHUNKS + 4] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_t, const float* sin_t, void* ws,
+                                 int BH, int S, float k_scale, float v_scale, hipStream_t stream) {
+    const int ntiles = (int)num_kv_tiles(S);
+    dim3 grid(ntiles, BH);
+    prepare_kv_fp8_kernel<<<grid, 256, 0, stream>>>(
+        static_cast<const uint4*>(k), static_cast<const uint4*>(v), reinterpret_cast<const float4*>(cos_t),
+        reinterpret_cast<const float4*>(sin_t), static_cast<uint8_t*>(ws), S, ntiles, cos_t != nullptr, k_scale,
+        v_scale);
+    return hipGetLastError();
 }
 
 hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, const float* sin_t,

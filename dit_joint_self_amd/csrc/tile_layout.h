@@ -55,4 +55,30 @@ __host__ __device__ constexpr inline int64_t num_kv_tiles(int S) {
     return (S + KV_TILE - 1) / KV_TILE;
 }
 
+// ---------------------------------------------------------------------------
+// fp8 (OCP e4m3) tiles, one byte per element, for the scaled-fp8 path.
+//
+//   K' part (F8_K_PART_BYTES = 9216): 64 rows of 144 bytes.  Row rho holds key
+//        kperm(rho): bytes 0..127 are dims 0..127 (re-quantized after RoPE),
+//        bytes 128..143 zero padding.
+//   V^T part (F8_V_PART_BYTES = 10240): 128 rows of 80 bytes, one per head dim
+//        d.  Byte 32*hh + j (hh in {0,1}, j < 32) holds key f8_vkey(hh, j) of
+//        the tile; bytes 64..79 zero padding.  f8_vkey lists, for lane half hh,
+//        the keys its 32x32 score accumulator holds in register order, so the
+//        bytes of P and of V^T pair up key by key in the PV product.
+//   Bytes [0, 16) of the workspace hold two fp32 scales written by the
+//   preparation kernel: the K' quantization step and the V step.
+// ---------------------------------------------------------------------------
+constexpr int F8_K_ROW_CHUNKS = 9;                             // 8 data chunks + 1 pad
+constexpr int F8_V_ROW_CHUNKS = 5;                             // 4 data chunks + 1 pad
+constexpr int F8_K_PART_CHUNKS = KV_TILE * F8_K_ROW_CHUNKS;    // 576
+constexpr int F8_V_PART_CHUNKS = HEAD_DIM * F8_V_ROW_CHUNKS;   // 640
+constexpr int F8_TILE_CHUNKS = F8_K_PART_CHUNKS + F8_V_PART_CHUNKS;  // 1216 = 19 x 64
+constexpr int F8_TILE_BYTES = F8_TILE_CHUNKS * 16;             // 19456
+constexpr int F8_HEADER_BYTES = 256;                           // scales, then the tiles
+
+static_assert(F8_K_PART_CHUNKS % 64 == 0 && F8_V_PART_CHUNKS % 64 == 0, "parts are whole wave copies");
+
+__host__ __device__ constexpr inline int f8_vkey(int hh, int j) { return 16 * (j >> 3) + 8 * hh + (j & 7); }
+
 }  // namespace dit

@@ -94,7 +94,8 @@ dit_status_t dit_rope_tables(const int32_t* pos, int S, int n_axes, const int32_
  *              means no RoPE; exactly one NULL is DIT_ERR_INVALID_ARG.
  *   out        device bf16 [B, H, S, D], written in full.
  *   scale      softmax scale (normally 1/sqrt(D)); finite.
- *   dtype      must be DIT_DTYPE_BF16 (fp8 has its own entry point).
+ *   dtype      must be DIT_DTYPE_BF16; DIT_DTYPE_FP8_E4M3 returns DIT_ERR_UNSUPPORTED
+ *              (fp8 inputs need their scales: dit_attn_forward_fp8).
  *
  * Rounding: rotated K is rounded to bf16 (RNE); rotated Q is multiplied by
  * scale*log2(e) in fp32 and rounded to bf16; QK^T and PV accumulate in fp32
@@ -135,6 +136,38 @@ dit_status_t dit_attn_prepare_kv(const void* k, const void* v,
 dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin,
                            const void* workspace, size_t workspace_bytes, void* out,
                            int B, int H, int S, int D, float scale, void* stream);
+
+/*
+ * fp8 path: Q, K, V as OCP e4m3 codes with one fp32 scale per tensor (the AMD
+ * RDNA 4 xDiT blog's fp8 attention backend; the pages give no format, the
+ * reading is OCP e4m3, max 448).  Real values are code * scale.
+ *
+ *   q8, k8, v8  device e4m3 [B, H, S, D] (one byte per element), 16-byte aligned.
+ *   q_scale, k_scale, v_scale  finite, > 0.
+ *   rope_cos, rope_sin, scale, out (bf16), S_txt, S_img, D, stream: as in
+ *               dit_attn_forward.
+ *
+ * RoPE is applied to the dequantised values in fp32; rotated K is re-quantised
+ * with step k_scale*sqrt(2) and rotated, scaled Q with a power-of-two-adjusted
+ * step (applied back through the MFMA's E8M0 scale); QK^T and PV run on
+ * v_mfma_scale_f32_32x32x64_f8f6f4 with fp32 accumulation; softmax state is
+ * fp32; the weights are rounded to e4m3 for PV; the output is bf16.
+ */
+size_t dit_attn_workspace_bytes_fp8(int B, int H, int S, int D);
+
+dit_status_t dit_attn_prepare_kv_fp8(const void* k8, const void* v8, float k_scale, float v_scale,
+                                     const float* rope_cos, const float* rope_sin,
+                                     void* workspace, size_t workspace_bytes,
+                                     int B, int H, int S, int D, void* stream);
+
+dit_status_t dit_attn_core_fp8(const void* q8, float q_scale, const float* rope_cos, const float* rope_sin,
+                               const void* workspace, size_t workspace_bytes, void* out,
+                               int B, int H, int S, int D, float scale, void* stream);
+
+dit_status_t dit_attn_forward_fp8(const void* q8, const void* k8, const void* v8,
+                                  float q_scale, float k_scale, float v_scale,
+                                  const float* rope_cos, const float* rope_sin, void* out,
+                                  int B, int H, int S_txt, int S_img, int D, float scale, void* stream);
 
 #ifdef __cplusplus
 }

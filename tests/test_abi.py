@@ -145,3 +145,29 @@ def test_binding_raises_on_error_status():
     with pytest.raises(dj.DitAttnError) as ei:
         dj._check(dj.DIT_ERR_UNSUPPORTED)
     assert "DIT_ERR_UNSUPPORTED" in str(ei.value)
+
+
+def test_fp8_entry_points_reject_bad_arguments():
+    L = dj.lib()
+    # fp8 workspace: 256-byte header + 19 KiB tiles, plus the same split partials as bf16.
+    assert dj.dit_attn_workspace_bytes_fp8(1, 1, 1, 128) == 256 + 19456
+    assert dj.dit_attn_workspace_bytes_fp8(1, 1, 64, 64) == 0
+    F = L.dit_attn_forward_fp8
+    ok = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, sq=0.1, sk=0.1, sv=0.1, out=FAKE * 4)
+    def call(**kw):
+        a = dict(ok); a.update(kw)
+        return F(a["q"], a["k"], a["v"], a["sq"], a["sk"], a["sv"], None, None, a["out"], 1, 2, 3, 5, 128, 0.1, None)
+    assert call(q=None) == dj.DIT_ERR_INVALID_ARG
+    assert call(sq=0.0) == dj.DIT_ERR_INVALID_ARG
+    assert call(sk=float("nan")) == dj.DIT_ERR_INVALID_ARG
+    assert call(sv=-1.0) == dj.DIT_ERR_INVALID_ARG
+    assert call(q=FAKE + 8) == dj.DIT_ERR_INVALID_ARG
+    assert call(out=FAKE * 3) == dj.DIT_ERR_INVALID_ARG
+    need = dj.dit_attn_workspace_bytes_fp8(1, 2, 8, 128)
+    ws = 0x10000000
+    assert L.dit_attn_prepare_kv_fp8(FAKE, FAKE * 2, 0.1, 0.1, None, None, ws, need - 1, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_kv_fp8(FAKE, FAKE * 2, 0.0, 0.1, None, None, ws, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core_fp8(FAKE, 0.1, None, None, ws, need, FAKE * 3, 1, 2, 8, 96, 0.1, None) == dj.DIT_ERR_UNSUPPORTED
+    assert L.dit_attn_core_fp8(FAKE, float("inf"), None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    if _no_device():
+        assert call() == dj.DIT_ERR_NO_DEVICE

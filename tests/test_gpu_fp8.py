@@ -1,0 +1,125 @@
+"""Parity of the fp8 (OCP e4m3, per-tensor scales) path with the float64 oracle
+on the dequantised inputs.
+
+Gates for unit-variance data quantised per tensor: max |gpu - oracle| <= 5e-2,
+mean <= 5e-3, and mean|diff| / mean|oracle| <= 8%.  The relative gate comes
+from the arithmetic: besides the inputs, the path rounds three things to e4m3
+(3 mantissa bits, RMS relative error 2^-4 / sqrt(3) ~ 3.6%): the rotated K', the
+rotated and scaled Q'' and the weights P.  The first two move each base-2
+logit by ~ sqrt(2) * 3.6% of its size (|s| ~ 1.5 here), i.e. a weight by
+~ ln2 * 0.076 ~ 5%; with P's own 3.6% the weights move by ~ 6% RMS, which
+averages down in O but not below a few percent of |O|.  Short sequences (S <= 256)
+average few V rows, so |O| is O(1): there e4m3's 2^-4 relative rounding of the
+re-quantised Q'', K' and of P dominates and the gates are max(5e-2, 2^-2 max|O|)
+and max(5e-3, 2^-4 mean|O|).  The same holds for sharpened logits (Q x 3): the
+softmax then puts its mass on a few keys, so O is again a short average of V
+rows, and the logit error (proportional to |s|) grows threefold; those cases
+take the |O|-relative gates too, with the same 8% relative-mean gate.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import dit_workloads as W
+from oracle import joint_attention, rope_angles
+from oracle.fp8 import dequantize
+from tests.gpu_inputs import err_stats, from_device_bf16, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, REL_MEAN = 5e-2, 5e-3, 8e-2
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _quantized(w, qmul=1.0):
+    q, k, v = W.draw_qkv_f32(w)
+    return [W.fp8_e4m3_quantize(x) for x in (q * qmul, k, v)]
+
+
+def _run(w, qkv8, rope=True, split=False, scale=None):
+    torch = _torch()
+    import dit_joint_self_amd as dj
+    (q8, sq), (k8, sk), (v8, sv) = qkv8
+    dev = lambda c: torch.from_numpy(np.ascontiguousarray(c)).to("cuda")
+    q, k, v = dev(q8), dev(k8), dev(v8)
+    cos = sin = None
+    if rope:
+        cos, sin = dj.dit_rope_tables(torch.from_numpy(W.positions(w)).to("cuda"), w.axes_dim, w.theta)
+    if split:
+        nb = dj.dit_attn_workspace_bytes_fp8(w.B, w.H, w.S, w.D)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+        dj.dit_attn_prepare_kv_fp8(k, v, sk, sv, cos, sin, ws)
+        dj.dit_attn_core_fp8(q, sq, cos, sin, ws, out, scale=scale)
+    else:
+        out = dj.dit_attn_forward_fp8(q, k, v, sq, sk, sv, cos, sin, S_txt=w.S_txt, scale=scale)
+    torch.cuda.synchronize()
+    return from_device_bf16(out)
+
+
+def _oracle(w, qkv8, rope=True, rows=None, scale=None):
+    (q8, sq), (k8, sk), (v8, sv) = qkv8
+    ang = rope_angles(W.positions(w), w.axes_dim, w.theta) if rope else None
+    return joint_attention(dequantize(q8, sq), dequantize(k8, sk), dequantize(v8, sv), ang, scale=scale, rows=rows)
+
+
+def _assert_close(got, want, tag, few_rows=False):
+    e = err_stats(got, want)
+    print(f"[fp8 parity] {tag}: {e}", flush=True)
+    assert np.all(np.isfinite(got)), tag
+    mg, ng = MAX_ABS, MEAN_ABS
+    if few_rows:
+        mg = max(MAX_ABS, 0.25 * float(np.abs(want).max()))
+        ng = max(MEAN_ABS, 2.0 ** -4 * float(np.abs(want).mean()))
+    assert e["max_abs"] <= mg and e["mean_abs"] <= ng and e["rel_mean"] <= REL_MEAN, (tag, e)
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux1024x768"])
+def test_fp8_full_parity(name):
+    w = W.get(name)
+    qkv8 = _quantized(w)
+    _assert_close(_run(w, qkv8), _oracle(w, qkv8), name)
+
+
+@pytest.mark.parametrize("name,n_random", [("flux2048_fp8", 96), ("video_ulysses4", 32)])
+def test_fp8_sampled_parity_full_size(name, n_random):
+    w = W.get(name)
+    qkv8 = _quantized(w)
+    got = _run(w, qkv8)
+    assert np.all(np.isfinite(got))
+    rows = sample_rows(w.S, w.S_txt, n_random, seed=w.seed)
+    _assert_close(got[:, :, rows], _oracle(w, qkv8, rows=rows), f"{name} ({len(rows)} rows)")
+
+
+@pytest.mark.parametrize("S_txt,grid,B,H", [(1, (0, 0), 1, 1), (0, (1, 31), 1, 1), (2, (1, 31), 1, 1),
+                                            (0, (7, 9), 1, 2), (1, (8, 8), 1, 3), (13, (12, 20), 1, 2),
+                                            (64, (16, 16), 2, 2)])
+def test_fp8_ragged_and_small(S_txt, grid, B, H):
+    """Includes single-tile sequences shorter than the 32-query MFMA block
+    (S = 1, 31, 33): the query lanes past S must still feed every MFMA."""
+    w = W.Workload("edge8", B=B, H=H, D=128, S_txt=S_txt, grid=grid, axes_dim=(64, 64), theta=10000.0,
+                   seed=77 + S_txt)
+    qkv8 = _quantized(w)
+    want = _oracle(w, qkv8)
+    for split in (False, True):
+        _assert_close(_run(w, qkv8, split=split), want, f"S={w.S} split={split}", few_rows=w.S <= 256)
+
+
+def test_fp8_no_rope_and_sharper_logits():
+    w = W.get("tiny").with_(H=2)
+    qkv8 = _quantized(w, qmul=3.0)
+    _assert_close(_run(w, qkv8, rope=False), _oracle(w, qkv8, rope=False), "no-rope q*3", few_rows=True)
+
+
+def test_fp8_deterministic_and_forward_equals_split():
+    w = W.get("tiny")
+    qkv8 = _quantized(w)
+    a, b, c = _run(w, qkv8), _run(w, qkv8), _run(w, qkv8, split=True)
+    assert np.array_equal(a, b) and np.array_equal(a, c)

@@ -262,3 +262,25 @@ def test_oracle_catches_planted_sign_error():
     z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * ang)
     assert np.max(np.abs(bad[..., 0::2] - z.real)) > 1e-3
     assert np.max(np.abs(rope_apply(x, ang)[..., 0::2] - z.real)) <= 1e-12
+
+
+# ---------------------------------------------------------------- fp8 decoding
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    from oracle.fp8 import e4m3_decode
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def test_e4m3_decode_closed_forms():
+    from oracle.fp8 import dequantize, e4m3_decode
+    # 0x38 = 0 0111 000 -> 2^0; 0x7e = 0 1111 110 -> 1.75 * 2^8; 0x08 -> 2^-6 (smallest normal);
+    # 0x01 -> 1/8 * 2^-6 (smallest subnormal); 0xc4 = 1 1000 100 -> -1.5 * 2
+    got = e4m3_decode(np.array([0x38, 0x7e, 0x08, 0x01, 0xc4, 0x00, 0x80], np.uint8))
+    assert got.tolist() == [1.0, 448.0, 2.0 ** -6, 2.0 ** -9, -3.0, 0.0, -0.0]
+    assert np.isnan(e4m3_decode(np.array([0x7f, 0xff], np.uint8))).all()
+    assert dequantize(np.array([0x40], np.uint8), 0.25).tolist() == [0.5]
