@@ -33,8 +33,10 @@ KERNEL_SOURCES = ["dit_joint_self_amd/csrc/attn_core.hip", "dit_joint_self_amd/c
                   "dit_joint_self_amd/csrc/attn_common.h", "dit_joint_self_amd/csrc/tile_layout.h",
                   "dit_joint_self_amd/csrc/bf16_util.h", "dit_joint_self_amd/csrc/fp8_util.h"]
 MEASURED_TRAFFIC = {
-    ("4570db5b9355adc5", "flux2048"): {"read_bytes": 995.0e6, "write_bytes": 103.8e6,
+    ("5b4cb76355ac9b4e", "flux2048"): {"read_bytes": 1083.7e6, "write_bytes": 135.8e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
+    ("5b4cb76355ac9b4e", "flux2048_fp8"): {"read_bytes": 694.4e6, "write_bytes": 136.1e6,
+                                           "profile": "profiles/attn_core_fp8_flux2048.md"},
 }
 
 
@@ -82,6 +84,13 @@ def copy_calibration(args, torch):
     ms = e0.elapsed_time(e1) / args.steps
     print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n, "ms": ms,
                       "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
+def ws_bytes_tiles(w, fp8):
+    """Bytes of prepared K'/V^T tiles the attention kernel streams: 64-key tiles of
+    35840 B (bf16) or 19456 B (fp8, plus its 256 B scale header) per (b, h)."""
+    tiles = w.B * w.H * ((w.S + 63) // 64)
+    return tiles * 19456 + 256 if fp8 else tiles * 35840
 
 
 def bf16_dev(bits, torch):
@@ -187,6 +196,7 @@ def main():
     prep_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
     core_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
     step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
+    steps_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
 
     # The allocating entry point itself (workspace from the stream pool), for reference.
     for _ in range(2):
@@ -215,6 +225,8 @@ def main():
     prep_avg = float(np.mean(prep_ms))
     achieved = flops / (core_avg * 1e-3) / 1e12
     tensor_bytes = w.B * w.H * w.S * w.D * (1 if fp8 else 2)
+    # read Q, the prepared tiles and the two tables; write the bf16 output
+    core_bytes = tensor_bytes + ws_bytes_tiles(w, fp8) + 2 * w.S * (w.D // 2) * 4 + w.B * w.H * w.S * w.D * 2
     prep_bytes = 4 * tensor_bytes + 2 * w.S * (w.D // 2) * 4  # read K, V, cos, sin; write 2 tensors of tiles
     rec = {
         "metric": METRIC,
@@ -224,6 +236,8 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": step_ms,
+        "ms_per_step_median": float(np.median(steps_ms)),
+        "ms_per_step_min": float(np.min(steps_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -232,10 +246,12 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S_txt": w.S_txt, "S_img": w.S_img, "S": w.S,
                    "D": w.D, "rope_axes": list(w.axes_dim), "non_causal": True},
         "pct_of_peak": 100.0 * flops / (step_ms * 1e-3) / 1e12 / peak,
-        "roofline": {"bound": "mfma", "kernel": "attn_core_fp8_kernel" if fp8 else "attn_core_kernel",
+        "roofline": {"bound": "mfma",
+                     "kernel": ("dit_attn_core_fp8: attn_core_fp8_kernel" if fp8 else "dit_attn_core: attn_core_kernel")
+                               + " (whole-range and key-range launches) + attn_merge_kernel",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic, "traffic_unit": "HBM bytes per launch (read + write)",
-                     "avg_ms": core_avg, "kernel_sources": src_hash},
+                     "traffic": traffic, "traffic_unit": "HBM bytes per dit_attn_core call (read + write)",
+                     "algorithmic_bytes": core_bytes, "avg_ms": core_avg, "kernel_sources": src_hash},
         "stages_ms": {"prepare_kv": prep_avg, "attn_core": core_avg,
                       "prepare_kv_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9},
         "forward_ms": fwd_ms,
