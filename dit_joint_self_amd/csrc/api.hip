@@ -16,6 +16,7 @@
 #include <mutex>
 
 #include "dit_attn.h"
+#include "attn_common.h"
 #include "tile_layout.h"
 
 namespace dit {
@@ -68,6 +69,8 @@ dit_status_t check_shape(int B, int H, int S, int D) {
     if (S < 1) return fail(DIT_ERR_INVALID_ARG, "S must be >= 1 (got %d)", S);
     if (D < 1) return fail(DIT_ERR_INVALID_ARG, "D must be >= 1 (got %d)", D);
     if (D != dit::HEAD_DIM) return fail(DIT_ERR_UNSUPPORTED, "only D = 128 is implemented (got %d)", D);
+    if (S > dit::MAX_SEQ)
+        return fail(DIT_ERR_UNSUPPORTED, "S = %d exceeds the longest supported sequence (%d)", S, dit::MAX_SEQ);
     const int64_t wgs = (int64_t)B * H * ((S + kMinBlockM - 1) / kMinBlockM);
     const int64_t tiles = (int64_t)B * H * dit::num_kv_tiles(S);
     if (wgs > INT_MAX || tiles > INT_MAX || (int64_t)B * H > 65535)

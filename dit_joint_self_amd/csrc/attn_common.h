@@ -25,6 +25,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));   // one 32x32 MFMA a
 // reads and writes the value, so every product feeding it stays before it.
 __device__ __forceinline__ void settle(f32x16& x) { asm volatile("" : "+v"(x)); }
 
+// Longest sequence the kernels accept: keeps every byte offset inside one
+// (batch, head) slice of prepared tiles below 2^31.
+constexpr int MAX_SEQ = 1 << 21;
+static_assert((int64_t)((MAX_SEQ + KV_TILE - 1) / KV_TILE) * TILE_BYTES < (int64_t)1 << 31, "slice offsets fit");
+
 // Partial results of one key-range workgroup: O (unnormalised, fp32, row-major
 // [BM][128]), then the offset m (base 2) and the weight sum l of each row.
 constexpr int PART_FLOATS = BM * HEAD_DIM + 2 * BM;
@@ -51,20 +56,33 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Copy `chunks` 16-byte chunks (a multiple of 64) HBM -> LDS: wave w copies
-// the 1 KiB pieces w, w + NW, ...; each lane moves 16 bytes per piece.
+// Buffer resource over `bytes` bytes from `base`, raw addressing (word 3 is the
+// gfx9 raw-buffer format).  Accesses at or past `bytes` read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One 1 KiB piece HBM -> LDS by the buffer form of the LDS DMA
+// (buffer_load_dwordx4 ... lds): lane l moves bytes [soff + 16 l, soff + 16 l + 16)
+// of the resource to lds_dst + 16 l.  The buffer form is counted on VM_CNT
+// only; with the global form in flight the compiler can only wait for all
+// outstanding LDS reads at once, which exposes the full LDS latency each time
+// an MFMA operand is needed.
+__device__ __forceinline__ void lds_piece(__amdgpu_buffer_rsrc_t rsrc, int soff, uint4* lds_dst, int lane) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, lane * 16,
+                                             soff, 0, 0);
+}
+
+// Copy CHUNKS 16-byte chunks (whole 1 KiB pieces) starting at byte soff of the
+// resource to lds_dst: wave w moves pieces w, w + NW, ...
 template <int NW, int CHUNKS>
-__device__ __forceinline__ void copy_to_lds_async(const uint4* __restrict__ src, uint4* lds_dst, int wave,
-                                                  int lane) {
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, int soff, uint4* lds_dst, int wave,
+                                            int lane) {
     static_assert(CHUNKS % 64 == 0, "whole 1 KiB pieces");
 #pragma unroll
     for (int i = 0; i < (CHUNKS / 64 + NW - 1) / NW; ++i) {
         const int piece = i * NW + wave;
-        if (piece < CHUNKS / 64) {
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(src + piece * 64 + lane),
-                (__attribute__((address_space(3))) void*)(lds_dst + piece * 64), 16, 0, 0);
-        }
+        if (piece < CHUNKS / 64) lds_piece(rsrc, soff + piece * 1024, lds_dst + piece * 64, lane);
     }
 }
 

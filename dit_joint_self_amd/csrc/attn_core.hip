@@ -14,8 +14,11 @@
 //     and the factor scale*log2(e) in fp32 and keeps them as bf16 MFMA
 //     B operands for the whole kernel (Q-tile resident in VGPRs).
 //   * K/V stream: 64-key tiles already rotated and laid out by
-//     prepare_kv.hip, copied HBM -> LDS with global_load_lds_dwordx4 into a
-//     double buffer (tile j+1 lands while tile j is consumed).
+//     prepare_kv.hip, copied HBM -> LDS by buffer_load_dwordx4 ... lds into
+//     two K' and two V^T buffers; K' runs one tile ahead of V^T, and the
+//     copies of a step are issued one at a time between its MFMAs.
+//   * Software pipeline per wave: the QK^T MFMAs of tile j+1 run beside the
+//     exp2 / bf16 / row-sum work of tile j, then O += P V for tile j.
 //   * S^T = K' Q'^T on v_mfma_f32_32x32x16_bf16: lane (n, hh) of the
 //     accumulator owns query n and 16 keys, so a row max is in-lane max ops
 //     plus one v_permlane32_swap, and the row sum stays per lane until the
@@ -46,149 +49,192 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-template <int NW>
-__device__ __forceinline__ void load_tile_async(const uint4* __restrict__ src, uint4* lds_dst,
-                                                int wave, int lane) {
-    copy_to_lds_async<NW, TILE_CHUNKS>(src, lds_dst, wave, lane);
-}
-
-// exp2 of one accumulator's 16 scores, rounded to bf16 as two PV B operands;
-// the rounded values are also summed (v_dot2c_f32_bf16 against (1, 1)), so
-// the row sum is the sum of exactly the weights the PV product uses.
-__device__ __forceinline__ void exp_pack16(const f32x16& sc, bf16x8 (&pf)[2], float& sum) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            w[i] = pack_bf16x2(__builtin_amdgcn_exp2f(sc[8 * t2 + 2 * i]),
-                               __builtin_amdgcn_exp2f(sc[8 * t2 + 2 * i + 1]));
-            sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]), ones, sum, false);
-        }
-        pf[t2] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-    }
-}
-
-// One 64-key tile: S^T = K' Q'^T, online softmax, O^T += V^T P^T.  `kt` is the
-// tile's LDS image (K part then V^T part), `j` its index.
+// One 64-key tile step of the software-pipelined loop.
 //
 // Softmax bookkeeping (base 2, per query): m is the offset subtracted before
 // exp2 and l the running sum of the bf16 weights.  negm holds -m in all 16
 // registers of the lane's accumulator shape and enters as the C operand of the
 // first QK^T MFMA, so the scores arrive already offset.  m is exact (the row
-// max) after tile 0; afterwards it is only raised when a tile's weights sum past
-// SUM_LIMIT in some lane (so no weight exceeds 2^20): then the tile's row max is
-// taken, O and l are scaled by 2^(m_old - m_new) and the tile is redone.  The
-// final O / l does not depend on when m moves.
+// max) after the first tile; afterwards it is only raised when a tile's
+// weights sum past SUM_LIMIT in some lane (so no weight exceeds 2^20): then
+// the tile's row max is taken, O and l are scaled by 2^(m_old - m_new) and the
+// tile's weights are redone.  The final O / l does not depend on when m moves.
+//
+// Pipelining: while the matrix cores compute the NEXT tile's scores, the VALU
+// turns the CURRENT tile's scores into weights (stage A, 16 fenced steps of
+// one MFMA + one score pair each); then O^T += V^T P^T for the current tile
+// (stage B).  The next tile's scores were offset with the m in force before
+// stage A, so a move of m in between is applied to them too.
 constexpr float SUM_LIMIT = 1048576.0f;  // 2^20
 
 // MFMA operand ring: LDS reads run RING - 1 MFMA steps ahead of their use.
 constexpr int RING = 4;
 
-template <int QB, bool MASKED>
-__device__ __forceinline__ void attn_tile(const uint4* kt, int j, bool first, int S, int n, int hh,
-                                          const bf16x8 (&qf)[QB][8], f32x16 (&o)[QB][4],
-                                          f32x16 (&negm)[QB], float (&lsum)[QB]) {
-    const uint4* vt = kt + K_PART_CHUNKS;
+// K' operand of QK^T step i (dim step i >> 1, key block i & 1) and V^T operand
+// of PV step i (16-key step i >> 2, dim block i & 3), for lane (n, hh).
+__device__ __forceinline__ bf16x8 k_operand(const uint4* kt, int i, int n, int hh) {
+    return as_bf16x8(kt[k_chunk((i & 1) * 32 + n, 2 * (i >> 1) + hh)]);
+}
+__device__ __forceinline__ bf16x8 v_operand(const uint4* vt, int i, int n, int hh) {
+    return as_bf16x8(vt[v_chunk((i & 3) * 32 + n, 2 * (i >> 2) + hh)]);
+}
 
-    // ---- S'^T = K' Q'^T - m for 64 keys x (32 * QB) queries: 16 MFMA steps
-    // i = (dim step t = i / 2, key block kb = i % 2).  K operands rotate
-    // through a ring read RING - 1 steps ahead; the scheduling fences keep the
-    // compiler from sinking the reads back to their use.
-    f32x16 s[QB][2];
-    {
-        bf16x8 ring[RING];
-#pragma unroll
-        for (int i0 = 0; i0 < RING - 1; ++i0)
-            ring[i0] = as_bf16x8(kt[k_chunk((i0 & 1) * 32 + n, 2 * (i0 >> 1) + hh)]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i + RING - 1 < 16) {
-                const int t2 = (i + RING - 1) >> 1, kb2 = (i + RING - 1) & 1;
-                ring[(i + RING - 1) % RING] = as_bf16x8(kt[k_chunk(kb2 * 32 + n, 2 * t2 + hh)]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            const int t = i >> 1, kb = i & 1;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % RING], qf[qb][t],
-                                                                    t == 0 ? negm[qb] : s[qb][kb], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+// Two weights of score pair p (0..15) of the current tile: pair p of key
+// block p >> 3 holds registers 2 (p & 7) and 2 (p & 7) + 1.  w[p] is the bf16
+// pair; its sum (v_dot2c against (1, 1)) is added to `sum`, so l sums exactly
+// the weights the PV product uses.
+__device__ __forceinline__ void weight_pair(const f32x16 (&sc)[2], int p, uint32_t (&w)[16], float& sum) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const f32x16& a = sc[p >> 3];
+    const int r = 2 * (p & 7);
+    w[p] = pack_bf16x2(__builtin_amdgcn_exp2f(a[r]), __builtin_amdgcn_exp2f(a[r + 1]));
+    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[p]), ones, sum, false);
+}
+
+// The tile copies one pipelined step issues, spread over stage A: piece j of
+// the K' part two tiles ahead at step 2j + 1, piece j of the V^T part one tile
+// ahead at step 2 (KJ + j) + 1.  Issued one at a time between MFMAs instead of
+// in a burst after the barrier, the copies do not hold up the wave's first
+// MFMAs.
+struct TileCopies {
+    static constexpr int KJ = (K_PART_CHUNKS / 64 + NW - 1) / NW;  // K' pieces per wave (at most)
+    static constexpr int VJ = (V_PART_CHUNKS / 64 + NW - 1) / NW;  // V^T pieces per wave (at most)
+    __amdgpu_buffer_rsrc_t rsrc;
+    int ksoff, vsoff;  // byte offsets of the two parts in the slice
+    uint4* kdst;
+    uint4* vdst;
+    bool kon;          // the K' part exists (wave-uniform)
+    int wave, lane;
+    __device__ __forceinline__ void at_step(int i) const {
+        if ((i & 1) == 0) return;
+        const int j = i >> 1;
+        if (j < KJ) {
+            const int p = j * NW + wave;
+            if (kon && p < K_PART_CHUNKS / 64) lds_piece(rsrc, ksoff + p * 1024, kdst + p * 64, lane);
+        } else if (j < KJ + VJ) {
+            const int p = (j - KJ) * NW + wave;
+            if (p < V_PART_CHUNKS / 64) lds_piece(rsrc, vsoff + p * 1024, vdst + p * 64, lane);
         }
     }
+};
+static_assert(2 * (TileCopies::KJ + TileCopies::VJ) <= 16, "the copies fit in the 16 steps of stage A");
 
-    // ---- keys past S (last tile only): lane half hh, register r of key
-    // block kb holds key 32 kb + 16 (r >> 3) + 8 hh + (r & 7).
-    if (MASKED) {
-        const int base = j * KV_TILE + 8 * hh;
+// Stage A: QK MFMA step i of the next tile (K' part kn) with weight pair i of
+// the current tile, and the step's share of the tile copies (cp may be null).
+// QK = false: weights only (the range's last tile); EXP = false: scores only
+// (the range's first tile, before the loop).
+template <bool QK, bool EXP>
+__device__ __forceinline__ void stage_a(const uint4* kn, const bf16x8 (&qf)[8], const f32x16& negm,
+                                        f32x16 (&sn)[2], const f32x16 (&sc)[2], uint32_t (&w)[16], float& sum,
+                                        int n, int hh, const TileCopies* cp = nullptr) {
+    bf16x8 ring[RING];
+    if (QK) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (base + 32 * kb + 16 * (r >> 3) + (r & 7) >= S) s[qb][kb][r] = -INFINITY;
+        for (int i0 = 0; i0 < RING - 1; ++i0) ring[i0] = k_operand(kn, i0, n, hh);
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (QK && i + RING - 1 < 16) ring[(i + RING - 1) % RING] = k_operand(kn, i + RING - 1, n, hh);
+        __builtin_amdgcn_sched_barrier(0);
+        if (QK)
+            sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % RING], qf[i >> 1],
+                                                                (i >> 1) == 0 ? negm : sn[i & 1], 0, 0, 0);
+        if (EXP) weight_pair(sc, i, w, sum);
+        if (cp) cp->at_step(i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
 
-    // ---- weights P = 2^(S'), bf16 B operands, row sums.
-    bf16x8 pf[QB][2][2];
+// Row max of a tile's offset scores (all 64 keys: both lane halves).
+__device__ __forceinline__ float tile_max(const f32x16 (&sc)[2]) {
+    float mx = sc[0][0];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        float t0 = 0.0f, t1 = 0.0f;
-        bool slow = first;
-        if (!slow) {
-            exp_pack16(s[qb][0], pf[qb][0], t0);
-            exp_pack16(s[qb][1], pf[qb][1], t1);
-            slow = __builtin_amdgcn_ballot_w64(!(t0 + t1 <= SUM_LIMIT)) != 0;
-        }
-        if (slow) {
-            float mx = s[qb][0][0];
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][1][r]);
-            mx = swap_halves_max(mx);
-            const float shift = first ? mx : fmaxf(mx, 0.0f);
-            if (!first) {
-                const float alpha = __builtin_amdgcn_exp2f(-shift);
-                lsum[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
-            }
-            s[qb][0] -= shift;
-            s[qb][1] -= shift;
-            negm[qb] -= shift;
-            t0 = t1 = 0.0f;
-            exp_pack16(s[qb][0], pf[qb][0], t0);
-            exp_pack16(s[qb][1], pf[qb][1], t1);
-        }
-        lsum[qb] += t0 + t1;
-    }
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+    return swap_halves_max(mx);
+}
 
-    // ---- O^T += V^T P^T: 128 dims x (32 * QB) queries, 64 keys: 16 MFMA
-    // steps i = (16-key step u = i / 4, dim block db = i % 4), V^T operands
-    // through the same kind of ring.
-    {
-        bf16x8 ring[RING];
+// Keys past S (a no-op unless tile j is the sequence's ragged last tile).
+// Lane half hh, register r of key block kb holds key 32 kb + 16 (r >> 3) +
+// 8 hh + (r & 7) of the tile.
+__device__ __forceinline__ void mask_tail(f32x16 (&sc)[2], int j, int S, int hh) {
+    const int base = j * KV_TILE + 8 * hh;
 #pragma unroll
-        for (int i0 = 0; i0 < RING - 1; ++i0)
-            ring[i0] = as_bf16x8(vt[v_chunk((i0 & 3) * 32 + n, 2 * (i0 >> 2) + hh)]);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i + RING - 1 < 16) {
-                const int u2 = (i + RING - 1) >> 2, db2 = (i + RING - 1) & 3;
-                ring[(i + RING - 1) % RING] = as_bf16x8(vt[v_chunk(db2 * 32 + n, 2 * u2 + hh)]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            const int u = i >> 2, db = i & 3;
+        for (int r = 0; r < 16; ++r)
+            if (base + 32 * kb + 16 * (r >> 3) + (r & 7) >= S) sc[kb][r] = -INFINITY;
+}
+
+// Between the stages: move m if this tile's weights overflow, then add the
+// tile's weight sum to l.  (The first tile's offset is set to its exact row
+// max before the loop, so the weights computed in stage A are always the ones
+// used on the fast path.)
+template <bool QK>
+__device__ __forceinline__ void settle_weights(f32x16 (&sc)[2], f32x16 (&sn)[2], uint32_t (&w)[16], float sum,
+                                               f32x16 (&o)[4], f32x16& negm, float& lsum) {
+    if (__builtin_amdgcn_ballot_w64(!(sum <= SUM_LIMIT)) != 0) {
+        const float shift = fmaxf(tile_max(sc), 0.0f);
+        const float alpha = __builtin_amdgcn_exp2f(-shift);
+        lsum *= alpha;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % RING], pf[qb][u >> 1][u & 1], o[qb][db],
-                                                                    0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        sc[0] -= shift;
+        sc[1] -= shift;
+        negm -= shift;
+        if (QK) {
+            sn[0] -= shift;
+            sn[1] -= shift;
         }
+        sum = 0.0f;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) weight_pair(sc, p, w, sum);
     }
+    lsum += sum;
+}
+
+// Stage B: O^T += V^T P^T over the tile's 64 keys (V^T part vt): 16 MFMA steps;
+// the weights of 16-key step u are w[4u .. 4u + 3], already in B-operand order.
+__device__ __forceinline__ void stage_b(const uint4* vt, const uint32_t (&w)[16], f32x16 (&o)[4], int n, int hh) {
+    bf16x8 pf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pf[u] = as_bf16x8(make_uint4(w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]));
+    bf16x8 ring[RING];
+#pragma unroll
+    for (int i0 = 0; i0 < RING - 1; ++i0) ring[i0] = v_operand(vt, i0, n, hh);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (i + RING - 1 < 16) ring[(i + RING - 1) % RING] = v_operand(vt, i + RING - 1, n, hh);
+        __builtin_amdgcn_sched_barrier(0);
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % RING], pf[i >> 2], o[i & 3], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// A tile with a successor: scores sc (current), sn (next, written), K' part of
+// the next tile kn, V^T part of the current tile vt, copies cp.
+__device__ __forceinline__ void tile_step(const uint4* kn, const uint4* vt, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                                          const bf16x8 (&qf)[8], f32x16 (&o)[4], f32x16& negm, float& lsum, int n,
+                                          int hh, const TileCopies& cp) {
+    uint32_t w[16];
+    float sum = 0.0f;
+    stage_a<true, true>(kn, qf, negm, sn, sc, w, sum, n, hh, &cp);
+    settle_weights<true>(sc, sn, w, sum, o, negm, lsum);
+    stage_b(vt, w, o, n, hh);
+}
+
+// The range's last tile (index j), masked.
+__device__ __forceinline__ void tile_step_last(const uint4* vt, f32x16 (&sc)[2], int j, int S,
+                                               const bf16x8 (&qf)[8], f32x16 (&o)[4], f32x16& negm, float& lsum,
+                                               int n, int hh) {
+    mask_tail(sc, j, S, hh);
+    uint32_t w[16];
+    float sum = 0.0f;
+    f32x16 none[2];
+    stage_a<false, true>(nullptr, qf, negm, none, sc, w, sum, n, hh);
+    settle_weights<false>(sc, none, w, sum, o, negm, lsum);
+    stage_b(vt, w, o, n, hh);
 }
 
 // One workgroup = BM queries of one (batch, head) against the key tiles
@@ -200,8 +246,15 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const uint4* __restrict__ q, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
     const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ part, int S, int ntiles, int nqt,
     int item0, int nsplit, float qmul, int has_rope) {
-    __shared__ uint4 lds0[TILE_CHUNKS];
-    __shared__ uint4 lds1[TILE_CHUNKS];
+    static_assert(QB == 1, "one 32-query block per wave");
+    // K' parts run one tile ahead of V^T parts, each through its own pair of
+    // buffers: step i reads K'(i + 1) and V^T(i) while K'(i + 2) and V^T(i + 1)
+    // land.  Distinct objects and a loop unrolled by two keep every buffer
+    // static, so the compiler does not make LDS reads wait for the copies.
+    __shared__ uint4 kb0[K_PART_CHUNKS];
+    __shared__ uint4 kb1[K_PART_CHUNKS];
+    __shared__ uint4 vb0[V_PART_CHUNKS];
+    __shared__ uint4 vb1[V_PART_CHUNKS];
 
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int item = item0 + logical / nsplit;
@@ -210,20 +263,40 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const int qt = item - (int)bh * nqt;
     const int tb = (int)((int64_t)f * ntiles / nsplit);
     const int te = (int)((int64_t)(f + 1) * ntiles / nsplit);
+    const int nt = te - tb;  // >= 1
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 31;
     const int hh = lane >> 5;
 
-    const uint4* src = ws + bh * (int64_t)ntiles * TILE_CHUNKS;
-    load_tile_async<NW>(src + (int64_t)tb * TILE_CHUNKS, lds0, wave, lane);
+    // The (batch, head) slice of prepared tiles as a buffer resource; tile
+    // tb + i starts at byte tile0 + i * TILE_BYTES (< 2^31 for S <= MAX_SEQ).
+    const __amdgpu_buffer_rsrc_t rsrc =
+        raw_rsrc(ws + bh * (int64_t)ntiles * TILE_CHUNKS, (uint32_t)ntiles * TILE_BYTES);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int tile0 = tb * TILE_BYTES;
+    auto copies = [&](int ki, uint4* kd, bool kon, int vi, uint4* vd) {
+        TileCopies c;
+        c.rsrc = rsrc;
+        c.ksoff = tile0 + ki * TILE_BYTES;
+        c.vsoff = tile0 + vi * TILE_BYTES + K_PART_BYTES;
+        c.kdst = kd;
+        c.vdst = vd;
+        c.kon = kon;
+        c.wave = wv;
+        c.lane = lane;
+        return c;
+    };
+    copy_to_lds<NW, K_PART_CHUNKS>(rsrc, tile0, kb0, wv, lane);
+    copy_to_lds<NW, V_PART_CHUNKS>(rsrc, tile0 + K_PART_BYTES, vb0, wv, lane);
+    if (nt > 1) copy_to_lds<NW, K_PART_CHUNKS>(rsrc, tile0 + TILE_BYTES, kb1, wv, lane);
 
     // ---- Q prologue: RoPE, fold scale*log2(e), round to bf16, keep resident.
-    bf16x8 qf[QB][8];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = qt * BM + (wave * QB + qb) * 32 + n;
+    bf16x8 qf[8];
+    const int rloc = wave * 32 + n;
+    const int row = qt * BM + rloc;
+    {
         const bool ok = row < S;
         const uint4* qrow = q + (bh * S + row) * 16;
 #pragma unroll
@@ -236,88 +309,83 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
             if (has_rope && ok) rotate4(fv, cos_t[(int64_t)row * 16 + c], sin_t[(int64_t)row * 16 + c]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) fv[e] *= qmul;
-            qf[qb][t] = as_bf16x8(pack8(fv));
+            qf[t] = as_bf16x8(pack8(fv));
         }
     }
 
-    f32x16 o[QB][4], negm[QB];
-    float lsum[QB];
+    f32x16 o[4], negm = f32x16{};
+    float lsum = 0.0f;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        negm[qb] = f32x16{};
-        lsum[qb] = 0.0f;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[qb][db] = f32x16{};
-    }
+    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
 
-    // Two distinct LDS buffers and a loop unrolled by two: the tile being read
-    // and the tile in flight are different objects, so the compiler does not
-    // make the reads wait for the prefetch.  Tiles tb .. te-2 take the
-    // unmasked path; the range's last tile takes the masked one (a no-op mask
-    // unless it is the sequence's ragged last tile).  Tile tb + i lives in
-    // buffer i mod 2.
-    const int last = te - 1;
-    int j = tb;
-    for (; j + 2 <= last; j += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        load_tile_async<NW>(src + (int64_t)(j + 1) * TILE_CHUNKS, lds1, wave, lane);
-        attn_tile<QB, false>(lds0, j, j == tb, S, n, hh, qf, o, negm, lsum);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        load_tile_async<NW>(src + (int64_t)(j + 2) * TILE_CHUNKS, lds0, wave, lane);
-        attn_tile<QB, false>(lds1, j + 1, false, S, n, hh, qf, o, negm, lsum);
-    }
-    if (j < last) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        load_tile_async<NW>(src + (int64_t)(j + 1) * TILE_CHUNKS, lds1, wave, lane);
-        attn_tile<QB, false>(lds0, j, j == tb, S, n, hh, qf, o, negm, lsum);
-        ++j;
-    }
+    // Scores of tile 0 (offset 0), then the pipelined steps.  Step i's scores
+    // live in sA for even i and sB for odd i.
+    f32x16 sA[2], sB[2];
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    attn_tile<QB, true>(((j - tb) & 1) ? lds1 : lds0, j, j == tb, S, n, hh, qf, o, negm, lsum);
+    {
+        uint32_t w[16];
+        float sum = 0.0f;
+        stage_a<true, false>(kb0, qf, negm, sA, sB, w, sum, n, hh);
+    }
+    // Offset of the first tile = its exact row max (masked first if it is
+    // also the range's last tile, so the max is over real keys only).
+    if (nt == 1) mask_tail(sA, te - 1, S, hh);
+    {
+        const float mx = tile_max(sA);
+        sA[0] -= mx;
+        sA[1] -= mx;
+        negm -= mx;
+    }
+    int i = 0;
+    for (; i + 2 <= nt - 1; i += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        tile_step(kb1, vb0, sA, sB, qf, o, negm, lsum, n, hh, copies(i + 2, kb0, true, i + 1, vb1));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        tile_step(kb0, vb1, sB, sA, qf, o, negm, lsum, n, hh, copies(i + 3, kb1, i + 3 < nt, i + 2, vb0));
+    }
+    if (i < nt - 1) {  // i = nt - 2, even: one more full step, then the last tile from sB / vb1
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        tile_step(kb1, vb0, sA, sB, qf, o, negm, lsum, n, hh, copies(i + 2, kb0, false, i + 1, vb1));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        tile_step_last(vb1, sB, te - 1, S, qf, o, negm, lsum, n, hh);
+    } else {  // i = nt - 1, even: the last tile from sA / vb0
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        tile_step_last(vb0, sA, te - 1, S, qf, o, negm, lsum, n, hh);
+    }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) settle(o[qb][db]);
+    for (int db = 0; db < 4; ++db) settle(o[db]);
 
     // ---- epilogue: lane (n, hh), register r of dim block db holds dim
     // 32 db + 8 (r >> 2) + 4 hh + (r & 3) of query n.
+    const float l = swap_halves_sum(lsum);
+    if (PARTIAL) {
+        float* pw = part + (int64_t)logical * PART_FLOATS;
+        float4* prow = reinterpret_cast<float4*>(pw + (int64_t)rloc * HEAD_DIM);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l = swap_halves_sum(lsum[qb]);
-        const int rloc = (wave * QB + qb) * 32 + n;
-        const int row = qt * BM + rloc;
-        if (PARTIAL) {
-            float* pw = part + (int64_t)logical * PART_FLOATS;
-            float4* prow = reinterpret_cast<float4*>(pw + (int64_t)rloc * HEAD_DIM);
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x16& acc = o[qb][db];
-                    prow[db * 8 + g * 2 + hh] =
-                        make_float4(acc[4 * g + 0], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
-                }
-            if (hh == 0) {
-                pw[BM * HEAD_DIM + rloc] = -negm[qb][0];
-                pw[BM * HEAD_DIM + BM + rloc] = l;
-            }
-        } else if (row < S) {
-            const float inv = 1.0f / l;
-            uint2* orow = out + (bh * S + row) * 32;
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x16& acc = o[qb][db];
-                    orow[db * 8 + g * 2 + hh] =
-                        make_uint2(pack_bf16x2(acc[4 * g + 0] * inv, acc[4 * g + 1] * inv),
-                                   pack_bf16x2(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv));
-                }
+            for (int g = 0; g < 4; ++g)
+                prow[db * 8 + g * 2 + hh] = make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2],
+                                                        o[db][4 * g + 3]);
+        if (hh == 0) {
+            pw[BM * HEAD_DIM + rloc] = -negm[0];
+            pw[BM * HEAD_DIM + BM + rloc] = l;
         }
+    } else if (row < S) {
+        const float inv = 1.0f / l;
+        uint2* orow = out + (bh * S + row) * 32;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                orow[db * 8 + g * 2 + hh] = make_uint2(pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                                       pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
     }
 }
 

@@ -152,8 +152,11 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
 
     const float sk = reinterpret_cast<const float*>(ws)[0];
     const float sv = reinterpret_cast<const float*>(ws)[1];
-    const uint4* src = reinterpret_cast<const uint4*>(ws + F8_HEADER_BYTES) + bh * (int64_t)ntiles * F8_TILE_CHUNKS;
-    copy_to_lds_async<NW, F8_TILE_CHUNKS>(src + (int64_t)tb * F8_TILE_CHUNKS, lds0, wave, lane);
+    // The (batch, head) slice of tiles as a buffer resource (byte offsets < 2^31 for S <= MAX_SEQ).
+    const __amdgpu_buffer_rsrc_t rsrc =
+        raw_rsrc(ws + F8_HEADER_BYTES + bh * (int64_t)ntiles * F8_TILE_BYTES, (uint32_t)ntiles * F8_TILE_BYTES);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, tb * F8_TILE_BYTES, lds0, wv, lane);
 
     // ---- Q prologue.  Largest |q'| is 448 q_scale (times sqrt(2) with RoPE);
     // choose e so that it maps to at most 448 after the factor qmul * sk.
@@ -206,17 +209,17 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     for (; j + 2 <= last; j += 2) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        copy_to_lds_async<NW, F8_TILE_CHUNKS>(src + (int64_t)(j + 1) * F8_TILE_CHUNKS, lds1, wave, lane);
+        copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (j + 1) * F8_TILE_BYTES, lds1, wv, lane);
         f8_tile<false>(lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        copy_to_lds_async<NW, F8_TILE_CHUNKS>(src + (int64_t)(j + 2) * F8_TILE_CHUNKS, lds0, wave, lane);
+        copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (j + 2) * F8_TILE_BYTES, lds0, wv, lane);
         f8_tile<false>(lds1, j + 1, false, S, n, hh, qscale, qf, o, negm, lsum);
     }
     if (j < last) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        copy_to_lds_async<NW, F8_TILE_CHUNKS>(src + (int64_t)(j + 1) * F8_TILE_CHUNKS, lds1, wave, lane);
+        copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (j + 1) * F8_TILE_BYTES, lds1, wv, lane);
         f8_tile<false>(lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
         ++j;
     }

@@ -32,8 +32,10 @@
  *     argument returns its status and enqueues nothing.  No exception crosses
  *     the ABI.  dit_last_error() returns a thread-local message for the last
  *     non-OK status of the calling thread.
- *   - D must be 128 (DIT_ERR_UNSUPPORTED otherwise).  Index arithmetic is
- *     64-bit; B*H*ceil(S/256) must fit in a signed 32-bit int.
+ *   - D must be 128 and S at most 2^21 = 2097152 (DIT_ERR_UNSUPPORTED
+ *     otherwise; the kernels address one head's prepared tiles with 32-bit
+ *     byte offsets).  Index arithmetic is 64-bit; B*H*ceil(S/256) must fit in
+ *     a signed 32-bit int and B*H must be at most 65535.
  *   - NaN/Inf inputs propagate to the output; they are not trapped.
  */
 #ifndef DIT_ATTN_H

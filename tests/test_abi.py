@@ -64,6 +64,9 @@ def test_workspace_bytes():
         assert dj.dit_attn_workspace_bytes(B, H, S, 128) == _expected_workspace(B, H, S), (B, H, S)
     assert dj.dit_attn_workspace_bytes(1, 1, 0, 128) == 0
     assert dj.dit_attn_workspace_bytes(1, 1, 64, 64) == 0
+    assert dj.dit_attn_workspace_bytes(1, 1, 2**21, 128) > 0
+    assert dj.dit_attn_workspace_bytes(1, 1, 2**21 + 1, 128) == 0
+    assert dj.dit_attn_workspace_bytes_fp8(1, 1, 2**21 + 1, 128) == 0
 
 
 FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
@@ -89,6 +92,7 @@ def _fwd(**kw):
     (dict(S_txt=0, S_img=0), dj.DIT_ERR_INVALID_ARG),
     (dict(S_txt=2**31 - 1, S_img=1), dj.DIT_ERR_INVALID_ARG),  # S overflows int
     (dict(D=64), dj.DIT_ERR_UNSUPPORTED),
+    (dict(S_txt=2**21, S_img=1), dj.DIT_ERR_UNSUPPORTED),      # longer than the longest supported sequence
     (dict(D=0), dj.DIT_ERR_INVALID_ARG),
     (dict(dtype=1), dj.DIT_ERR_UNSUPPORTED),
     (dict(dtype=7), dj.DIT_ERR_INVALID_ARG),
