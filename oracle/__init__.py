@@ -20,6 +20,9 @@ What it computes, in float64, as the plain definition with no tiling:
   paper's reference list (catalogue page, "Other references"). The joint
   text+image sequence is the one the xDiT abstract describes as growing with
   resolution.
+* Ring blocks (``oracle.ring``): attention of a query shard over one key/value
+  block with the row log-sum-exp, and the exact merge of two such partial
+  results (ring attention, in the same reference list).
 * ``oracle.brute``: the same steps as pure-Python scalar loops, used to pin
   the numpy version on tiny inputs.
 
@@ -29,5 +32,7 @@ forms and invariants.
 """
 from .rope import rope_angles, rope_apply
 from .attention import attention, joint_attention, softmax_probs, lse
+from .ring import block_attention, merge_lse
 
-__all__ = ["rope_angles", "rope_apply", "attention", "joint_attention", "softmax_probs", "lse"]
+__all__ = ["rope_angles", "rope_apply", "attention", "joint_attention", "softmax_probs", "lse", "block_attention",
+           "merge_lse"]

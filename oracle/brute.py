@@ -57,3 +57,29 @@ def joint_attention(q, k, v, pos=None, axes_dim=None, theta=10000.0, scale=None)
             ob.append(oh)
         out.append(ob)
     return out
+
+
+def row_lse(q, k, pos_q=None, pos_k=None, axes_dim=None, theta=10000.0, scale=None):
+    """Natural-log log-sum-exp of each query row's scaled scores, nested lists
+    [B][H][Sq] from q [B][H][Sq][D] and k [B][H][Sk][D]; pos_q / pos_k are the
+    token coordinates of the rows (both None: no RoPE)."""
+    B, H, Sq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = []
+    for b in range(B):
+        ob = []
+        for h in range(H):
+            qs = [list(map(float, r)) for r in q[b][h]]
+            ks = [list(map(float, r)) for r in k[b][h]]
+            if pos_q is not None:
+                qs = [rotate_row(qs[i], pos_q[i], axes_dim, theta) for i in range(Sq)]
+                ks = [rotate_row(ks[j], pos_k[j], axes_dim, theta) for j in range(len(ks))]
+            oh = []
+            for i in range(Sq):
+                s = [scale * math.fsum(qs[i][d] * ks[j][d] for d in range(D)) for j in range(len(ks))]
+                m = max(s)
+                oh.append(m + math.log(math.fsum(math.exp(x - m) for x in s)))
+            ob.append(oh)
+        out.append(ob)
+    return out

@@ -284,3 +284,80 @@ def test_e4m3_decode_closed_forms():
     assert got.tolist() == [1.0, 448.0, 2.0 ** -6, 2.0 ** -9, -3.0, 0.0, -0.0]
     assert np.isnan(e4m3_decode(np.array([0x7f, 0xff], np.uint8))).all()
     assert dequantize(np.array([0x40], np.uint8), 0.25).tolist() == [0.5]
+
+
+# ---------------------------------------------------------------- ring blocks and the log-sum-exp merge
+
+def _positions_2d(n, width):
+    return np.stack([np.arange(n) // width, np.arange(n) % width], axis=1).astype(np.int64)
+
+
+def test_block_lse_matches_brute_force_with_block_positions():
+    from oracle import block_attention
+    rng = np.random.default_rng(40)
+    q, k, v = _rand(rng, 1, 2, 3, 8), _rand(rng, 1, 2, 5, 8), _rand(rng, 1, 2, 5, 8)
+    pos_q = _positions_2d(3, 2) + np.array([1, 0])      # the query shard sits elsewhere in the grid
+    pos_k = _positions_2d(5, 3)
+    aq, ak = rope_angles(pos_q, (4, 4), 100.0), rope_angles(pos_k, (4, 4), 100.0)
+    o, L = block_attention(q, k, v, aq, ak)
+    want = brute.row_lse(q.tolist(), k.tolist(), pos_q.tolist(), pos_k.tolist(), (4, 4), 100.0)
+    assert np.max(np.abs(L - np.array(want))) <= 1e-12
+    # O of the block is ordinary attention of the rotated rows
+    qr = np.array(brute.rotate_row(q[0, 1, 2].tolist(), pos_q[2].tolist(), (4, 4), 100.0))
+    kr = np.array([brute.rotate_row(k[0, 1, j].tolist(), pos_k[j].tolist(), (4, 4), 100.0) for j in range(5)])
+    s = kr @ qr / math.sqrt(8)
+    p = np.exp(s - s.max())
+    assert np.max(np.abs(o[0, 1, 2] - (p / p.sum()) @ v[0, 1])) <= 1e-12
+
+
+def test_ring_blocks_merge_to_joint_attention():
+    """Three uneven key blocks, each rotated with its own positions, folded in
+    ring order: equal to attention over the whole joint sequence."""
+    from oracle import block_attention, merge_lse
+    rng = np.random.default_rng(41)
+    S, D = 37, 16
+    q, k, v = _rand(rng, 1, 2, S, D), _rand(rng, 1, 2, S, D), _rand(rng, 1, 2, S, D)
+    pos = _positions_2d(S, 6)
+    ang = rope_angles(pos, (8, 8), 10000.0)
+    whole, L_whole = block_attention(q, k, v, ang, ang)
+    bounds = [0, 9, 30, S]
+    o = L = None
+    for b0, b1 in zip(bounds[:-1], bounds[1:]):
+        ob, lb = block_attention(q, k[:, :, b0:b1], v[:, :, b0:b1], ang, ang[b0:b1])
+        o, L = (ob, lb) if o is None else merge_lse(o, L, ob, lb)
+    assert np.max(np.abs(o - joint_attention(q, k, v, ang))) <= 1e-12
+    assert np.max(np.abs(L - L_whole)) <= 1e-12
+    # a fold that forgets to renormalise by the merged L fails
+    o1, l1 = block_attention(q, k[:, :, :9], v[:, :, :9], ang, ang[:9])
+    o2, l2 = block_attention(q, k[:, :, 9:], v[:, :, 9:], ang, ang[9:])
+    wrong = 0.5 * (o1 + o2)
+    assert np.max(np.abs(wrong - whole)) > 1e-3
+
+
+def test_merge_lse_closed_forms():
+    from oracle import merge_lse
+    rng = np.random.default_rng(42)
+    o, l = _rand(rng, 1, 2, 4, 8), rng.normal(size=(1, 2, 4))
+    m, L = merge_lse(o, l, o, l)                          # a block merged with its copy
+    assert np.max(np.abs(m - o)) <= 1e-15 and np.max(np.abs(L - (l + math.log(2.0)))) <= 1e-15
+    m, L = merge_lse(o, l, 7.0 * o, np.full_like(l, -np.inf))   # empty second block
+    assert np.array_equal(m, o) and np.array_equal(L, l)
+    # two blocks of identical keys: weights in proportion to their sizes
+    oa, ob = _rand(rng, 1, 1, 1, 8), _rand(rng, 1, 1, 1, 8)
+    s = 0.7
+    m, L = merge_lse(oa, np.array([[[s + math.log(3)]]]), ob, np.array([[[s + math.log(5)]]]))
+    assert np.max(np.abs(m - (3 * oa + 5 * ob) / 8)) <= 1e-15
+    assert abs(L[0, 0, 0] - (s + math.log(8))) <= 1e-15
+
+
+def test_lse_identical_keys_closed_form():
+    from oracle import block_attention
+    rng = np.random.default_rng(43)
+    q = _rand(rng, 1, 1, 3, 8)
+    krow = _rand(rng, 1, 1, 1, 8)
+    k = np.repeat(krow, 11, axis=2)
+    v = _rand(rng, 1, 1, 11, 8)
+    o, L = block_attention(q, k, v)
+    s = (q[0, 0] @ krow[0, 0, 0]) / math.sqrt(8)
+    assert np.max(np.abs(L[0, 0] - (s + math.log(11)))) <= 1e-13
+    assert np.max(np.abs(o[0, 0] - v[0, 0].mean(axis=0))) <= 1e-13
