@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the path runs in the library's HIP
 kernels.  Functions keep the C names (``dit_attn_forward``, ``dit_rope_tables``,
-``dit_attn_workspace_bytes``, ``dit_attn_prepare_kv``, ``dit_attn_core``) and
+``dit_attn_workspace_bytes``, ``dit_attn_prepare_kv``, ``dit_attn_core``,
+``dit_attn_core_lse``, ``dit_attn_merge_lse`` and the ``_fp8`` entries) and
 take torch tensors (their device pointers are passed) or plain integers as
 pointers.  A missing library raises ``RuntimeError``: there is no fallback.
 """
@@ -17,7 +18,7 @@ __all__ = [
     "LIB_PATH", "DitAttnError", "lib", "lib_loaded", "dit_last_error", "dit_abi_version",
     "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_kv",
     "dit_attn_core", "dit_attn_workspace_bytes_fp8", "dit_attn_prepare_kv_fp8", "dit_attn_core_fp8",
-    "dit_attn_forward_fp8", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
+    "dit_attn_forward_fp8", "dit_attn_core_lse", "dit_attn_merge_lse", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
     "DIT_ERR_NO_DEVICE", "DIT_ERR_OUT_OF_MEMORY", "DIT_ERR_LAUNCH", "DIT_DTYPE_BF16",
     "DIT_DTYPE_FP8_E4M3",
 ]
@@ -54,6 +55,8 @@ _SIGNATURES = {
     "dit_attn_prepare_kv_fp8": (_I, [_P, _P, _F, _F, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P]),
     "dit_attn_core_fp8": (_I, [_P, _F, _P, _P, _P, ctypes.c_size_t, _P, _I, _I, _I, _I, _F, _P]),
     "dit_attn_forward_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "dit_attn_core_lse": (_I, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P, _I, _I, _I, _I, _F, _P]),
+    "dit_attn_merge_lse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -178,6 +181,35 @@ def dit_attn_core(q, rope_cos, rope_sin, workspace, out, scale: Optional[float] 
     _check(lib().dit_attn_core(_ptr(q), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace), int(workspace_bytes),
                                _ptr(out), B, H, S, D, float(scale), _stream(stream)))
     return out
+
+
+def dit_attn_core_lse(q, rope_cos, rope_sin, workspace, out, lse=None, scale: Optional[float] = None,
+                      workspace_bytes: Optional[int] = None, stream=None):
+    """dit_attn_core plus the row log-sum-exp [B, H, S] fp32 (allocated when not given); returns (out, lse)."""
+    import torch
+    B, H, S, D = (int(s) for s in q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _check(lib().dit_attn_core_lse(_ptr(q), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace), int(workspace_bytes),
+                                   _ptr(out), _ptr(lse), B, H, S, D, float(scale), _stream(stream)))
+    return out, lse
+
+
+def dit_attn_merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
+    """Fold two partial results over disjoint key blocks; out / lse_out may be o_a / lse_a (in place)."""
+    import torch
+    B, H, S, D = (int(s) for s in o_a.shape)
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    _check(lib().dit_attn_merge_lse(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse_out),
+                                    B, H, S, D, _stream(stream)))
+    return out, lse_out
 
 
 # ---------------------------------------------------------------- fp8 (e4m3 codes + per-tensor scales)

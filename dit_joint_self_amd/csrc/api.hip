@@ -22,8 +22,10 @@
 namespace dit {
 hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, const float* sin_t,
                              void* ws, int BH, int S, hipStream_t stream);
+hipError_t launch_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* out,
+                            float* lse_out, int64_t rows, hipStream_t stream);
 hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
-                            void* out, int BH, int S, float qmul, hipStream_t stream);
+                            void* out, float* lse, int BH, int S, float qmul, hipStream_t stream);
 size_t core_partial_bytes(int BH, int S);
 hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_t, const float* sin_t, void* ws,
                                  int BH, int S, float k_scale, float v_scale, hipStream_t stream);
@@ -36,7 +38,7 @@ hipError_t launch_rope_tables(const int32_t* pos, int S, int n_axes, const int32
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kMaxDevices = 64;
 // Smallest query tile any kernel variant uses; bounds the workgroup count.
 constexpr int kMinBlockM = 128;
@@ -192,9 +194,9 @@ dit_status_t dit_attn_prepare_kv(const void* k, const void* v, const float* rope
                     "prepare_kv_kernel");
 }
 
-dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin, const void* workspace,
-                           size_t workspace_bytes, void* out, int B, int H, int S, int D, float scale,
-                           void* stream) {
+static dit_status_t core_impl(const void* q, const float* rope_cos, const float* rope_sin, const void* workspace,
+                              size_t workspace_bytes, void* out, float* lse, int B, int H, int S, int D, float scale,
+                              void* stream) {
     if (!q || !workspace || !out) return fail(DIT_ERR_INVALID_ARG, "q, workspace and out must be non-NULL");
     dit_status_t st = check_shape(B, H, S, D);
     if (st != DIT_OK) return st;
@@ -207,12 +209,63 @@ dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* ro
     const size_t tbytes = (size_t)B * H * S * D * 2;
     if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, workspace, need))
         return fail(DIT_ERR_INVALID_ARG, "out overlaps q or the workspace");
+    if (lse) {
+        const size_t lbytes = (size_t)B * H * S * 4;
+        if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(DIT_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+        if (overlaps(lse, lbytes, out, tbytes) || overlaps(lse, lbytes, q, tbytes) ||
+            overlaps(lse, lbytes, workspace, need))
+            return fail(DIT_ERR_INVALID_ARG, "lse overlaps q, out or the workspace");
+    }
     if ((st = check_device()) != DIT_OK) return st;
     const float qmul = (float)((double)scale * 1.4426950408889634073599);  // scale * log2(e)
     void* part = static_cast<char*>(const_cast<void*>(workspace)) + tiles_bytes(B, H, S);
-    return launched(dit::launch_attn_core(q, rope_cos, rope_sin, workspace, part, out, B * H, S, qmul,
+    return launched(dit::launch_attn_core(q, rope_cos, rope_sin, workspace, part, out, lse, B * H, S, qmul,
                                           static_cast<hipStream_t>(stream)),
                     "attn_core_kernel");
+}
+
+dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin, const void* workspace,
+                           size_t workspace_bytes, void* out, int B, int H, int S, int D, float scale,
+                           void* stream) {
+    return core_impl(q, rope_cos, rope_sin, workspace, workspace_bytes, out, nullptr, B, H, S, D, scale, stream);
+}
+
+dit_status_t dit_attn_core_lse(const void* q, const float* rope_cos, const float* rope_sin, const void* workspace,
+                               size_t workspace_bytes, void* out, float* lse, int B, int H, int S, int D,
+                               float scale, void* stream) {
+    if (!lse) return fail(DIT_ERR_INVALID_ARG, "lse must be non-NULL");
+    return core_impl(q, rope_cos, rope_sin, workspace, workspace_bytes, out, lse, B, H, S, D, scale, stream);
+}
+
+// Two regions either coincide exactly (an allowed in-place fold) or are disjoint.
+static bool same_or_disjoint(const void* a, const void* b, size_t bytes) {
+    return a == b || !overlaps(a, bytes, b, bytes);
+}
+
+dit_status_t dit_attn_merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* out,
+                                float* lse_out, int B, int H, int S, int D, void* stream) {
+    if (!o_a || !lse_a || !o_b || !lse_b || !out || !lse_out)
+        return fail(DIT_ERR_INVALID_ARG, "o_a, lse_a, o_b, lse_b, out and lse_out must be non-NULL");
+    dit_status_t st = check_shape(B, H, S, D);
+    if (st != DIT_OK) return st;
+    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(out))
+        return fail(DIT_ERR_INVALID_ARG, "o_a, o_b and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse_a) | reinterpret_cast<uintptr_t>(lse_b) |
+         reinterpret_cast<uintptr_t>(lse_out)) & 3u)
+        return fail(DIT_ERR_INVALID_ARG, "lse arrays must be 4-byte aligned");
+    const size_t tbytes = (size_t)B * H * S * D * 2, lbytes = (size_t)B * H * S * 4;
+    if (!same_or_disjoint(out, o_a, tbytes) || !same_or_disjoint(out, o_b, tbytes))
+        return fail(DIT_ERR_INVALID_ARG, "out must be o_a, o_b or disjoint from both");
+    if (!same_or_disjoint(lse_out, lse_a, lbytes) || !same_or_disjoint(lse_out, lse_b, lbytes))
+        return fail(DIT_ERR_INVALID_ARG, "lse_out must be lse_a, lse_b or disjoint from both");
+    if (overlaps(out, tbytes, lse_a, lbytes) || overlaps(out, tbytes, lse_b, lbytes) ||
+        overlaps(out, tbytes, lse_out, lbytes) || overlaps(lse_out, lbytes, o_a, tbytes) ||
+        overlaps(lse_out, lbytes, o_b, tbytes))
+        return fail(DIT_ERR_INVALID_ARG, "an output overlaps an input of the other kind");
+    if ((st = check_device()) != DIT_OK) return st;
+    return launched(dit::launch_lse_merge(o_a, lse_a, o_b, lse_b, out, lse_out, (int64_t)B * H * S,
+                                          static_cast<hipStream_t>(stream)),
+                    "lse_merge_kernel");
 }
 
 // ---------------------------------------------------------------- fp8
@@ -354,7 +407,7 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const
     if (e == hipSuccess) {
         const float qmul = (float)((double)scale * 1.4426950408889634073599);
         e = dit::launch_attn_core(q, rope_cos, rope_sin, ws, static_cast<char*>(ws) + tiles_bytes(B, H, S), out,
-                                  B * H, S, qmul, s);
+                                  nullptr, B * H, S, qmul, s);
     }
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return launched(e, "dit_attn_forward kernels");

@@ -15,6 +15,7 @@ constexpr int NW = 8;                 // waves per workgroup (two per SIMD)
 constexpr int QB = 1;                 // 32-query blocks per wave
 constexpr int BM = NW * 32 * QB;      // queries per workgroup
 constexpr int MI355X_CUS = 256;       // workgroups resident at once (one per CU)
+constexpr float LN2 = 0.693147180559945309f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));   // one 32x32 MFMA accumulator
 
@@ -117,7 +118,7 @@ inline size_t core_partial_bytes_for(const CorePlan& p) {
     return (size_t)p.split * p.nsplit * PART_FLOATS * sizeof(float);
 }
 
-hipError_t launch_merge(const float* part, void* out, int S, int nqt, int item0, int nsplit, int split_items,
-                        hipStream_t stream);
+hipError_t launch_merge(const float* part, void* out, float* lse, int S, int nqt, int item0, int nsplit,
+                        int split_items, hipStream_t stream);
 
 }  // namespace dit

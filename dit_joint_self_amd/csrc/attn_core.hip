@@ -244,8 +244,8 @@ __device__ __forceinline__ void tile_step_last(const uint4* vt, f32x16 (&sc)[2],
 template <bool PARTIAL>
 __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const uint4* __restrict__ q, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
-    const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ part, int S, int ntiles, int nqt,
-    int item0, int nsplit, float qmul, int has_rope) {
+    const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, int S,
+    int ntiles, int nqt, int item0, int nsplit, float qmul, int has_rope) {
     static_assert(QB == 1, "one 32-query block per wave");
     // K' parts run one tile ahead of V^T parts, each through its own pair of
     // buffers: step i reads K'(i + 1) and V^T(i) while K'(i + 2) and V^T(i + 1)
@@ -378,6 +378,10 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
             pw[BM * HEAD_DIM + BM + rloc] = l;
         }
     } else if (row < S) {
+        // Row log-sum-exp of the scaled scores (natural log): the kernel's
+        // base-2 scores are scale * log2(e) * q'.k', offset by m, so
+        // sum_j exp(scale q'.k_j) = 2^m * l.
+        if (lse != nullptr && hh == 0) lse[bh * S + row] = LN2 * (-negm[0] + __builtin_amdgcn_logf(l));
         const float inv = 1.0f / l;
         uint2* orow = out + (bh * S + row) * 32;
 #pragma unroll
@@ -393,7 +397,8 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
 // softmax merge, exact): M = max m_f, O = sum 2^(m_f - M) O_f / sum 2^(m_f - M) l_f.
 // One workgroup per 16 rows of an item; 16 threads per row, 8 dims each.
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part, uint4* __restrict__ out,
-                                                         int S, int nqt, int item0, int nsplit) {
+                                                         float* __restrict__ lse, int S, int nqt, int item0,
+                                                         int nsplit) {
     const int item_local = blockIdx.x / (BM / 16);
     const int rloc = (blockIdx.x % (BM / 16)) * 16 + (threadIdx.x >> 4);
     const int seg = threadIdx.x & 15;
@@ -419,11 +424,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= inv;
     out[(bh * S + row) * 16 + seg] = pack8(acc);
+    if (lse != nullptr && seg == 0) lse[bh * S + row] = LN2 * (M + __builtin_amdgcn_logf(L));
 }
 
-hipError_t launch_merge(const float* part, void* out, int S, int nqt, int item0, int nsplit, int split_items,
-                        hipStream_t stream) {
-    attn_merge_kernel<<<split_items * (BM / 16), 256, 0, stream>>>(part, static_cast<uint4*>(out), S, nqt, item0,
+hipError_t launch_merge(const float* part, void* out, float* lse, int S, int nqt, int item0, int nsplit,
+                        int split_items, hipStream_t stream) {
+    attn_merge_kernel<<<split_items * (BM / 16), 256, 0, stream>>>(part, static_cast<uint4*>(out), lse, S, nqt, item0,
                                                                    nsplit);
     return hipGetLastError();
 }
@@ -431,7 +437,7 @@ hipError_t launch_merge(const float* part, void* out, int S, int nqt, int item0,
 size_t core_partial_bytes(int BH, int S) { return core_partial_bytes_for(core_plan(BH, S)); }
 
 hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
-                            void* out, int BH, int S, float qmul, hipStream_t stream) {
+                            void* out, float* lse, int BH, int S, float qmul, hipStream_t stream) {
     const CorePlan p = core_plan(BH, S);
     const uint4* wsv = static_cast<const uint4*>(ws);
     const uint4* qv = static_cast<const uint4*>(q);
@@ -439,14 +445,14 @@ hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_
     const float4* sv = reinterpret_cast<const float4*>(sin_t);
     const int rope = cos_t != nullptr;
     if (p.full > 0) {
-        attn_core_kernel<false><<<p.full, NW * 64, 0, stream>>>(qv, cv, sv, wsv, static_cast<uint2*>(out), nullptr,
-                                                               S, p.ntiles, p.nqt, 0, 1, qmul, rope);
+        attn_core_kernel<false><<<p.full, NW * 64, 0, stream>>>(qv, cv, sv, wsv, static_cast<uint2*>(out), lse,
+                                                               nullptr, S, p.ntiles, p.nqt, 0, 1, qmul, rope);
     }
     if (p.split > 0) {
         float* pt = static_cast<float*>(part);
         attn_core_kernel<true><<<p.split * p.nsplit, NW * 64, 0, stream>>>(
-            qv, cv, sv, wsv, nullptr, pt, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
-        launch_merge(pt, out, S, p.nqt, p.full, p.nsplit, p.split, stream);
+            qv, cv, sv, wsv, nullptr, nullptr, pt, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
+        launch_merge(pt, out, lse, S, p.nqt, p.full, p.nsplit, p.split, stream);
     }
     return hipGetLastError();
 }

@@ -275,7 +275,7 @@ hipError_t launch_attn_core_fp8(const void* q, float q_scale, const float* cos_t
         float* pt = static_cast<float*>(part);
         attn_core_fp8_kernel<true><<<p.split * p.nsplit, NW * 64, 0, stream>>>(
             qv, q_scale, cv, sv, wsv, nullptr, pt, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
-        launch_merge(pt, out, S, p.nqt, p.full, p.nsplit, p.split, stream);
+        launch_merge(pt, out, nullptr, S, p.nqt, p.full, p.nsplit, p.split, stream);
     }
     return hipGetLastError();
 }

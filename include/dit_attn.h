@@ -140,6 +140,39 @@ dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* ro
                            int B, int H, int S, int D, float scale, void* stream);
 
 /*
+ * Ring-attention building blocks.  The xDiT paper page lists "Ring Attention
+ * with Blockwise Transformers for Near-Infinite Context" among its references
+ * and the xDiT runner configuration in the MXFP4/Quark on MI350 blog has a
+ * ring degree: a rank attends its query shard to one key/value block at a
+ * time and folds the partial results together with their row log-sum-exp.
+ *
+ * dit_attn_core_lse  dit_attn_core plus lse: device fp32 [B, H, S], 4-byte
+ *   aligned, written with the natural-log log-sum-exp of each query row's
+ *   scaled scores, L = log(sum_j exp(scale * q'.k'_j)) over the keys of the
+ *   workspace (computed from the same rounded Q'' and K' and the same bf16
+ *   weights as out).  For a ring step, prepare the key/value block with the
+ *   block's own RoPE tables (dit_attn_prepare_kv) and pass the query shard's
+ *   tables here: RoPE of a row depends only on its own position.  The shard
+ *   and the block have the same length S.  lse must not overlap q, out or the
+ *   workspace.
+ *
+ * dit_attn_merge_lse  folds two partial results over disjoint key blocks:
+ *   out = w_a o_a + w_b o_b with w_x = exp(lse_x - lse_out) and
+ *   lse_out = log(exp(lse_a) + exp(lse_b)); fp32 arithmetic, out rounded to
+ *   bf16 RNE.  o_a, o_b, out: device bf16 [B, H, S, D], 16-byte aligned;
+ *   lse_a, lse_b, lse_out: device fp32 [B, H, S], 4-byte aligned.  out may be
+ *   exactly o_a or o_b and lse_out exactly lse_a or lse_b (in-place folding);
+ *   any other overlap is DIT_ERR_INVALID_ARG.  A row whose two LSEs are both
+ *   -inf (no keys on either side) yields NaN.
+ */
+dit_status_t dit_attn_core_lse(const void* q, const float* rope_cos, const float* rope_sin,
+                               const void* workspace, size_t workspace_bytes, void* out, float* lse,
+                               int B, int H, int S, int D, float scale, void* stream);
+
+dit_status_t dit_attn_merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                                void* out, float* lse_out, int B, int H, int S, int D, void* stream);
+
+/*
  * fp8 path: Q, K, V as OCP e4m3 codes with one fp32 scale per tensor (the AMD
  * RDNA 4 xDiT blog's fp8 attention backend; the pages give no format, the
  * reading is OCP e4m3, max 448).  Real values are code * scale.

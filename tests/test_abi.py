@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     lib = dj.lib()
     for name in dj.EXPORTED_SYMBOLS:
         assert getattr(lib, name) is not None
-    assert dj.dit_abi_version() == 1
+    assert dj.dit_abi_version() == 2
 
 
 def _expected_workspace(B, H, S):
@@ -175,3 +175,35 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert L.dit_attn_core_fp8(FAKE, float("inf"), None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
     if _no_device():
         assert call() == dj.DIT_ERR_NO_DEVICE
+
+
+def test_lse_entry_points_reject_bad_arguments():
+    L = dj.lib()
+    need = dj.dit_attn_workspace_bytes(1, 2, 8, 128)
+    ws = 0x10000000
+    lse = 0x20000000
+    core = lambda **kw: L.dit_attn_core_lse(kw.get("q", FAKE), None, None, ws, need, kw.get("out", FAKE * 3),
+                                            kw.get("lse", lse), 1, 2, 8, 128, 0.1, None)
+    assert core(lse=None) == dj.DIT_ERR_INVALID_ARG
+    assert core(lse=lse + 2) == dj.DIT_ERR_INVALID_ARG                 # misaligned
+    assert core(lse=FAKE * 3 + 64) == dj.DIT_ERR_INVALID_ARG           # inside out
+    assert core(lse=ws + 128) == dj.DIT_ERR_INVALID_ARG                # inside the workspace
+    assert core(q=None) == dj.DIT_ERR_INVALID_ARG
+    tb, lb = 2 * 8 * 128 * 2, 2 * 8 * 4
+    oa, ob, o = 0x30000000, 0x40000000, 0x50000000
+    la, lb_, lo = 0x60000000, 0x70000000, 0x80000000
+    merge = lambda **kw: L.dit_attn_merge_lse(kw.get("oa", oa), kw.get("la", la), kw.get("ob", ob), kw.get("lb", lb_),
+                                              kw.get("o", o), kw.get("lo", lo), 1, 2, 8, kw.get("D", 128), None)
+    assert merge(oa=None) == dj.DIT_ERR_INVALID_ARG
+    assert merge(lo=None) == dj.DIT_ERR_INVALID_ARG
+    assert merge(D=64) == dj.DIT_ERR_UNSUPPORTED
+    assert merge(o=oa + 16) == dj.DIT_ERR_INVALID_ARG                  # partial overlap with o_a
+    assert merge(lo=la + 4) == dj.DIT_ERR_INVALID_ARG                  # partial overlap with lse_a
+    assert merge(o=la) == dj.DIT_ERR_INVALID_ARG                       # out over an lse input
+    assert merge(lo=ob + 64) == dj.DIT_ERR_INVALID_ARG                 # lse_out inside o_b
+    assert merge(o=oa + 8) == dj.DIT_ERR_INVALID_ARG                   # misaligned
+    assert merge(la=la + 1) == dj.DIT_ERR_INVALID_ARG
+    if _no_device():                                                   # exact in-place folding is valid
+        assert merge(o=oa, lo=la) == dj.DIT_ERR_NO_DEVICE
+        assert merge(o=ob, lo=lb_) == dj.DIT_ERR_NO_DEVICE
+        assert core() == dj.DIT_ERR_NO_DEVICE
