@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--workload", default="flux2048", choices=list(W.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ring", type=int, default=1,
+                    help="time one rank's share of a ring of this many ranks (bf16 workloads): its query shard "
+                         "against every key/value block, folded with the LSE merge")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -97,10 +100,13 @@ def bf16_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
 
 
-def cpu_baseline(w, f64_head, budget_s):
+def cpu_baseline(w, f64_head, budget_s, gpu_rows=None):
     """The float64 oracle as it stands, on the first query rows of successive
     heads until the time budget is spent; TFLOP/s at 4 * rows * S * D flop.
-    ``f64_head(h)`` returns the head's (q, k, v) as float64 [1, 1, S, D]."""
+    ``f64_head(h)`` returns the head's (q, k, v) as float64 [1, 1, S, D].
+    ``gpu_rows(h, rows)`` returns the timed GPU output of those rows of head h
+    ([1, 1, R, D], float64): the oracle rows computed for the timing are also
+    compared with it (max |diff|, reported as the sample's parity)."""
     from oracle import joint_attention, rope_angles
     try:
         from threadpoolctl import threadpool_info
@@ -113,9 +119,14 @@ def cpu_baseline(w, f64_head, budget_s):
     t0 = time.perf_counter()
     done_rows = 0
     heads = 0
+    parity = None
     for h in range(w.H):
         q, k, v = f64_head(h)
-        joint_attention(q, k, v, ang, rows=rows)
+        ref = joint_attention(q, k, v, ang, rows=rows)
+        if gpu_rows is not None and h == 0:
+            tc = time.perf_counter()
+            parity = float(np.abs(gpu_rows(h, rows) - ref).max())
+            t0 += time.perf_counter() - tc  # the comparison is not oracle time
         done_rows += rows_per_head
         heads += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -125,7 +136,95 @@ def cpu_baseline(w, f64_head, budget_s):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{w.name}: first {rows_per_head} query rows x {heads} of {w.H} heads vs all {w.S} keys, "
                       f"float64 numpy (incl. RoPE of the head's K), {dt:.1f} s",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "sample_parity_max_abs": parity}
+
+
+def ring_bench(args, w, torch, dj):
+    """One rank of a P-way ring on one GPU: the rank holds query shard 0 (S/P rows)
+    and receives the P key/value blocks of S/P tokens in ring order; for each
+    block it prepares the tiles (the block's own RoPE tables), runs attention
+    with the row LSE and folds the result into its running output in place."""
+    P = args.ring
+    if w.dtype != "bf16" or w.S % P:
+        print(f"--ring {P} needs a bf16 workload whose S is a multiple of {P}", file=sys.stderr)
+        sys.exit(2)
+    n = w.S // P
+    stream = torch.cuda.current_stream()
+    qb, kb, vb = W.make_bf16_inputs(w)
+    q, k, v = bf16_dev(qb, torch), bf16_dev(kb, torch), bf16_dev(vb, torch)
+    pos = W.positions(w)
+    tabs = [dj.dit_rope_tables(torch.from_numpy(np.ascontiguousarray(pos[b * n:(b + 1) * n])).to("cuda"),
+                               w.axes_dim, w.theta) for b in range(P)]
+    qs = q[:, :, :n].contiguous()
+    kbk = [k[:, :, b * n:(b + 1) * n].contiguous() for b in range(P)]
+    vbk = [v[:, :, b * n:(b + 1) * n].contiguous() for b in range(P)]
+    ws_bytes = dj.dit_attn_workspace_bytes(w.B, w.H, n, w.D)
+    ws = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(P)]
+    outs = [torch.empty_like(qs) for _ in range(P)]
+    lses = [torch.empty((w.B, w.H, n), dtype=torch.float32, device="cuda") for _ in range(P)]
+    scale = 1.0 / math.sqrt(w.D)
+
+    def step(ev):
+        for b in range(P):
+            ev.append(torch.cuda.Event(enable_timing=True)); ev[-1].record(stream)
+            dj.dit_attn_prepare_kv(kbk[b], vbk[b], tabs[b][0], tabs[b][1], ws[b], ws_bytes, stream=stream)
+            ev.append(torch.cuda.Event(enable_timing=True)); ev[-1].record(stream)
+            dj.dit_attn_core_lse(qs, tabs[0][0], tabs[0][1], ws[b], outs[b], lses[b], scale=scale,
+                                 workspace_bytes=ws_bytes, stream=stream)
+            ev.append(torch.cuda.Event(enable_timing=True)); ev[-1].record(stream)
+            if b > 0:
+                dj.dit_attn_merge_lse(outs[0], lses[0], outs[b], lses[b], out=outs[0], lse_out=lses[0],
+                                      stream=stream)
+            ev.append(torch.cuda.Event(enable_timing=True)); ev[-1].record(stream)
+
+    for _ in range(args.warmup):
+        step([])
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[] for _ in range(K)]
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    prep = [sum(e[4 * b].elapsed_time(e[4 * b + 1]) for b in range(P)) for e in evs]
+    core = [sum(e[4 * b + 1].elapsed_time(e[4 * b + 2]) for b in range(P)) for e in evs]
+    merge = [sum(e[4 * b + 2].elapsed_time(e[4 * b + 3]) for b in range(1, P)) for e in evs]
+    steps_ms = [e[0].elapsed_time(e[-1]) for e in evs]
+    step_ms = evs[0][0].elapsed_time(evs[-1][-1]) / K
+
+    flops = 4.0 * w.B * w.H * n * w.S * w.D
+    core_avg = float(np.mean(core))
+    achieved = flops / (core_avg * 1e-3) / 1e12
+    rows_all = w.B * w.H * n
+    merge_bytes = rows_all * (2 * w.D * 2 + 8 + w.D * 2 + 4)
+    merge_avg = float(np.mean(merge)) / max(P - 1, 1)
+    rec = {
+        "metric": METRIC,
+        "value": flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "ms_per_step_median": float(np.median(steps_ms)),
+        "ms_per_step_min": float(np.min(steps_ms)),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} ring of {P}: one rank ({n} query rows x {P} key/value blocks of {n})",
+                   "B": w.B, "H": w.H, "S": w.S, "D": w.D, "ranks_in_ring": P, "non_causal": True},
+        "pct_of_peak": 100.0 * flops / (step_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "dit_attn_core_lse: attn_core_kernel + attn_merge_kernel",
+                     "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "avg_ms": core_avg / P},
+        "stages_ms": {"prepare_kv_all_blocks": float(np.mean(prep)), "attn_core_lse_all_blocks": core_avg,
+                      "merge_all": float(np.mean(merge))},
+        "merge": {"bound": "hbm", "avg_ms": merge_avg, "algorithmic_bytes": merge_bytes,
+                  "achieved_GBps": merge_bytes / (merge_avg * 1e-3) / 1e9 if P > 1 else None,
+                  "peak_GBps": HBM_PEAK_GBS},
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -144,6 +243,9 @@ def main():
         copy_calibration(args, torch)
         return
     w = W.get(args.workload)
+    if args.ring > 1:
+        ring_bench(args, w, torch, dj)
+        return
     fp8 = w.dtype == "fp8_e4m3"
     print(f"[bench] workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype}", file=sys.stderr, flush=True)
     pos = torch.from_numpy(W.positions(w)).to("cuda")
@@ -151,7 +253,6 @@ def main():
     scale = 1.0 / math.sqrt(w.D)
     stream = torch.cuda.current_stream()
     if fp8:
-        from oracle.fp8 import dequantize
         (q8, sq), (k8, sk), (v8, sv) = [W.fp8_e4m3_quantize(x) for x in W.draw_qkv_f32(w)]
         q, k, v = (torch.from_numpy(np.ascontiguousarray(c)).to("cuda") for c in (q8, k8, v8))
         out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
@@ -162,7 +263,9 @@ def main():
                                             stream=stream)
         forward = lambda: dj.dit_attn_forward_fp8(q, k, v, sq, sk, sv, cos, sin, out=out, S_txt=w.S_txt,
                                                   scale=scale)
-        f64_head = lambda h: tuple(dequantize(c[:, h:h + 1], s_) for c, s_ in ((q8, sq), (k8, sk), (v8, sv)))
+        def f64_head(h):  # the oracle's dequantisation, for the CPU baseline leg only
+            from oracle.fp8 import dequantize
+            return tuple(dequantize(c[:, h:h + 1], s_) for c, s_ in ((q8, sq), (k8, sk), (v8, sv)))
         peak = FP8_PEAK_TFLOPS
     else:
         qb, kb, vb = W.make_bf16_inputs(w)
@@ -209,14 +312,6 @@ def main():
     torch.cuda.synchronize()
     fwd_ms = e0.elapsed_time(e1) / K
 
-    # Spot parity of the timed output against the oracle (a few rows of head 0).
-    from oracle import joint_attention, rope_angles
-    rows = np.array([0, 1, w.S_txt - 1, w.S_txt, w.S // 2, w.S - 1])
-    ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
-    ref = joint_attention(*f64_head(0), ang, rows=rows)
-    got_bits = out[:, :1, torch.from_numpy(rows).to("cuda")].cpu().view(torch.int16).numpy().view(np.uint16)
-    spot_err = float(np.abs(W.bf16_bits_to_f32(got_bits) - ref).max())
-
     flops = w.flops
     src_hash = kernel_sources_hash()
     meas = MEASURED_TRAFFIC.get((src_hash, w.name))
@@ -256,11 +351,16 @@ def main():
                       "prepare_kv_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9},
         "forward_ms": fwd_ms,
         "wall_s": wall,
-        "spot_parity_max_abs": spot_err,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, f64_head, args.cpu_seconds)
+        out_host = out.cpu()
+
+        def gpu_rows(h, rows):
+            bits = out_host[:, h:h + 1, torch.from_numpy(rows)].view(torch.int16).numpy().view(np.uint16)
+            return W.bf16_bits_to_f32(bits).astype(np.float64)
+
+        rec["cpu_baseline"] = cpu_baseline(w, f64_head, args.cpu_seconds, gpu_rows)
     print(json.dumps(rec), flush=True)
 
 
