@@ -33,9 +33,9 @@ KERNEL_SOURCES = ["dit_joint_self_amd/csrc/attn_core.hip", "dit_joint_self_amd/c
                   "dit_joint_self_amd/csrc/attn_common.h", "dit_joint_self_amd/csrc/tile_layout.h",
                   "dit_joint_self_amd/csrc/bf16_util.h", "dit_joint_self_amd/csrc/fp8_util.h"]
 MEASURED_TRAFFIC = {
-    ("5b4cb76355ac9b4e", "flux2048"): {"read_bytes": 1083.7e6, "write_bytes": 135.8e6,
+    ("03489aa4bb220259", "flux2048"): {"read_bytes": 1102.4e6, "write_bytes": 210.1e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
-    ("5b4cb76355ac9b4e", "flux2048_fp8"): {"read_bytes": 694.4e6, "write_bytes": 136.1e6,
+    ("03489aa4bb220259", "flux2048_fp8"): {"read_bytes": 694.4e6, "write_bytes": 136.0e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
 }
 

@@ -117,6 +117,26 @@ def test_sampled_parity_full_size(name, n_random):
     _assert_close(got[:, :, rows], want, f"{name} ({len(rows)} rows x {w.H} heads)")
 
 
+def test_longest_supported_sequence():
+    """S = 2^21, the longest sequence the library accepts (one head): the last
+    tiles sit just below the 32-bit byte offsets of the tile addressing.
+    Sampled rows, including the last tile's."""
+    torch = _torch()
+    dj = _dj()
+    w = W.Workload("max", B=1, H=1, D=128, S_txt=0, grid=(1, 1024, 2048), axes_dim=(16, 56, 56), theta=10000.0,
+                   seed=2021)
+    assert w.S == 2 ** 21
+    qb, kb, vb = W.make_bf16_inputs(w)
+    q, k, v = to_device_bf16(qb), to_device_bf16(kb), to_device_bf16(vb)
+    cos, sin = _tables(w)
+    out = dj.dit_attn_forward(q, k, v, cos, sin)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(w.S, 0, 24, seed=3), [2 ** 20, w.S - 64, w.S - 2, w.S - 1]]))
+    got = from_device_bf16(out[:, :, torch.from_numpy(rows).to("cuda")])
+    del q, k, v, out
+    _assert_close(got, _oracle(w, qb, kb, vb, rows=rows), f"S=2^21 ({len(rows)} rows)")
+
+
 # ---------------------------------------------------------------- edge cases
 
 def _small(S_txt, grid, B=1, H=3, axes=(64, 64), seed=7):
