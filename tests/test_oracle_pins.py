@@ -361,3 +361,81 @@ def test_lse_identical_keys_closed_form():
     s = (q[0, 0] @ krow[0, 0, 0]) / math.sqrt(8)
     assert np.max(np.abs(L[0, 0] - (s + math.log(11)))) <= 1e-13
     assert np.max(np.abs(o[0, 0] - v[0, 0].mean(axis=0))) <= 1e-13
+
+
+# ---------------------------------------------------------------- MXFP4 (OCP MX) quantisation and linear
+
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # codes 0..7 from sign/exponent/mantissa by hand
+
+
+def test_e2m1_and_e8m0_decode_tables():
+    from oracle.mx import e2m1_decode, e8m0_decode
+    got = e2m1_decode(np.arange(16))
+    assert got[:8].tolist() == E2M1_TABLE
+    assert (-got[8:]).tolist() == E2M1_TABLE and np.signbit(got[8])
+    e = e8m0_decode(np.array([0, 1, 126, 127, 128, 254, 255]))
+    assert e[:6].tolist() == [2.0 ** -127, 2.0 ** -126, 0.5, 1.0, 2.0, 2.0 ** 127] and np.isnan(e[6])
+
+
+def test_mxfp4_quantize_closed_forms():
+    from oracle.mx import mxfp4_quantize, mxfp4_dequantize
+    blk = lambda vals: np.array(vals + [0.0] * (32 - len(vals)))
+    # block max 6 * 2^k: scale 2^k, the max maps to code 7, exactly representable values survive
+    x = blk([6.0 * 8, 0.5 * 8, -3.0 * 8, 1.5 * 8])
+    c, s = mxfp4_quantize(x)
+    assert s.tolist() == [127 + 3] and c[:4].tolist() == [7, 1, 8 + 5, 3]
+    assert np.array_equal(mxfp4_dequantize(c, s), x)
+    # max 7: floor(log2 7) - 2 = 0, 7 saturates to 6
+    c, s = mxfp4_quantize(blk([7.0, 1.0]))
+    assert s.tolist() == [127] and c[:2].tolist() == [7, 2]
+    # ties go to the even code: 0.25->0, 0.75->1, 1.25->1, 1.75->2, 2.5->2, 3.5->4, -0.25->-0 (scale 2^0: max 4)
+    c, s = mxfp4_quantize(blk([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 4.0, -0.25]))
+    assert s.tolist() == [127] and c[:9].tolist() == [6, 0, 2, 2, 4, 4, 6, 6, 8]
+    c, s = mxfp4_quantize(blk([6.0, 5.0]))                  # 5 is halfway between 4 and 6
+    assert c[:2].tolist() == [7, 6]
+    # zero block: smallest scale, zero codes; tiny block: scale clamped to 2^-127
+    c, s = mxfp4_quantize(np.zeros(32))
+    assert s.tolist() == [0] and not c.any()
+    c, s = mxfp4_quantize(blk([2.0 ** -130]))
+    assert s.tolist() == [0] and c[0] == 0
+
+
+def test_mxfp4_quantize_picks_the_nearest_code_by_search():
+    """Property pin: the scale obeys 2^X <= max|V| / 4 < 2^(X+1), and every code
+    is the one of all 16 whose value times 2^X is nearest (ties: even code)."""
+    from oracle.mx import mxfp4_quantize
+    rng = np.random.default_rng(44)
+    x = rng.standard_normal((6, 128)) * np.exp2(rng.integers(-8, 8, size=(6, 1)))
+    c, s = mxfp4_quantize(x)
+    table = np.array(E2M1_TABLE + [-v for v in E2M1_TABLE])
+    for r in range(6):
+        for b in range(4):
+            blk = x[r, 32 * b:32 * b + 32]
+            sc = 2.0 ** (int(s[r, b]) - 127)
+            assert sc <= np.abs(blk).max() / 4 < 2 * sc
+            for i, v in enumerate(blk):
+                y = min(abs(v) / sc, 6.0) * (1 if v >= 0 else -1)
+                d = np.abs(table - y)
+                ok = np.flatnonzero(d == d.min())
+                want = ok[0] if len(ok) == 1 or ok[0] % 2 == 0 else ok[1]
+                if abs(table[want]) == 0.0:
+                    want = 8 if v < 0 else 0
+                assert c[r, 32 * b + i] == want, (r, b, i, v)
+
+
+def test_mx_linear_exact_on_representable_values():
+    """Codes and scales chosen so every product is a dyadic rational: the oracle
+    must equal the exact sum computed with Python fractions."""
+    from fractions import Fraction
+    from oracle.mx import mx_linear
+    rng = np.random.default_rng(45)
+    M, N, K = 3, 4, 64
+    ac, wc = rng.integers(0, 16, size=(M, K)), rng.integers(0, 16, size=(N, K))
+    asc, wsc = rng.integers(120, 134, size=(M, K // 32)), rng.integers(120, 134, size=(N, K // 32))
+    val = lambda code: (Fraction(E2M1_TABLE[code & 7]) * (-1 if code & 8 else 1))
+    got = mx_linear(ac, asc, wc, wsc)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(val(int(ac[m, k])) * Fraction(2) ** (int(asc[m, k // 32]) - 127) *
+                        val(int(wc[n, k])) * Fraction(2) ** (int(wsc[n, k // 32]) - 127) for k in range(K))
+            assert got[m, n] == float(exact)
