@@ -64,8 +64,9 @@ def _oracle(w, qb, kb, vb, rope=True, scale=None, rows=None):
 
 def _assert_close(got, want, tag, short=False):
     """Gates above.  ``short`` sequences (S <= 256) average few V rows, so |O|
-    is O(1) and the bf16 output rounding alone (up to 2^-9 |O|) plus the bf16
-    rounding of P (relative 2^-9 per weight) can exceed 1e-3 on the mean: for
+    is O(1) and the bf16 output rounding alone (up to 2^-8 |O|: bf16 carries
+    8 significant bits) plus the bf16 rounding of P (relative 2^-8 per weight)
+    can exceed 1e-3 on the mean: for
     them the gates are max(1e-2, 2^-7 max|O|) and max(1e-3, 2^-8 mean|O|)."""
     e = err_stats(got, want)
     print(f"[parity] {tag}: {e}", flush=True)
@@ -185,8 +186,10 @@ def test_sharp_softmax_and_rising_max():
     No RoPE, and scale = 0.25 / log2(e): the kernel's scaled Q'' = Q / 4 and
     K' = K are then exact in bf16, the scores are exact up to fp32 summation,
     and the only differences from the oracle are the bf16 rounding of P
-    (relative 2^-9 per weight) and of the output (2^-9 |O|), so the gates
-    below are 2^-7 max|V| and 2^-9 mean|V| + 2^-9 mean|O|."""
+    (relative 2^-8 per weight, bf16's unit roundoff: it moves the normalised
+    weights by at most 2 x 2^-8 of their sum, so O by 2^-7 max|V|) and of the
+    output (2^-8 |O| <= 2^-8 max|V|), so the gates below are 3 x 2^-8 max|V|
+    and, on the mean, 2^-8 (mean|V| + mean|O|)."""
     w = _small(40, (20, 25), H=2, seed=99)
     q, k, v = W.draw_qkv_f32(w)
     growth = np.linspace(0.5, 3.0, w.S, dtype=np.float32)[None, None, :, None]
@@ -198,19 +201,20 @@ def test_sharp_softmax_and_rising_max():
     print(f"[parity] sharp: {e}", flush=True)
     vabs = np.abs(bf16_f64(vb))
     assert np.all(np.isfinite(got))
-    assert e["max_abs"] <= 2.0 ** -7 * vabs.max(), e
-    assert e["mean_abs"] <= 2.0 ** -9 * (vabs.mean() + np.abs(want).mean()), e
+    assert e["max_abs"] <= 3 * 2.0 ** -8 * vabs.max(), e
+    assert e["mean_abs"] <= 2.0 ** -8 * (vabs.mean() + np.abs(want).mean()), e
 
 
 def test_sharp_softmax_with_rope():
     """Sharper logits (Q x 4) through the whole RoPE path.
 
     Here the bf16 rounding of the rotated K' and of the scaled Q'' (relative
-    2^-9 each) moves logit (i, j) by at most d_ij = 2^-8 * scale * sum_d
-    |q'_id| |k'_jd| (natural-log units), so row i of the output can move by at
-    most (exp(2 D_i) - 1) max|v| with D_i = max_j d_ij, plus the P rounding
-    (2^-8 max|v|) and the output rounding (2^-9 |O_i|).  The unit-variance
-    gates do not apply at these logit sizes; this per-row bound does."""
+    2^-8 each, bf16's unit roundoff) moves logit (i, j) by at most
+    d_ij = 2^-7 * scale * sum_d |q'_id| |k'_jd| (natural-log units), so row i
+    of the output can move by at most (exp(2 D_i) - 1) max|v| with
+    D_i = max_j d_ij, plus the P rounding (2^-7 max|v|) and the output
+    rounding (2^-8 |O_i|).  The unit-variance gates do not apply at these
+    logit sizes; this per-row bound does."""
     from oracle import rope_apply
     w = _small(40, (20, 25), H=2, seed=98)
     q, k, v = W.draw_qkv_f32(w)
@@ -220,9 +224,9 @@ def test_sharp_softmax_with_rope():
     ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
     qr, kr = np.abs(rope_apply(bf16_f64(qb), ang)), np.abs(rope_apply(bf16_f64(kb), ang))
     scale = 1.0 / math.sqrt(w.D)
-    D = 2.0 ** -8 * scale * np.einsum("bhid,bhjd->bhij", qr, kr).max(axis=3)
+    D = 2.0 ** -7 * scale * np.einsum("bhid,bhjd->bhij", qr, kr).max(axis=3)
     vmax = np.abs(bf16_f64(vb)).max()
-    bound = (np.expm1(2 * D) + 2.0 ** -8) * vmax + 2.0 ** -9 * np.abs(want).max(axis=3)
+    bound = (np.expm1(2 * D) + 2.0 ** -7) * vmax + 2.0 ** -8 * np.abs(want).max(axis=3)
     err = np.abs(got - want).max(axis=3)
     print(f"[parity] sharp+rope: max err {err.max():.3g}, min slack {(bound - err).min():.3g}", flush=True)
     assert np.all(np.isfinite(got)) and np.all(err <= bound)

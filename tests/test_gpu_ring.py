@@ -4,14 +4,17 @@ against the float64 oracle (oracle.ring), through the C ABI.
 Gates.
 * O after a ring of key blocks: the bf16 attention gates (max 1e-2, mean 1e-3,
   relative mean 1%), since each block's O carries the attention kernel's error
-  and the merge adds one bf16 rounding (relative 2^-9) of values of size |O|.
+  and the merge adds one bf16 rounding (relative 2^-8, bf16's unit roundoff)
+  of values of size |O|.
 * Row log-sum-exp L: a score on the GPU is scale * sum_d q'_d k'_d with q'
-  (times scale * log2 e) and k' each rounded to bf16 (relative error <= 2^-9),
-  so |dL| <= 2^-8 * scale * sum_d |q'_d k'_d| to first order; for unit-variance
-  rows with D = 128 that sum is about 0.64 * 128 * scale = 7.2, so
-  |dL| <= 0.03 in the worst case; rounding errors of random sign make it ~10x
-  smaller on average. The weight sum l adds at most 2^-9 (relative) = 0.002.
-  Gates: max |dL| <= 3e-2, mean |dL| <= 3e-3.
+  (times scale * log2 e) and k' each rounded to bf16 (relative error <= 2^-8),
+  so a logit moves by at most 2^-7 * scale * sum_d |q'_d k'_d|; for
+  unit-variance rows with D = 128 that sum is about 0.64 * 128 * scale = 7.2,
+  i.e. 0.056. L moves by the softmax-weighted average of its row's logit
+  errors, and the weight sum l (bf16 weights) by at most 2^-8 = 0.004
+  relative: max |dL| <= 0.06. Rounding errors of random sign average down
+  over the dims and the keys; the mean gate 3e-3 is ten times the means
+  observed. Gates: max |dL| <= 6e-2, mean |dL| <= 3e-3.
 * The merge alone, on the GPU's own partial results: fp32 arithmetic and one
   bf16 RNE rounding, so |out - exact| <= 2^-8 |exact| + 1e-6 element-wise and
   |L_out - exact| <= 1e-5 (1 + |exact|).
@@ -28,7 +31,7 @@ from tests.gpu_inputs import bf16_f64, err_stats, from_device_bf16, sample_rows,
 pytestmark = pytest.mark.gpu
 
 MAX_ABS, MEAN_ABS, REL_MEAN = 1e-2, 1e-3, 1e-2
-LSE_MAX, LSE_MEAN = 3e-2, 3e-3
+LSE_MAX, LSE_MEAN = 6e-2, 3e-3
 
 
 def _torch():
