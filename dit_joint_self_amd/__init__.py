@@ -18,7 +18,8 @@ __all__ = [
     "LIB_PATH", "DitAttnError", "lib", "lib_loaded", "dit_last_error", "dit_abi_version",
     "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_kv",
     "dit_attn_core", "dit_attn_workspace_bytes_fp8", "dit_attn_prepare_kv_fp8", "dit_attn_core_fp8",
-    "dit_attn_forward_fp8", "dit_attn_core_lse", "dit_attn_merge_lse", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
+    "dit_attn_forward_fp8", "dit_attn_core_lse", "dit_attn_merge_lse", "dit_mxfp4_quantize", "dit_mxfp4_gemm",
+    "dit_mxfp4_linear", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
     "DIT_ERR_NO_DEVICE", "DIT_ERR_OUT_OF_MEMORY", "DIT_ERR_LAUNCH", "DIT_DTYPE_BF16",
     "DIT_DTYPE_FP8_E4M3",
 ]
@@ -57,6 +58,9 @@ _SIGNATURES = {
     "dit_attn_forward_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "dit_attn_core_lse": (_I, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P, _I, _I, _I, _I, _F, _P]),
     "dit_attn_merge_lse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "dit_mxfp4_quantize": (_I, [_P, _P, _P, _I, _I, _P]),
+    "dit_mxfp4_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "dit_mxfp4_linear": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -210,6 +214,42 @@ def dit_attn_merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=No
     _check(lib().dit_attn_merge_lse(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse_out),
                                     B, H, S, D, _stream(stream)))
     return out, lse_out
+
+
+# ---------------------------------------------------------------- MXFP4 linear layers
+
+def dit_mxfp4_quantize(x, codes=None, scales=None, stream=None):
+    """bf16 [rows, K] -> (codes uint8 [rows, K/2], scales uint8 [rows, K/32]) on the device."""
+    import torch
+    rows, K = (int(s) for s in x.shape)
+    if codes is None:
+        codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().dit_mxfp4_quantize(_ptr(x), _ptr(codes), _ptr(scales), rows, K, _stream(stream)))
+    return codes, scales
+
+
+def dit_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out=None, stream=None):
+    """out [M, N] bf16 = deq(A) deq(W)^T from MXFP4 codes/scales ([M, K/2], [M, K/32], [N, K/2], [N, K/32])."""
+    import torch
+    M, N, K = int(a_codes.shape[0]), int(w_codes.shape[0]), 2 * int(a_codes.shape[1])
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
+    _check(lib().dit_mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), _ptr(out), M, N, K,
+                                _stream(stream)))
+    return out
+
+
+def dit_mxfp4_linear(x, w_codes, w_scales, out=None, stream=None):
+    """x bf16 [M, K] times the MXFP4 weight [N, K]^T: dynamic per-1x32 quantisation + A4W4 GEMM."""
+    import torch
+    M, K = (int(s) for s in x.shape)
+    N = int(w_codes.shape[0])
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib().dit_mxfp4_linear(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(out), M, N, K, _stream(stream)))
+    return out
 
 
 # ---------------------------------------------------------------- fp8 (e4m3 codes + per-tensor scales)

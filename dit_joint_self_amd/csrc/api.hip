@@ -24,6 +24,9 @@ hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, c
                              void* ws, int BH, int S, hipStream_t stream);
 hipError_t launch_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* out,
                             float* lse_out, int64_t rows, hipStream_t stream);
+hipError_t launch_mxfp4_quantize(const void* x, void* codes, void* scales, int64_t rows, int K, hipStream_t stream);
+hipError_t launch_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+                             void* out, int M, int N, int K, hipStream_t stream);
 hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
                             void* out, float* lse, int BH, int S, float qmul, hipStream_t stream);
 size_t core_partial_bytes(int BH, int S);
@@ -415,3 +418,83 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- MXFP4 linear layers
+
+static dit_status_t check_mx_rows(int rows, int K, const char* what) {
+    if (rows < 1 || K < 1) return fail(DIT_ERR_INVALID_ARG, "%s: rows and K must be >= 1 (got %d, %d)", what, rows, K);
+    if ((int64_t)rows * K / 2 > INT_MAX)
+        return fail(DIT_ERR_UNSUPPORTED, "%s: rows * K / 2 must be below 2^31 (got %d x %d)", what, rows, K);
+    return DIT_OK;
+}
+
+static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+dit_status_t dit_mxfp4_quantize(const void* x, void* codes, void* scales, int rows, int K, void* stream) {
+    if (!x || !codes || !scales) return fail(DIT_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+    dit_status_t st = check_mx_rows(rows, K, "dit_mxfp4_quantize");
+    if (st != DIT_OK) return st;
+    if (K % 32) return fail(DIT_ERR_INVALID_ARG, "K must be a multiple of 32 (got %d)", K);
+    if (!aligned16(x) || !aligned(codes, 4)) return fail(DIT_ERR_INVALID_ARG, "x must be 16-byte and codes 4-byte aligned");
+    const size_t xb = (size_t)rows * K * 2, cb = (size_t)rows * K / 2, sb = (size_t)rows * K / 32;
+    if (overlaps(codes, cb, x, xb) || overlaps(scales, sb, x, xb) || overlaps(codes, cb, scales, sb))
+        return fail(DIT_ERR_INVALID_ARG, "x, codes and scales must not overlap");
+    if ((st = check_device()) != DIT_OK) return st;
+    return launched(dit::launch_mxfp4_quantize(x, codes, scales, rows, K, static_cast<hipStream_t>(stream)),
+                    "mxfp4_quantize_kernel");
+}
+
+static dit_status_t check_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+                               const void* out, int M, int N, int K) {
+    dit_status_t st;
+    if ((st = check_mx_rows(M, K, "A")) != DIT_OK || (st = check_mx_rows(N, K, "W")) != DIT_OK) return st;
+    if (K % 128) return fail(DIT_ERR_INVALID_ARG, "K must be a multiple of 128 (got %d)", K);
+    if (N % 4) return fail(DIT_ERR_INVALID_ARG, "N must be a multiple of 4 (got %d)", N);
+    if ((a_codes && !aligned16(a_codes)) || (w_codes && !aligned16(w_codes)))
+        return fail(DIT_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+    if ((a_scales && !aligned(a_scales, 4)) || !aligned(w_scales, 4))
+        return fail(DIT_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+    if (!aligned(out, 8)) return fail(DIT_ERR_INVALID_ARG, "out must be 8-byte aligned");
+    const size_t ob = (size_t)M * N * 2;
+    if ((a_codes && overlaps(out, ob, a_codes, (size_t)M * K / 2)) ||
+        (a_scales && overlaps(out, ob, a_scales, (size_t)M * K / 32)) || overlaps(out, ob, w_codes, (size_t)N * K / 2) ||
+        overlaps(out, ob, w_scales, (size_t)N * K / 32))
+        return fail(DIT_ERR_INVALID_ARG, "out overlaps an input");
+    return DIT_OK;
+}
+
+dit_status_t dit_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+                            void* out, int M, int N, int K, void* stream) {
+    if (!a_codes || !a_scales || !w_codes || !w_scales || !out)
+        return fail(DIT_ERR_INVALID_ARG, "codes, scales and out must be non-NULL");
+    dit_status_t st = check_gemm(a_codes, a_scales, w_codes, w_scales, out, M, N, K);
+    if (st != DIT_OK) return st;
+    if ((st = check_device()) != DIT_OK) return st;
+    return launched(dit::launch_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out, M, N, K,
+                                           static_cast<hipStream_t>(stream)),
+                    "mxfp4_gemm_kernel");
+}
+
+dit_status_t dit_mxfp4_linear(const void* x, const void* w_codes, const void* w_scales, void* out, int M, int N,
+                              int K, void* stream) {
+    if (!x || !w_codes || !w_scales || !out) return fail(DIT_ERR_INVALID_ARG, "x, w_codes, w_scales and out must be non-NULL");
+    dit_status_t st = check_gemm(nullptr, nullptr, w_codes, w_scales, out, M, N, K);
+    if (st != DIT_OK) return st;
+    if (!aligned16(x)) return fail(DIT_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    if (overlaps(out, (size_t)M * N * 2, x, (size_t)M * K * 2)) return fail(DIT_ERR_INVALID_ARG, "out overlaps x");
+    if ((st = check_device()) != DIT_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t cb = ((size_t)M * K / 2 + 255) & ~(size_t)255, sb = (size_t)M * K / 32;
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, cb + sb, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(DIT_ERR_OUT_OF_MEMORY, "could not allocate %zu bytes for the quantised activations", cb + sb);
+    }
+    void* codes = ws;
+    void* scales = static_cast<char*>(ws) + cb;
+    hipError_t e = dit::launch_mxfp4_quantize(x, codes, scales, M, K, s);
+    if (e == hipSuccess) e = dit::launch_mxfp4_gemm(codes, scales, w_codes, w_scales, out, M, N, K, s);
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = ef;
+    return launched(e, "mxfp4 linear");
+}

@@ -14,6 +14,13 @@ Q, K and V are drawn as N(0, 1) float32 from ``numpy.random.default_rng(seed)``
 in the order Q, K, V, each with shape [B, H, S, D], then rounded to bfloat16
 with round-to-nearest-even. The fp8 workload quantises those same draws per
 tensor to OCP E4M3 (one fp32 scale per tensor, amax / 448).
+
+The linear-layer workloads (MXFP4 GEMMs on either side of attention) are the
+FLUX.1-dev transformer's projections at a token count M: hidden size 3072
+(24 heads x 128), MLP width 12288 (the MXFP4/Quark on MI350 blog quantises
+these linear layers). The activation x [M, K] is drawn N(0, 1) and the weight
+w [N, K] (one row per output feature) N(0, 1/K), float32 from
+``default_rng(seed)`` in the order x, w, then rounded to bfloat16.
 """
 from __future__ import annotations
 
@@ -24,7 +31,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "positions", "draw_qkv_f32", "bf16_round_bits",
-    "bf16_bits_to_f32", "make_bf16_inputs", "fp8_e4m3_quantize", "E4M3_MAX",
+    "bf16_bits_to_f32", "make_bf16_inputs", "fp8_e4m3_quantize", "E4M3_MAX", "LinearWorkload",
+    "LINEAR_WORKLOADS", "make_linear_inputs",
 ]
 
 E4M3_MAX = 448.0
@@ -154,3 +162,43 @@ def fp8_e4m3_quantize(x: np.ndarray):
     y = torch.clamp(y, -E4M3_MAX, E4M3_MAX)
     codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     return codes, scale
+
+
+@dataclass(frozen=True)
+class LinearWorkload:
+    name: str
+    M: int      # tokens (rows of x and of the output)
+    N: int      # output features (rows of w)
+    K: int      # input features (the reduction axis; MX blocks run along it)
+    seed: int
+    note: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+
+LINEAR_WORKLOADS: Dict[str, LinearWorkload] = {
+    w.name: w for w in [
+        LinearWorkload("flux2048_qkv", M=16896, N=9216, K=3072, seed=2001,
+                       note="fused Q, K, V projection of the 16896-token 2048x2048 sequence"),
+        LinearWorkload("flux2048_out", M=16896, N=3072, K=3072, seed=2002,
+                       note="attention output projection, 16896 tokens"),
+        LinearWorkload("flux2048_mlp_up", M=16896, N=12288, K=3072, seed=2003,
+                       note="MLP up projection, 16896 tokens"),
+        LinearWorkload("flux2048_mlp_down", M=16896, N=3072, K=12288, seed=2004,
+                       note="MLP down projection, 16896 tokens"),
+        LinearWorkload("flux1024x768_qkv", M=3584, N=9216, K=3072, seed=2005,
+                       note="fused Q, K, V projection of the 3584-token 1024x768 sequence"),
+        LinearWorkload("small_ragged", M=200, N=100, K=384, seed=2006,
+                       note="test shape: partial tiles in M and N, an odd number of K steps"),
+    ]
+}
+
+
+def make_linear_inputs(w: LinearWorkload):
+    """(x_bits [M, K], w_bits [N, K]) as bfloat16 bit patterns (uint16)."""
+    rng = np.random.default_rng(w.seed)
+    x = rng.standard_normal((w.M, w.K), dtype=np.float32)
+    wt = rng.standard_normal((w.N, w.K), dtype=np.float32) * np.float32(1.0 / np.sqrt(w.K))
+    return bf16_round_bits(x), bf16_round_bits(wt)

@@ -204,6 +204,43 @@ dit_status_t dit_attn_forward_fp8(const void* q8, const void* k8, const void* v8
                                   const float* rope_cos, const float* rope_sin, void* out,
                                   int B, int H, int S_txt, int S_img, int D, float scale, void* stream);
 
+/*
+ * MXFP4 linear layers around attention.  The MXFP4/Quark on MI350 blog runs
+ * FLUX's linear layers (the projections on either side of attention and the
+ * MLPs) in MXFP4 as the OCP Microscaling specification defines it: blocks of
+ * 32 FP4 (E2M1) elements along the reduction axis K share one E8M0 scale;
+ * weights are quantised once, activations per call, and the product is an
+ * A4W4 matrix-core GEMM ("MXFP4 Quantization" and "MXFP4 Kernel" sections).
+ *
+ * Layouts (device memory, row-major):
+ *   codes  [rows, K/2] bytes: element k in byte k/2, low nibble for even k.
+ *   scales [rows, K/32] bytes: E8M0 (2^(s - 127)) of each 32-element block.
+ *
+ * dit_mxfp4_quantize  x: bf16 [rows, K], 16-byte aligned, K a multiple of 32,
+ *   finite values.  Per block: X = floor(log2 max|x|) - 2 clamped to
+ *   [-127, 127] (-127 for an all-zero block), codes = x * 2^-X rounded to the
+ *   nearest E2M1 value (ties to the even code, magnitudes above 6 saturate,
+ *   the sign bit is kept); scales = X + 127.  Used for the activations at run
+ *   time and, once, for the weights.  codes 4-byte aligned; no overlaps.
+ *
+ * dit_mxfp4_gemm  out[M, N] (bf16 RNE) = deq(A)[M, K] deq(W)[N, K]^T with fp32
+ *   accumulation: a_codes/a_scales the quantised activations [M, K], w_codes/
+ *   w_scales the quantised weight [N, K] (the nn.Linear layout: one row per
+ *   output feature).  K a multiple of 128, N a multiple of 4; rows * K / 2
+ *   below 2^31 for both operands; codes 16-byte, scales 4-byte and out
+ *   8-byte aligned; out must not overlap an input.
+ *
+ * dit_mxfp4_linear  quantise x (bf16 [M, K]) into a stream-ordered workspace
+ *   (hipMallocAsync / hipFreeAsync on stream), then dit_mxfp4_gemm.
+ */
+dit_status_t dit_mxfp4_quantize(const void* x, void* codes, void* scales, int rows, int K, void* stream);
+
+dit_status_t dit_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+                            void* out, int M, int N, int K, void* stream);
+
+dit_status_t dit_mxfp4_linear(const void* x, const void* w_codes, const void* w_scales, void* out,
+                              int M, int N, int K, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -207,3 +207,35 @@ def test_lse_entry_points_reject_bad_arguments():
         assert merge(o=oa, lo=la) == dj.DIT_ERR_NO_DEVICE
         assert merge(o=ob, lo=lb_) == dj.DIT_ERR_NO_DEVICE
         assert core() == dj.DIT_ERR_NO_DEVICE
+
+
+def test_mxfp4_entry_points_reject_bad_arguments():
+    L = dj.lib()
+    x, c, s, o = 0x30000000, 0x40000000, 0x50000000, 0x60000000
+    q = L.dit_mxfp4_quantize
+    assert q(None, c, s, 4, 64, None) == dj.DIT_ERR_INVALID_ARG
+    assert q(x, c, s, 0, 64, None) == dj.DIT_ERR_INVALID_ARG
+    assert q(x, c, s, 4, 48, None) == dj.DIT_ERR_INVALID_ARG              # K not a multiple of 32
+    assert q(x + 8, c, s, 4, 64, None) == dj.DIT_ERR_INVALID_ARG          # x misaligned
+    assert q(x, x + 64, s, 4, 64, None) == dj.DIT_ERR_INVALID_ARG         # codes inside x
+    assert q(x, c, c + 8, 4, 64, None) == dj.DIT_ERR_INVALID_ARG          # scales inside codes
+    assert q(x, c, s, 2 ** 20, 2 ** 12, None) == dj.DIT_ERR_UNSUPPORTED   # rows * K / 2 >= 2^31
+    g = lambda **kw: L.dit_mxfp4_gemm(kw.get("ac", c), kw.get("as_", s), kw.get("wc", c + 2 ** 24),
+                                      kw.get("ws", s + 2 ** 24), kw.get("o", o), kw.get("M", 8),
+                                      kw.get("N", 16), kw.get("K", 256), None)
+    assert g(ac=None) == dj.DIT_ERR_INVALID_ARG
+    assert g(K=192) == dj.DIT_ERR_INVALID_ARG                             # K not a multiple of 128
+    assert g(N=18) == dj.DIT_ERR_INVALID_ARG                              # N not a multiple of 4
+    assert g(ac=c + 8) == dj.DIT_ERR_INVALID_ARG                          # codes misaligned
+    assert g(ws=s + 2 ** 24 + 2) == dj.DIT_ERR_INVALID_ARG                # scales misaligned
+    assert g(o=o + 4) == dj.DIT_ERR_INVALID_ARG                           # out misaligned
+    assert g(o=c) == dj.DIT_ERR_INVALID_ARG                               # out over the A codes
+    assert g(M=2 ** 20, K=2 ** 12) == dj.DIT_ERR_UNSUPPORTED
+    lin = L.dit_mxfp4_linear
+    assert lin(None, c, s, o, 8, 16, 256, None) == dj.DIT_ERR_INVALID_ARG
+    assert lin(x, c, s, x, 8, 16, 256, None) == dj.DIT_ERR_INVALID_ARG    # out over x
+    assert lin(x, c, s, o, 8, 16, 100, None) == dj.DIT_ERR_INVALID_ARG
+    if _no_device():
+        assert q(x, c, s, 4, 64, None) == dj.DIT_ERR_NO_DEVICE
+        assert g() == dj.DIT_ERR_NO_DEVICE
+        assert lin(x, c, s, o, 8, 16, 256, None) == dj.DIT_ERR_NO_DEVICE
