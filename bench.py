@@ -50,6 +50,7 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 FP8_PEAK_TFLOPS = 5033.2    # 256 CU x 8192 flop/clk x 2.4 GHz, dense
+FP4_PEAK_TFLOPS = 10066.3   # 256 CU x 16384 flop/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 
 
@@ -58,7 +59,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="flux2048", choices=list(W.WORKLOADS))
+    ap.add_argument("--workload", default="flux2048", choices=list(W.WORKLOADS) + list(W.LINEAR_WORKLOADS),
+                    help="an attention workload, or an MXFP4 linear-layer shape (quantise + A4W4 GEMM)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ring", type=int, default=1,
@@ -227,6 +229,100 @@ def ring_bench(args, w, torch, dj):
     print(json.dumps(rec), flush=True)
 
 
+def gemm_bench(args, lw, torch, dj):
+    """MXFP4 linear layer: one step = dit_mxfp4_linear on bf16 activations
+    [M, K] with a weight [N, K] quantised beforehand (the activation quantiser
+    and the A4W4 GEMM, the two kernels of the layer); the GEMM is also timed
+    alone for the roofline."""
+    xb, wb = W.make_linear_inputs(lw)
+    x, w = bf16_dev(xb, torch), bf16_dev(wb, torch)
+    stream = torch.cuda.current_stream()
+    wc, ws = dj.dit_mxfp4_quantize(w, stream=stream)
+    ac, as_ = dj.dit_mxfp4_quantize(x, stream=stream)
+    out = torch.empty((lw.M, lw.N), dtype=torch.bfloat16, device="cuda")
+    step = lambda: dj.dit_mxfp4_linear(x, wc, ws, out=out, stream=stream)
+    gemm = lambda: dj.dit_mxfp4_gemm(ac, as_, wc, ws, out=out, stream=stream)
+    quant = lambda: dj.dit_mxfp4_quantize(x, ac, as_, stream=stream)
+
+    def timed(fn, K):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+    for _ in range(args.warmup):
+        step(); gemm(); quant()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / K
+    gemm_ms = timed(gemm, K)
+    quant_ms = timed(quant, K)
+    g_avg, q_avg = float(np.mean(gemm_ms)), float(np.mean(quant_ms))
+    flops = lw.flops
+    gemm_bytes = lw.M * lw.K // 2 + lw.M * lw.K // 32 + lw.N * lw.K // 2 + lw.N * lw.K // 32 + 2 * lw.M * lw.N
+    quant_bytes = 2 * lw.M * lw.K + lw.M * lw.K // 2 + lw.M * lw.K // 32
+    rec = {
+        "metric": "MXFP4 linear-layer TFLOP/s (dynamic 1x32 activation quantisation + A4W4 GEMM), 1 GPU",
+        "value": flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 (e2m1 + e8m0 per 32), bf16 in/out",
+        "data": "synthetic",
+        "config": {"workload": lw.name, "M": lw.M, "N": lw.N, "K": lw.K, "note": lw.note},
+        "pct_of_peak": 100.0 * flops / (step_ms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "mxfp4_gemm_kernel", "achieved": flops / (g_avg * 1e-3) / 1e12,
+                     "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (g_avg * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_bytes": gemm_bytes, "avg_ms": g_avg},
+        "stages_ms": {"mxfp4_quantize": q_avg, "mxfp4_gemm": g_avg,
+                      "quantize_GBps": quant_bytes / (q_avg * 1e-3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        from oracle.mx import mx_linear, mxfp4_quantize
+        w_c, w_s = mxfp4_quantize(W.bf16_bits_to_f32(wb).astype(np.float64))
+        xf = W.bf16_bits_to_f32(xb).astype(np.float64)
+        rows = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds and rows < lw.M:
+            a_c, a_s = mxfp4_quantize(xf[rows:rows + 64])
+            ref = mx_linear(a_c, a_s, w_c, w_s)
+            if rows == 0:
+                tc = time.perf_counter()
+                got = out[:64].float().cpu().numpy().astype(np.float64)
+                parity = float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+                t0 += time.perf_counter() - tc
+            rows += 64
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        except Exception:  # pragma: no cover
+            threads = 1
+        rec["cpu_baseline"] = {"value": 2.0 * rows * lw.N * lw.K / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": int(threads), "kind": "oracle",
+                               "sample": f"{lw.name}: quantise + float64 product of the first {rows} of {lw.M} rows "
+                                         f"(weight quantised beforehand), {dt:.1f} s",
+                               "host_cpus": len(os.sched_getaffinity(0)),
+                               "sample_parity_max_rel": parity}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -241,6 +337,9 @@ def main():
         sys.exit(2)
     if args.copy_mib:
         copy_calibration(args, torch)
+        return
+    if args.workload in W.LINEAR_WORKLOADS:
+        gemm_bench(args, W.LINEAR_WORKLOADS[args.workload], torch, dj)
         return
     w = W.get(args.workload)
     if args.ring > 1:

@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_common.h"
 #include "bf16_util.h"
@@ -87,22 +88,31 @@ hipError_t launch_mxfp4_quantize(const void* x, void* codes, void* scales, int64
 
 // ---------------------------------------------------------------- GEMM
 
-constexpr int GM = 128;  // rows of A (output rows) per workgroup
-constexpr int GN = 256;  // rows of W (output columns) per workgroup
-constexpr int GK = 128;  // K per pipeline step (two 64-deep MFMA steps, four MX blocks)
+constexpr int GM = 256;      // rows of A (output rows) per workgroup
+constexpr int GN = 256;      // rows of W (output columns) per workgroup
+constexpr int GK = 256;      // K per pipeline step: four 64-deep MFMA steps, 128 bytes of each row
+constexpr int GWAVES = 8;    // wave (wm, wn) = (w & 3, w >> 2): 64 rows x 128 columns each
+constexpr int G_GROUP = 8;   // column tiles per group of the workgroup order
+constexpr int G_CODE_PIECES = (GM + GN) * (GK / 2) / 1024 / GWAVES;   // 1 KiB code pieces per wave and step (8)
+constexpr int G_SCALE_PIECES = (GM + GN) * (GK / 128) / 64 / GWAVES;  // 64-word scale pieces per wave and step (2)
+static_assert(G_SCALE_PIECES * GWAVES == 16 && G_CODE_PIECES * GWAVES == 64, "pieces are spread evenly");
 
-// LDS image of a tile: rows of GK/2 = 64 bytes = four 16-byte chunks; chunk c
-// of row r sits at position c ^ ((r >> 2) & 3), so the 16 lanes of an LDS read
-// quarter (rows r .. r+15, one chunk each) hit 16 distinct bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+// LDS image of a tile: rows of GK/2 = 128 bytes = eight 16-byte chunks; chunk c
+// of row r sits at position c ^ ((r >> 1) & 7), so the 16 lanes of an LDS read
+// quarter (rows r .. r+15, one chunk each) hit 16 distinct bank groups.  A copy
+// piece is 8 whole rows: every global read of the copy is a full 128-byte line
+// (pieces gathering half lines from 16 rows copy at half the rate).
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-// Per-lane global byte offset of the chunk that lane `lane` of copy piece p
-// brings in: LDS chunk 64 p + lane = (row, position), global chunk = position
-// un-swizzled.  Rows past the matrix repeat its last row (never stored).
+// Per-lane global byte offset (without the step's K offset) of the chunk that
+// lane `lane` of code piece p brings in: LDS chunk 64 p + lane = (row, position),
+// global chunk = position un-swizzled.  Rows past the matrix repeat its last
+// row (never stored); chunks past K (the last step when K % 256 == 128) are
+// never read by the MFMAs.
 __device__ __forceinline__ int piece_offset(int p, int lane, int row0, int rows, int rowbytes) {
     const int i = p * 64 + lane;
-    const int r = i >> 2, q = i & 3;
-    const int c = q ^ ((r >> 2) & 3);
+    const int r = i >> 3, q = i & 7;
+    const int c = q ^ ((r >> 1) & 7);
     const int row = min(row0 + r, rows - 1);
     return row * rowbytes + c * 16;
 }
@@ -116,61 +126,98 @@ __device__ __forceinline__ f32x16 mfma_fp4(const uint4& a, const uint4& b, const
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 2, sa, 2, sb);
 }
 
-// Workgroup: 4 waves, wave (wm, wn) = (w & 1, w >> 1) computes output rows
-// m0 + 64 wm .. +63 and columns n0 + 128 wn .. +127 as 2 x 4 blocks of 32 x 32
-// (accumulators acc[nb][mb] of C^T).
-__global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint8_t* __restrict__ a_codes,
-                                                         const uint8_t* __restrict__ a_scales,
-                                                         const uint8_t* __restrict__ w_codes,
-                                                         const uint8_t* __restrict__ w_scales,
-                                                         uint2* __restrict__ out, int M, int N, int K) {
-    __shared__ uint4 sa0[GM * 4];
-    __shared__ uint4 sa1[GM * 4];
-    __shared__ uint4 sw0[GN * 4];
-    __shared__ uint4 sw1[GN * 4];
+// One pipeline stage: the A tile (GM rows) and the W tile (GN rows) of a K
+// step, and the step's eight block scales of every row (two 32-bit words per
+// row), ordered so each lane's words are contiguous: sa[wm][n_lane][mb][word]
+// for row 64 wm + 32 mb + n_lane of A, sw[wn][n_lane][nb][word] for row
+// 128 wn + 32 nb + n_lane of W.  A lane reads its A words with one 16-byte
+// and its W words with two 16-byte LDS reads (4-byte reads would be merged into
+// ds_read2 instructions that lose the LDS alias information, and the compiler
+// would then make them wait for every copy in flight).
+struct GStage {
+    uint4 a[GM * 8];
+    uint4 w[GN * 8];
+    uint4 sa[GM / 2];
+    uint4 sw[GN / 2];
+};
+
+// Workgroup: 8 waves over a 256 x 256 output tile; accumulators acc[nb][mb]
+// of C^T (wave columns 128 wn + 32 nb, rows 64 wm + 32 mb).
+__global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* __restrict__ a_codes,
+                                                                const uint8_t* __restrict__ a_scales,
+                                                                const uint8_t* __restrict__ w_codes,
+                                                                const uint8_t* __restrict__ w_scales,
+                                                                uint2* __restrict__ out, int M, int N, int K) {
+    // two distinct stage objects, statically indexed (the loop is unrolled by
+    // two), so the compiler never makes an LDS read wait for the copy in flight
+    __shared__ GStage st0, st1;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
-    const int n_tiles = (N + GN - 1) / GN;
-    const int m0 = (blockIdx.x / n_tiles) * GM;
-    const int n0 = (blockIdx.x % n_tiles) * GN;
+    const int wm = wave & 3, wn = wave >> 2;
+    const int n_lane = lane & 31, hh = lane >> 5;
+
+    // Tile order: groups of G_GROUP column tiles, row tiles fastest-but-one
+    // inside a group (logical r -> row tile r / gw, column tile r % gw), and
+    // each XCD a contiguous range of the order.  The ~32 workgroups an XCD
+    // runs at once then cover 4 row tiles x 8 column tiles: the group's W
+    // tiles stay in that XCD's L2 while it sweeps down the rows.
+    const int m_tiles = (M + GM - 1) / GM, n_tiles = (N + GN - 1) / GN;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int g = logical / (G_GROUP * m_tiles);
+    const int gw = min(G_GROUP, n_tiles - g * G_GROUP);
+    const int r = logical - g * G_GROUP * m_tiles;
+    const int m0 = (r / gw) * GM;
+    const int n0 = (g * G_GROUP + r % gw) * GN;
     const int rowbytes = K / 2, srow = K / 32;
-    const int nk = K / GK;
+    const int nk = (K + GK - 1) / GK;      // the last step is a half step when K % 256 == 128
+    const bool half_last = (K % GK) != 0;
 
     const __amdgpu_buffer_rsrc_t ra = raw_rsrc(a_codes, (uint32_t)((int64_t)M * rowbytes));
     const __amdgpu_buffer_rsrc_t rw = raw_rsrc(w_codes, (uint32_t)((int64_t)N * rowbytes));
-    // copy pieces of this wave: A pieces wave, wave + 4 (of 8); W pieces wave + 4 j (of 16)
-    int offa[2], offw[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) offa[j] = piece_offset(wave + 4 * j, lane, m0, M, rowbytes);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) offw[j] = piece_offset(wave + 4 * j, lane, n0, N, rowbytes);
-    auto copy_tile = [&](int kk, uint4* da, uint4* dw) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(da + (wave + 4 * j) * 64),
-                                                     16, offa[j], kk * (GK / 2), 0, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(dw + (wave + 4 * j) * 64),
-                                                     16, offw[j], kk * (GK / 2), 0, 0);
-    };
+    const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(a_scales, (uint32_t)((int64_t)M * srow));
+    const __amdgpu_buffer_rsrc_t rsw = raw_rsrc(w_scales, (uint32_t)((int64_t)N * srow));
 
-    // scale rows of this lane: output rows (B operand) and columns (A operand)
-    const int n_lane = lane & 31, hh = lane >> 5;
-    const uint8_t* sa_row[2];
-    const uint8_t* sw_row[4];
+    // code pieces of this wave: pieces wave + 8 j of the 64 per step (A: 0..31, W: 32..63);
+    // their per-lane offsets are recomputed at each step (a few integer ops) to spare registers
+    // scale pieces of this wave: pieces 2 wave, 2 wave + 1 of the 16 (A: 0..7, W: 8..15); lane l of
+    // piece q fills word 64 q' + l of sa / sw, gathered from the row and word the order above puts there
+    const bool scale_of_a = wave < GWAVES / 2;
+    int soff[G_SCALE_PIECES];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) sa_row[mb] = a_scales + (int64_t)min(m0 + 64 * wm + 32 * mb + n_lane, M - 1) * srow;
+    for (int j = 0; j < G_SCALE_PIECES; ++j) {
+        const int wd = 64 * (2 * (scale_of_a ? wave : wave - GWAVES / 2) + j) + lane;
+        const int word = wd & 1;
+        const int row = scale_of_a ? 64 * (wd >> 7) + 32 * ((wd >> 1) & 1) + ((wd >> 2) & 31)
+                                   : 128 * (wd >> 8) + 32 * ((wd >> 1) & 3) + ((wd >> 3) & 31);
+        soff[j] = min((scale_of_a ? m0 : n0) + row, (scale_of_a ? M : N) - 1) * srow + 4 * word;
+    }
+    const int sbase = 64 * 2 * (scale_of_a ? wave : wave - GWAVES / 2);   // first word of this wave's pieces
+
+    auto copy_stage = [&](int kk, GStage& d) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) sw_row[nb] = w_scales + (int64_t)min(n0 + 128 * wn + 32 * nb + n_lane, N - 1) * srow;
-    // the four block scales of step kk, shifted so byte 0 / byte 2 belong to this lane's K-half
-    auto load_scales = [&](int kk, uint32_t (&sa)[2], uint32_t (&sw)[4]) {
+        for (int j = 0; j < G_SCALE_PIECES; ++j) {
+            if (scale_of_a)  // wave-uniform
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsa, (__attribute__((address_space(3))) void*)(reinterpret_cast<uint32_t*>(d.sa) + sbase + 64 * j),
+                    4, soff[j], kk * (GK / 32), 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsw, (__attribute__((address_space(3))) void*)(reinterpret_cast<uint32_t*>(d.sw) + sbase + 64 * j),
+                    4, soff[j], kk * (GK / 32), 0, 0);
+        }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sa[mb] = *reinterpret_cast<const uint32_t*>(sa_row[mb] + 4 * kk);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) sw[nb] = *reinterpret_cast<const uint32_t*>(sw_row[nb] + 4 * kk);
+        for (int j = 0; j < G_CODE_PIECES; ++j) {
+            const int p = wave + GWAVES * j;
+            if (p < GM / 8)  // wave-uniform
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(d.a + p * 64),
+                                                         16, piece_offset(p, lane, m0, M, rowbytes), kk * (GK / 2),
+                                                         0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (__attribute__((address_space(3))) void*)(d.w + (p - GM / 8) * 64), 16,
+                    piece_offset(p - GM / 8, lane, n0, N, rowbytes), kk * (GK / 2), 0, 0);
+        }
     };
 
     f32x16 acc[4][2];
@@ -183,26 +230,43 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint8_t* __res
     // them below the next step's wait for the copies in flight, and memory
     // latency and compute stop overlapping.  settle() (an ordered volatile asm
     // reading every accumulator) and the scheduling fences pin them there.
-    auto compute = [&](const uint4* ta, const uint4* tw, const uint32_t (&sa)[2], const uint32_t (&sw)[4]) {
+    // NSUB = 4 MFMA steps per pipeline step, 2 for the half step.
+    auto compute = [&](const GStage& t, auto nsub_c) {
+        constexpr int NSUB = decltype(nsub_c)::value;
         __builtin_amdgcn_sched_barrier(0);
-        int sca[2], scw[4];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sca[mb] = (int)(sa[mb] >> (8 * hh));
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) scw[nb] = (int)(sw[nb] >> (8 * hh));
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        // scale words: A rows (mb, word) and W rows (nb, word) of this lane
+        const uint4 wa = t.sa[32 * wm + n_lane];
+        const uint4 wwlo = t.sw[2 * (32 * wn + n_lane)];
+        const uint4 wwhi = t.sw[2 * (32 * wn + n_lane) + 1];
+        const uint32_t sa_w[2][2] = {{wa.x, wa.y}, {wa.z, wa.w}};
+        const uint32_t sw_w[4][2] = {{wwlo.x, wwlo.y}, {wwlo.z, wwlo.w}, {wwhi.x, wwhi.y}, {wwhi.z, wwhi.w}};
+        // operand fragments of MFMA step s, read just before its MFMAs (fenced,
+        // so the compiler cannot hoist every read of the stage and run out of
+        // registers; the other wave of the SIMD covers the read latency)
+        uint4 fa[2][2], fw[2][4];
+        auto read_frags = [&](int s, uint4 (&a)[2], uint4 (&w)[4]) {
             const int c = 2 * s + hh;
-            uint4 fa[2], fw[4];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) fa[mb] = ta[swz(64 * wm + 32 * mb + n_lane, c)];
+            for (int mb = 0; mb < 2; ++mb) a[mb] = t.a[swz(64 * wm + 32 * mb + n_lane, c)];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) fw[nb] = tw[swz(128 * wn + 32 * nb + n_lane, c)];
+            for (int nb = 0; nb < 4; ++nb) w[nb] = t.w[swz(128 * wn + 32 * nb + n_lane, c)];
+        };
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            read_frags(s, fa[s & 1], fw[s & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // MFMA step s covers blocks 2 s and 2 s + 1: word s >> 1, bytes 2 (s & 1) + hh
+            int sca[2], scw[4];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) sca[mb] = (int)(sa_w[mb][s >> 1] >> (8 * hh));
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) scw[nb] = (int)(sw_w[nb][s >> 1] >> (8 * hh));
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
-                    acc[nb][mb] = mfma_fp4(fw[nb], fa[mb], acc[nb][mb], scw[nb], sca[mb], 2 * s);
+                    acc[nb][mb] = mfma_fp4(fw[s & 1][nb], fa[s & 1][mb], acc[nb][mb], scw[nb], sca[mb], 2 * (s & 1));
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
@@ -211,28 +275,37 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint8_t* __res
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    uint32_t sa_0[2], sw_0[4], sa_1[2], sw_1[4];
-    copy_tile(0, sa0, sw0);
-    load_scales(0, sa_0, sw_0);
-    int kk = 0;
-    for (; kk + 2 <= nk; kk += 2) {
+    // Step i: wait for its copies (the only ones in flight), barrier (every
+    // wave's pieces have landed, and every wave is done with the stage step
+    // i + 1 will overwrite), issue step i + 1, compute step i.  __syncthreads()
+    // serves: its fence waits for outstanding memory operations, and at the
+    // barrier those are exactly the copies step i needs.  Full steps run in the
+    // loop; a final half step (K % 256 == 128) has its own copy of the code, as
+    // one shared step with both variants behind a branch exhausts the registers.
+    copy_stage(0, st0);
+    auto step = [&](int i, const GStage& cur, GStage& nxt, auto nsub_c) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        copy_tile(kk + 1, sa1, sw1);
-        load_scales(kk + 1, sa_1, sw_1);
-        compute(sa0, sw0, sa_0, sw_0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (kk + 2 < nk) {
-            copy_tile(kk + 2, sa0, sw0);
-            load_scales(kk + 2, sa_0, sw_0);
-        }
-        compute(sa1, sw1, sa_1, sw_1);
+        if (i + 1 < nk) copy_stage(i + 1, nxt);
+        compute(cur, nsub_c);
+    };
+    const std::integral_constant<int, 4> full_step;
+    const std::integral_constant<int, 2> half_step;
+    const int nfull = half_last ? nk - 1 : nk;
+    int i = 0;
+    for (; i + 2 <= nfull; i += 2) {
+        step(i, st0, st1, full_step);
+        step(i + 1, st1, st0, full_step);
     }
-    if (kk < nk) {  // odd number of steps: the last one is in buffer 0
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        compute(sa0, sw0, sa_0, sw_0);
+    if (i < nfull) {
+        step(i, st0, st1, full_step);
+        ++i;
+    }
+    if (half_last) {  // step i = nk - 1 lives in stage i & 1
+        if (i & 1)
+            step(i, st1, st0, half_step);
+        else
+            step(i, st0, st1, half_step);
     }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -249,11 +322,12 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint8_t* __res
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hh;
+            for (int gq = 0; gq < 4; ++gq) {
+                const int n = n0 + 128 * wn + 32 * nb + 8 * gq + 4 * hh;
                 if (n < N) {
                     const f32x16& c = acc[nb][mb];
-                    orow[n / 4] = make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
+                    orow[n / 4] = make_uint2(pack_bf16x2(c[4 * gq], c[4 * gq + 1]),
+                                             pack_bf16x2(c[4 * gq + 2], c[4 * gq + 3]));
                 }
             }
     }
@@ -262,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint8_t* __res
 hipError_t launch_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
                              void* out, int M, int N, int K, hipStream_t stream) {
     const int64_t grid = (int64_t)((M + GM - 1) / GM) * ((N + GN - 1) / GN);
-    mxfp4_gemm_kernel<<<(int)grid, 256, 0, stream>>>(
+    mxfp4_gemm_kernel<<<(int)grid, GWAVES * 64, 0, stream>>>(
         static_cast<const uint8_t*>(a_codes), static_cast<const uint8_t*>(a_scales),
         static_cast<const uint8_t*>(w_codes), static_cast<const uint8_t*>(w_scales), static_cast<uint2*>(out), M,
         N, K);
