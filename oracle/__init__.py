@@ -23,6 +23,10 @@ What it computes, in float64, as the plain definition with no tiling:
 * Ring blocks (``oracle.ring``): attention of a query shard over one key/value
   block with the row log-sum-exp, and the exact merge of two such partial
   results (ring attention, in the same reference list).
+* MXFP4 (``oracle.mx``): OCP MX quantisation and the block-scaled linear
+  layer (MXFP4/Quark on MI350 blog).
+* DBCache (``oracle.dbcache``): the relative L1 residual difference and the
+  reuse decision against the threshold (RDNA 4 xDiT blog, step caching).
 * ``oracle.brute``: the same steps as pure-Python scalar loops, used to pin
   the numpy version on tiny inputs.
 

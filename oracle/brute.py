@@ -83,3 +83,10 @@ def row_lse(q, k, pos_q=None, pos_k=None, axes_dim=None, theta=10000.0, scale=No
             ob.append(oh)
         out.append(ob)
     return out
+
+
+def residual_diff(prev, cur):
+    """The DBCache relative L1 difference of two flat residuals, scalar loops."""
+    den = math.fsum(abs(float(p)) for p in prev)
+    num = math.fsum(abs(float(c) - float(p)) for p, c in zip(prev, cur))
+    return math.inf if den == 0.0 else num / den

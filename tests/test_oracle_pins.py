@@ -439,3 +439,27 @@ def test_mx_linear_exact_on_representable_values():
             exact = sum(val(int(ac[m, k])) * Fraction(2) ** (int(asc[m, k // 32]) - 127) *
                         val(int(wc[n, k])) * Fraction(2) ** (int(wsc[n, k // 32]) - 127) for k in range(K))
             assert got[m, n] == float(exact)
+
+
+# ---------------------------------------------------------------- DBCache reuse decision
+
+def test_residual_diff_closed_forms():
+    from oracle.dbcache import can_reuse, residual_diff
+    rng = np.random.default_rng(46)
+    p = rng.standard_normal(1000)
+    assert residual_diff(p, p) == 0.0
+    assert abs(residual_diff(p, 1.25 * p) - 0.25) <= 1e-15          # cur = (1 + a) prev -> |a|
+    assert abs(residual_diff(p, 0.9 * p) - 0.1) <= 1e-15
+    assert residual_diff(p, np.zeros_like(p)) == 1.0                 # cur = 0 -> 1
+    assert residual_diff(p, -p) == 2.0
+    c = p + 0.05 * rng.standard_normal(1000)
+    assert abs(residual_diff(3.0 * p, 3.0 * c) - residual_diff(p, c)) <= 1e-15   # scale invariance
+    assert residual_diff(np.zeros(5), np.ones(5)) == math.inf and not can_reuse(np.zeros(5), np.zeros(5), 0.12)
+    assert can_reuse(p, 1.1 * p, 0.12) and not can_reuse(p, 1.2 * p, 0.12)
+
+
+def test_residual_diff_matches_brute_force():
+    from oracle.dbcache import residual_diff
+    rng = np.random.default_rng(47)
+    p, c = rng.standard_normal(257), rng.standard_normal(257)
+    assert abs(residual_diff(p, c) - brute.residual_diff(p.tolist(), c.tolist())) <= 1e-14
