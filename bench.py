@@ -37,14 +37,25 @@ MEASURED_TRAFFIC = {
                                        "profile": "profiles/attn_core_flux2048.md"},
     ("03489aa4bb220259", "flux2048_fp8"): {"read_bytes": 694.4e6, "write_bytes": 136.0e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
+    # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
+    ("69dde4a003be8d54", "flux2048_qkv"): {"read_bytes": 435.7e6, "write_bytes": 331.1e6,
+                                           "profile": "profiles/mxfp4_gemm_flux2048_qkv.md"},
+    # residual_diff_partials + residual_diff_finish (hash over RESIDUAL_SOURCES)
+    ("c4af6b56612c2ae2", "flux2048_residual"): {"read_bytes": 207.80e6, "write_bytes": 0.26e6,
+                                                "profile": "profiles/dbcache_residual_diff_flux2048.md"},
 }
 
 
-def kernel_sources_hash() -> str:
+MXFP4_SOURCES = ["dit_joint_self_amd/csrc/mxfp4.hip", "dit_joint_self_amd/csrc/attn_common.h",
+                 "dit_joint_self_amd/csrc/bf16_util.h"]
+RESIDUAL_SOURCES = ["dit_joint_self_amd/csrc/dbcache.hip", "dit_joint_self_amd/csrc/attn_common.h"]
+
+
+def kernel_sources_hash(files=None) -> str:
     import hashlib
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
-    for f in KERNEL_SOURCES:
+    for f in files or KERNEL_SOURCES:
         with open(os.path.join(root, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -54,12 +65,19 @@ FP4_PEAK_TFLOPS = 10066.3   # 256 CU x 16384 flop/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 
 
+def _traffic(files, workload):
+    """Measured HBM bytes per launch while the kernel sources match the ones profiled, else None."""
+    meas = MEASURED_TRAFFIC.get((kernel_sources_hash(files), workload))
+    return None if meas is None else meas["read_bytes"] + meas["write_bytes"]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="flux2048", choices=list(W.WORKLOADS) + list(W.LINEAR_WORKLOADS),
+    ap.add_argument("--workload", default="flux2048",
+                    choices=list(W.WORKLOADS) + list(W.LINEAR_WORKLOADS) + list(W.RESIDUAL_WORKLOADS),
                     help="an attention workload, or an MXFP4 linear-layer shape (quantise + A4W4 GEMM)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -287,7 +305,7 @@ def gemm_bench(args, lw, torch, dj):
         "pct_of_peak": 100.0 * flops / (step_ms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "mxfp4_gemm_kernel", "achieved": flops / (g_avg * 1e-3) / 1e12,
                      "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": flops / (g_avg * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, "traffic": None,
+                     "frac": flops / (g_avg * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, "traffic": _traffic(MXFP4_SOURCES, lw.name),
                      "algorithmic_bytes": gemm_bytes, "avg_ms": g_avg},
         "stages_ms": {"mxfp4_quantize": q_avg, "mxfp4_gemm": g_avg,
                       "quantize_GBps": quant_bytes / (q_avg * 1e-3) / 1e9},
@@ -323,6 +341,75 @@ def gemm_bench(args, lw, torch, dj):
     print(json.dumps(rec), flush=True)
 
 
+def residual_bench(args, rw, torch, dj):
+    """DBCache reuse decision: one step = dit_dbcache_residual_diff over two
+    bf16 residuals of one step pair (the partial-sum kernel and the one-block
+    finish).  HBM bound: the algorithmic bytes are the two residuals, read once."""
+    pb, cb = W.make_residual_inputs(rw)
+    prev, cur = bf16_dev(pb, torch), bf16_dev(cb, torch)
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(dj.dit_dbcache_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    diff = torch.empty(1, dtype=torch.float64, device="cuda")
+    reuse = torch.empty(1, dtype=torch.int32, device="cuda")
+    step = lambda: dj.dit_dbcache_residual_diff(prev, cur, 0.12, ws=ws, diff=diff, reuse=reuse, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = 4.0 * rw.n
+    gbs = nbytes / (step_ms * 1e-3) / 1e9
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "DBCache residual-difference GB/s (relative L1 distance of two bf16 residuals + decision), 1 GPU",
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32/fp64 sums",
+        "data": "synthetic",
+        "config": {"workload": rw.name, "tokens": rw.tokens, "hidden": rw.hidden, "n": rw.n, "note": rw.note},
+        "decision": {"diff": float(diff.item()), "reuse": int(reuse.item()), "threshold": 0.12},
+        "roofline": {"bound": "hbm", "kernel": "residual_diff_partials + residual_diff_finish (one call)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": _traffic(RESIDUAL_SOURCES, rw.name), "algorithmic_bytes": nbytes, "avg_ms": call_ms},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        from oracle.dbcache import residual_diff
+        rows, chunk = 0, 512
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds and rows < rw.tokens:
+            residual_diff(W.bf16_bits_to_f32(pb[rows:rows + chunk]), W.bf16_bits_to_f32(cb[rows:rows + chunk]))
+            rows += chunk
+        dt = time.perf_counter() - t0
+        rows = min(rows, rw.tokens)
+        rec["cpu_baseline"] = {"value": 4.0 * rows * rw.hidden / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{rw.name}: the float64 difference over the first {rows} of {rw.tokens} "
+                                         f"tokens in chunks of {chunk}, {dt:.1f} s",
+                               "host_cpus": len(os.sched_getaffinity(0))}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -340,6 +427,9 @@ def main():
         return
     if args.workload in W.LINEAR_WORKLOADS:
         gemm_bench(args, W.LINEAR_WORKLOADS[args.workload], torch, dj)
+        return
+    if args.workload in W.RESIDUAL_WORKLOADS:
+        residual_bench(args, W.RESIDUAL_WORKLOADS[args.workload], torch, dj)
         return
     w = W.get(args.workload)
     if args.ring > 1:

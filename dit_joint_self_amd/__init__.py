@@ -3,7 +3,8 @@
 Argument marshalling only: every step of the path runs in the library's HIP
 kernels.  Functions keep the C names (``dit_attn_forward``, ``dit_rope_tables``,
 ``dit_attn_workspace_bytes``, ``dit_attn_prepare_kv``, ``dit_attn_core``,
-``dit_attn_core_lse``, ``dit_attn_merge_lse`` and the ``_fp8`` entries) and
+``dit_attn_core_lse``, ``dit_attn_merge_lse``, the ``_fp8`` entries, the
+MXFP4 linear-layer entries and the DBCache decision) and
 take torch tensors (their device pointers are passed) or plain integers as
 pointers.  A missing library raises ``RuntimeError``: there is no fallback.
 """
@@ -19,7 +20,7 @@ __all__ = [
     "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_kv",
     "dit_attn_core", "dit_attn_workspace_bytes_fp8", "dit_attn_prepare_kv_fp8", "dit_attn_core_fp8",
     "dit_attn_forward_fp8", "dit_attn_core_lse", "dit_attn_merge_lse", "dit_mxfp4_quantize", "dit_mxfp4_gemm",
-    "dit_mxfp4_linear", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
+    "dit_mxfp4_linear", "dit_dbcache_workspace_bytes", "dit_dbcache_residual_diff", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
     "DIT_ERR_NO_DEVICE", "DIT_ERR_OUT_OF_MEMORY", "DIT_ERR_LAUNCH", "DIT_DTYPE_BF16",
     "DIT_DTYPE_FP8_E4M3",
 ]
@@ -61,6 +62,8 @@ _SIGNATURES = {
     "dit_mxfp4_quantize": (_I, [_P, _P, _P, _I, _I, _P]),
     "dit_mxfp4_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dit_mxfp4_linear": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
+    "dit_dbcache_workspace_bytes": (ctypes.c_size_t, []),
+    "dit_dbcache_residual_diff": (_I, [_P, _P, ctypes.c_int64, ctypes.c_double, _P, ctypes.c_size_t, _P, _P, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -250,6 +253,32 @@ def dit_mxfp4_linear(x, w_codes, w_scales, out=None, stream=None):
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _check(lib().dit_mxfp4_linear(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(out), M, N, K, _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------- DBCache reuse decision
+
+def dit_dbcache_workspace_bytes() -> int:
+    return int(lib().dit_dbcache_workspace_bytes())
+
+
+def dit_dbcache_residual_diff(prev, cur, threshold: float, ws=None, diff=None, reuse=None, stream=None):
+    """Relative L1 difference of two bf16 residuals of the same size and the
+    decision diff < threshold, both left on the device: (diff float64 [1],
+    reuse int32 [1])."""
+    import torch
+    n = int(prev.numel())
+    if int(cur.numel()) != n:
+        raise ValueError("prev and cur must have the same number of elements")
+    if ws is None:
+        ws = torch.empty(dit_dbcache_workspace_bytes(), dtype=torch.uint8, device=prev.device)
+    if diff is None:
+        diff = torch.empty(1, dtype=torch.float64, device=prev.device)
+    if reuse is None:
+        reuse = torch.empty(1, dtype=torch.int32, device=prev.device)
+    ws_bytes = int(ws.numel() * ws.element_size()) if hasattr(ws, "numel") else 0
+    _check(lib().dit_dbcache_residual_diff(_ptr(prev), _ptr(cur), n, float(threshold), _ptr(ws), ws_bytes,
+                                           _ptr(diff), _ptr(reuse), _stream(stream)))
+    return diff, reuse
 
 
 # ---------------------------------------------------------------- fp8 (e4m3 codes + per-tensor scales)

@@ -25,6 +25,9 @@ hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, c
 hipError_t launch_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* out,
                             float* lse_out, int64_t rows, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const void* x, void* codes, void* scales, int64_t rows, int K, hipStream_t stream);
+size_t residual_diff_workspace_bytes();
+hipError_t launch_residual_diff(const void* prev, const void* cur, int64_t n, double threshold, void* ws,
+                                double* diff, int32_t* reuse, hipStream_t stream);
 hipError_t launch_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
                              void* out, int M, int N, int K, hipStream_t stream);
 hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
@@ -41,7 +44,7 @@ hipError_t launch_rope_tables(const int32_t* pos, int S, int n_axes, const int32
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kMaxDevices = 64;
 // Smallest query tile any kernel variant uses; bounds the workgroup count.
 constexpr int kMinBlockM = 128;
@@ -497,4 +500,33 @@ dit_status_t dit_mxfp4_linear(const void* x, const void* w_codes, const void* w_
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e == hipSuccess) e = ef;
     return launched(e, "mxfp4 linear");
+}
+
+// ---------------------------------------------------------------- DBCache reuse decision
+
+size_t dit_dbcache_workspace_bytes(void) { return dit::residual_diff_workspace_bytes(); }
+
+dit_status_t dit_dbcache_residual_diff(const void* prev, const void* cur, int64_t n, double threshold, void* ws,
+                                       size_t ws_bytes, double* diff, int32_t* reuse, void* stream) {
+    if (n < 0) return fail(DIT_ERR_INVALID_ARG, "n must be >= 0 (got %lld)", (long long)n);
+    if (!ws || !diff || (n > 0 && (!prev || !cur)))
+        return fail(DIT_ERR_INVALID_ARG, "ws, diff and (for n > 0) prev and cur must be non-NULL");
+    if (n > ((int64_t)1 << 40)) return fail(DIT_ERR_UNSUPPORTED, "n must be at most 2^40 (got %lld)", (long long)n);
+    const size_t need = dit::residual_diff_workspace_bytes();
+    if (ws_bytes < need) return fail(DIT_ERR_INVALID_ARG, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
+    if (!aligned16(prev) || !aligned16(cur) || !aligned16(ws))
+        return fail(DIT_ERR_INVALID_ARG, "prev, cur and ws must be 16-byte aligned");
+    if (!aligned(diff, 8) || (reuse && !aligned(reuse, 4)))
+        return fail(DIT_ERR_INVALID_ARG, "diff must be 8-byte and reuse 4-byte aligned");
+    const size_t nb = (size_t)n * 2;
+    if (overlaps(ws, need, prev, nb) || overlaps(ws, need, cur, nb) || overlaps(ws, need, diff, 8) ||
+        (reuse && overlaps(ws, need, reuse, 4)))
+        return fail(DIT_ERR_INVALID_ARG, "the workspace overlaps an input or an output");
+    if (overlaps(diff, 8, prev, nb) || overlaps(diff, 8, cur, nb) ||
+        (reuse && (overlaps(reuse, 4, prev, nb) || overlaps(reuse, 4, cur, nb) || overlaps(reuse, 4, diff, 8))))
+        return fail(DIT_ERR_INVALID_ARG, "diff or reuse overlaps an input or the other output");
+    dit_status_t st;
+    if ((st = check_device()) != DIT_OK) return st;
+    return launched(dit::launch_residual_diff(prev, cur, n, threshold, ws, diff, reuse, static_cast<hipStream_t>(stream)),
+                    "residual_diff kernels");
 }

@@ -202,3 +202,48 @@ def make_linear_inputs(w: LinearWorkload):
     x = rng.standard_normal((w.M, w.K), dtype=np.float32)
     wt = rng.standard_normal((w.N, w.K), dtype=np.float32) * np.float32(1.0 / np.sqrt(w.K))
     return bf16_round_bits(x), bf16_round_bits(wt)
+
+
+@dataclass(frozen=True)
+class ResidualWorkload:
+    """Residuals of the first Fn blocks of a DiT in two consecutive denoising
+    steps, for the DBCache reuse decision: [tokens, hidden] bf16 each."""
+    name: str
+    tokens: int
+    hidden: int
+    rel_change: float   # scale of the step-to-step change relative to the residual
+    seed: int
+    note: str = field(default="", compare=False)
+
+    @property
+    def n(self) -> int:
+        return self.tokens * self.hidden
+
+
+RESIDUAL_WORKLOADS: Dict[str, ResidualWorkload] = {
+    w.name: w for w in [
+        ResidualWorkload("flux2048_residual", tokens=16896, hidden=3072, rel_change=0.1, seed=3001,
+                         note="hidden state of the 16896-token 2048x2048 joint sequence (24 heads x 128)"),
+        ResidualWorkload("flux1024x768_residual", tokens=3584, hidden=3072, rel_change=0.2, seed=3002,
+                         note="hidden state of the 3584-token 1024x768 joint sequence"),
+        ResidualWorkload("residual_ragged", tokens=333, hidden=1003, rel_change=0.05, seed=3003,
+                         note="test shape: n = 333 x 1003, not a multiple of 8"),
+    ]
+}
+
+
+def make_residual_inputs(w: ResidualWorkload):
+    """(prev_bits, cur_bits), bfloat16 bit patterns [tokens, hidden].  The
+    previous residual is Gaussian with a log-normal scale per hidden channel
+    (a few channels carry most of the magnitude, as activation outliers do);
+    the current one adds an independent Gaussian change of relative size
+    rel_change per element, so the relative L1 difference is close to
+    rel_change."""
+    rng = np.random.default_rng(w.seed)
+    ch = np.exp(rng.standard_normal(w.hidden, dtype=np.float32))
+    prev = rng.standard_normal((w.tokens, w.hidden), dtype=np.float32)
+    prev *= ch
+    cur = rng.standard_normal((w.tokens, w.hidden), dtype=np.float32)
+    cur *= np.float32(w.rel_change) * ch
+    cur += prev
+    return bf16_round_bits(prev), bf16_round_bits(cur)

@@ -241,6 +241,36 @@ dit_status_t dit_mxfp4_gemm(const void* a_codes, const void* a_scales, const voi
 dit_status_t dit_mxfp4_linear(const void* x, const void* w_codes, const void* w_scales, void* out,
                               int M, int N, int K, void* stream);
 
+/*
+ * DBCache step caching.  The AMD RDNA 4 xDiT blog (section on skipping
+ * transformer work when the model takes enough denoising steps) enables
+ * DBCache with a residual diff threshold: after the first Fn transformer
+ * blocks of a step, the residual those blocks produced is compared with the
+ * previous step's, and the rest of the step reuses cached work when they are
+ * close.  The page names the threshold (0.12 in its example) but no formula;
+ * this library takes the relative L1 distance
+ *
+ *     diff  = sum_i |cur_i - prev_i| / sum_i |prev_i|   (+inf when prev is all zero)
+ *     reuse = diff < threshold
+ *
+ * dit_dbcache_workspace_bytes  the fixed workspace size (bytes) that
+ *   dit_dbcache_residual_diff needs, for any n.
+ *
+ * dit_dbcache_residual_diff  prev, cur: bf16 residuals of n elements each
+ *   (any shape, contiguous, 16-byte aligned; n >= 0; n = 0 gives +inf and no
+ *   reuse, and prev and cur may then be NULL).  ws: device workspace of at least dit_dbcache_workspace_bytes(),
+ *   16-byte aligned, not overlapping the inputs or outputs; its contents are
+ *   scratch.  diff: device double (8-byte aligned), written with the
+ *   difference; reuse: device int32 (4-byte aligned) set to 1 or 0, or NULL.
+ *   Sums of |.| are taken in fp32 over 8 elements and in fp64 beyond, in a
+ *   fixed order: the result is reproducible for a given n.  NaN inputs give a
+ *   NaN diff and reuse = 0.
+ */
+size_t dit_dbcache_workspace_bytes(void);
+
+dit_status_t dit_dbcache_residual_diff(const void* prev, const void* cur, int64_t n, double threshold,
+                                       void* ws, size_t ws_bytes, double* diff, int32_t* reuse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     lib = dj.lib()
     for name in dj.EXPORTED_SYMBOLS:
         assert getattr(lib, name) is not None
-    assert dj.dit_abi_version() == 2
+    assert dj.dit_abi_version() == 3
 
 
 def _expected_workspace(B, H, S):
@@ -239,3 +239,29 @@ def test_mxfp4_entry_points_reject_bad_arguments():
         assert q(x, c, s, 4, 64, None) == dj.DIT_ERR_NO_DEVICE
         assert g() == dj.DIT_ERR_NO_DEVICE
         assert lin(x, c, s, o, 8, 16, 256, None) == dj.DIT_ERR_NO_DEVICE
+
+
+def test_dbcache_entry_point_rejects_bad_arguments():
+    L = dj.lib()
+    need = L.dit_dbcache_workspace_bytes()
+    assert need == 8192 * 16
+    p, c, w, d, r = 0x30000000, 0x40000000, 0x50000000, 0x60000000, 0x60000040
+    f = lambda **kw: L.dit_dbcache_residual_diff(kw.get("p", p), kw.get("c", c), kw.get("n", 1000), 0.12,
+                                                 kw.get("w", w), kw.get("wb", need), kw.get("d", d),
+                                                 kw.get("r", r), None)
+    assert f(p=None) == dj.DIT_ERR_INVALID_ARG
+    assert f(c=None) == dj.DIT_ERR_INVALID_ARG
+    assert f(w=None) == dj.DIT_ERR_INVALID_ARG
+    assert f(d=None) == dj.DIT_ERR_INVALID_ARG
+    assert f(n=-1) == dj.DIT_ERR_INVALID_ARG
+    assert f(n=2 ** 40 + 1) == dj.DIT_ERR_UNSUPPORTED
+    assert f(wb=need - 16) == dj.DIT_ERR_INVALID_ARG                      # workspace too small
+    assert f(c=c + 2) == dj.DIT_ERR_INVALID_ARG                           # misaligned input
+    assert f(d=d + 4) == dj.DIT_ERR_INVALID_ARG                           # misaligned diff
+    assert f(w=p + 1024) == dj.DIT_ERR_INVALID_ARG                        # workspace inside prev
+    assert f(d=c + 16) == dj.DIT_ERR_INVALID_ARG                          # diff inside cur
+    assert f(r=d + 4) == dj.DIT_ERR_INVALID_ARG                           # reuse over diff
+    if _no_device():
+        assert f() == dj.DIT_ERR_NO_DEVICE
+        assert f(n=0, r=None) == dj.DIT_ERR_NO_DEVICE                     # empty residuals are valid
+        assert f(n=0, p=None, c=None) == dj.DIT_ERR_NO_DEVICE             # ... also as NULL pointers
