@@ -65,6 +65,19 @@ FP4_PEAK_TFLOPS = 10066.3   # 256 CU x 16384 flop/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 
 
+def clock_record(torch, dj, kernel_tflops, step_tflops, flop_per_clk_per_cu):
+    """Peak recomputed from the device's CU count and the shader clock that a
+    bf16 MFMA load on every CU runs at (the clock probe, right after the timed
+    steps), and the two rates priced against it."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ghz, probe_tflops = dj.dit_clock_probe(blocks=2 * cus, iters=20000)
+    peak = cus * flop_per_clk_per_cu * ghz * 1e9 / 1e12
+    return {"probe_GHz": ghz, "cus": cus, "peak_at_probe_clock_TFLOPs": peak,
+            "probe_mfma_TFLOPs": probe_tflops,
+            "pct_of_peak_at_probe_clock": 100.0 * step_tflops / peak,
+            "kernel_frac_at_probe_clock": kernel_tflops / peak}
+
+
 def _traffic(files, workload):
     """Measured HBM bytes per launch while the kernel sources match the ones profiled, else None."""
     meas = MEASURED_TRAFFIC.get((kernel_sources_hash(files), workload))
@@ -540,6 +553,7 @@ def main():
                       "prepare_kv_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9},
         "forward_ms": fwd_ms,
         "wall_s": wall,
+        "clock": clock_record(torch, dj, achieved, flops / (step_ms * 1e-3) / 1e12, 8192 if fp8 else 4096),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

@@ -20,7 +20,8 @@ __all__ = [
     "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_kv",
     "dit_attn_core", "dit_attn_workspace_bytes_fp8", "dit_attn_prepare_kv_fp8", "dit_attn_core_fp8",
     "dit_attn_forward_fp8", "dit_attn_core_lse", "dit_attn_merge_lse", "dit_mxfp4_quantize", "dit_mxfp4_gemm",
-    "dit_mxfp4_linear", "dit_dbcache_workspace_bytes", "dit_dbcache_residual_diff", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
+    "dit_mxfp4_linear", "dit_dbcache_workspace_bytes", "dit_dbcache_residual_diff", "dit_clock_probe",
+    "dit_wall_clock_khz", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
     "DIT_ERR_NO_DEVICE", "DIT_ERR_OUT_OF_MEMORY", "DIT_ERR_LAUNCH", "DIT_DTYPE_BF16",
     "DIT_DTYPE_FP8_E4M3",
 ]
@@ -64,6 +65,8 @@ _SIGNATURES = {
     "dit_mxfp4_linear": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
     "dit_dbcache_workspace_bytes": (ctypes.c_size_t, []),
     "dit_dbcache_residual_diff": (_I, [_P, _P, ctypes.c_int64, ctypes.c_double, _P, ctypes.c_size_t, _P, _P, _P]),
+    "dit_clock_probe": (_I, [_P, ctypes.c_size_t, _I, _I, _P]),
+    "dit_wall_clock_khz": (_I, [ctypes.POINTER(ctypes.c_int)]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -279,6 +282,32 @@ def dit_dbcache_residual_diff(prev, cur, threshold: float, ws=None, diff=None, r
     _check(lib().dit_dbcache_residual_diff(_ptr(prev), _ptr(cur), n, float(threshold), _ptr(ws), ws_bytes,
                                            _ptr(diff), _ptr(reuse), _stream(stream)))
     return diff, reuse
+
+
+# ---------------------------------------------------------------- clock probe
+
+def dit_wall_clock_khz() -> int:
+    khz = ctypes.c_int(0)
+    _check(lib().dit_wall_clock_khz(ctypes.byref(khz)))
+    return int(khz.value)
+
+
+def dit_clock_probe(blocks: int = 512, iters: int = 20000, stream=None):
+    """Shader clock under a bf16 MFMA load on every CU: (GHz, MFMA TFLOP/s of
+    the probe).  The median over waves of shader cycles / constant-rate ticks,
+    times the constant counter's rate."""
+    import torch
+    out = torch.zeros(blocks * 4 * 3, dtype=torch.int64, device="cuda")
+    _check(lib().dit_clock_probe(_ptr(out), out.numel() * 8, blocks, iters, _stream(stream)))
+    torch.cuda.synchronize()
+    v = out.view(-1, 3).cpu().numpy().astype("float64")
+    if (v[:, 2] != 0).any() or (v[:, 1] <= 0).any():
+        raise RuntimeError("clock probe produced invalid counters")
+    rate_hz = dit_wall_clock_khz() * 1e3
+    ghz = float(sorted(v[:, 0] / v[:, 1])[len(v) // 2]) * rate_hz / 1e9
+    seconds = float(v[:, 1].max()) / rate_hz
+    tflops = blocks * 4 * iters * 4 * 2.0 * 32 * 32 * 16 / seconds / 1e12
+    return ghz, tflops
 
 
 # ---------------------------------------------------------------- fp8 (e4m3 codes + per-tensor scales)

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libditattn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "prepare_kv.hip", "attn_core.hip", "attn_core_fp8.hip", "lse_merge.hip", "mxfp4.hip", "dbcache.hip", "rope_tables.hip"]
+SOURCES = ["api.hip", "prepare_kv.hip", "attn_core.hip", "attn_core_fp8.hip", "lse_merge.hip", "mxfp4.hip", "dbcache.hip", "clock_probe.hip", "rope_tables.hip"]
 
 # Packed-fp32 VALU forms are disabled for all device code.
 HIPCC_FLAGS = [

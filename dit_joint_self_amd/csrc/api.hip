@@ -26,6 +26,7 @@ hipError_t launch_lse_merge(const void* o_a, const float* lse_a, const void* o_b
                             float* lse_out, int64_t rows, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const void* x, void* codes, void* scales, int64_t rows, int K, hipStream_t stream);
 size_t residual_diff_workspace_bytes();
+hipError_t launch_clock_probe(int blocks, int iters, void* out, hipStream_t stream);
 hipError_t launch_residual_diff(const void* prev, const void* cur, int64_t n, double threshold, void* ws,
                                 double* diff, int32_t* reuse, hipStream_t stream);
 hipError_t launch_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
@@ -529,4 +530,30 @@ dit_status_t dit_dbcache_residual_diff(const void* prev, const void* cur, int64_
     if ((st = check_device()) != DIT_OK) return st;
     return launched(dit::launch_residual_diff(prev, cur, n, threshold, ws, diff, reuse, static_cast<hipStream_t>(stream)),
                     "residual_diff kernels");
+}
+
+// ---------------------------------------------------------------- clock probe
+
+dit_status_t dit_clock_probe(void* out, size_t out_bytes, int blocks, int iters, void* stream) {
+    if (!out) return fail(DIT_ERR_INVALID_ARG, "out must be non-NULL");
+    if (blocks < 1 || blocks > 65535) return fail(DIT_ERR_INVALID_ARG, "blocks must be in [1, 65535] (got %d)", blocks);
+    if (iters < 1 || iters > (1 << 24)) return fail(DIT_ERR_INVALID_ARG, "iters must be in [1, 2^24] (got %d)", iters);
+    if (out_bytes < (size_t)blocks * 4 * 24)
+        return fail(DIT_ERR_INVALID_ARG, "out holds %zu bytes, %zu needed", out_bytes, (size_t)blocks * 4 * 24);
+    if (!aligned(out, 8)) return fail(DIT_ERR_INVALID_ARG, "out must be 8-byte aligned");
+    dit_status_t st;
+    if ((st = check_device()) != DIT_OK) return st;
+    return launched(dit::launch_clock_probe(blocks, iters, out, static_cast<hipStream_t>(stream)), "clock_probe_kernel");
+}
+
+dit_status_t dit_wall_clock_khz(int* khz) {
+    if (!khz) return fail(DIT_ERR_INVALID_ARG, "khz must be non-NULL");
+    dit_status_t st;
+    if ((st = check_device()) != DIT_OK) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(DIT_ERR_LAUNCH, "could not read the wall clock rate");
+    }
+    return ok();
 }

@@ -271,6 +271,26 @@ size_t dit_dbcache_workspace_bytes(void);
 dit_status_t dit_dbcache_residual_diff(const void* prev, const void* cur, int64_t n, double threshold,
                                        void* ws, size_t ws_bytes, double* diff, int32_t* reuse, void* stream);
 
+/*
+ * Clock probe (measurement aid, not part of the attention path).  The
+ * published MI355X peaks assume a 2.4 GHz shader clock; under a sustained
+ * matrix-core load the chip runs slower, and a roofline can also be priced at
+ * the clock it actually runs at.
+ *
+ * dit_clock_probe  runs `blocks` workgroups of 256 threads (4 waves each, two
+ *   workgroups per CU) that each issue iters x 4 independent
+ *   v_mfma_f32_32x32x16_bf16 between two reads of the shader cycle counter
+ *   and of the constant-rate counter.  out: device buffer of at least
+ *   blocks x 4 x 24 bytes, 8-byte aligned; per wave three uint64: shader
+ *   cycles, constant-rate ticks, 0.  blocks in [1, 65535], iters in
+ *   [1, 2^24].
+ * dit_wall_clock_khz  the constant-rate counter's frequency (kHz) of the
+ *   current device.
+ */
+dit_status_t dit_clock_probe(void* out, size_t out_bytes, int blocks, int iters, void* stream);
+
+dit_status_t dit_wall_clock_khz(int* khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -265,3 +265,17 @@ def test_dbcache_entry_point_rejects_bad_arguments():
         assert f() == dj.DIT_ERR_NO_DEVICE
         assert f(n=0, r=None) == dj.DIT_ERR_NO_DEVICE                     # empty residuals are valid
         assert f(n=0, p=None, c=None) == dj.DIT_ERR_NO_DEVICE             # ... also as NULL pointers
+
+
+def test_clock_probe_rejects_bad_arguments():
+    L = dj.lib()
+    out = 0x30000000
+    assert L.dit_clock_probe(None, 4096, 8, 10, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_clock_probe(out, 4096, 0, 10, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_clock_probe(out, 4096, 8, 0, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_clock_probe(out, 4096, 8, 2 ** 24 + 1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_clock_probe(out, 8 * 4 * 24 - 1, 8, 10, None) == dj.DIT_ERR_INVALID_ARG   # out too small
+    assert L.dit_clock_probe(out + 4, 4096, 8, 10, None) == dj.DIT_ERR_INVALID_ARG         # misaligned
+    assert L.dit_wall_clock_khz(None) == dj.DIT_ERR_INVALID_ARG
+    if _no_device():
+        assert L.dit_clock_probe(out, 4096, 8, 10, None) == dj.DIT_ERR_NO_DEVICE
