@@ -26,16 +26,21 @@ import dit_workloads as W
 
 METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=16896,H=24,D=128 (1 GPU)"
 
-# HBM bytes per attention-kernel launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
-# (scaled by a plain-copy calibration), keyed by the hash of the kernel sources they were
-# taken on and by workload; reported as roofline.traffic only while the sources match.
-KERNEL_SOURCES = ["dit_joint_self_amd/csrc/attn_core.hip", "dit_joint_self_amd/csrc/attn_core_fp8.hip",
-                  "dit_joint_self_amd/csrc/attn_common.h", "dit_joint_self_amd/csrc/tile_layout.h",
-                  "dit_joint_self_amd/csrc/bf16_util.h", "dit_joint_self_amd/csrc/fp8_util.h"]
+# HBM bytes per kernel launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a
+# plain-copy calibration), keyed by the hash of the sources of the kernel they were taken on
+# and by workload; reported as roofline.traffic only while those sources are unchanged.
+BF16_SOURCES = ["dit_joint_self_amd/csrc/attn_core.hip", "dit_joint_self_amd/csrc/attn_common.h",
+                "dit_joint_self_amd/csrc/tile_layout.h", "dit_joint_self_amd/csrc/bf16_util.h"]
+FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/csrc/attn_common.h",
+               "dit_joint_self_amd/csrc/tile_layout.h", "dit_joint_self_amd/csrc/bf16_util.h",
+               "dit_joint_self_amd/csrc/fp8_util.h"]
+KERNEL_SOURCES = BF16_SOURCES
 MEASURED_TRAFFIC = {
-    ("03489aa4bb220259", "flux2048"): {"read_bytes": 1102.4e6, "write_bytes": 210.1e6,
+    # dit_attn_core (attn_core_kernel x 2 + attn_merge_kernel), hash over BF16_SOURCES
+    ("9cce712c3c61e9a3", "flux2048"): {"read_bytes": 1102.4e6, "write_bytes": 210.1e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
-    ("03489aa4bb220259", "flux2048_fp8"): {"read_bytes": 694.4e6, "write_bytes": 136.0e6,
+    # dit_attn_core_fp8 (attn_core_fp8_kernel x 2 + attn_merge_kernel), hash over FP8_SOURCES
+    ("5a97fc88a92dae14", "flux2048_fp8"): {"read_bytes": 695.3e6, "write_bytes": 140.1e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
     ("69dde4a003be8d54", "flux2048_qkv"): {"read_bytes": 435.7e6, "write_bytes": 331.1e6,
@@ -515,7 +520,7 @@ def main():
     fwd_ms = e0.elapsed_time(e1) / K
 
     flops = w.flops
-    src_hash = kernel_sources_hash()
+    src_hash = kernel_sources_hash(FP8_SOURCES if fp8 else BF16_SOURCES)
     meas = MEASURED_TRAFFIC.get((src_hash, w.name))
     traffic = None if meas is None else meas["read_bytes"] + meas["write_bytes"]
     core_avg = float(np.mean(core_ms))
