@@ -16,13 +16,9 @@
 //     rescaled) only when a lane's step weights sum past 16 * 24, which keeps
 //     every p' below 448.  l sums the fp32 p'; O = O_acc * v_scale / l.
 //
-// Work per workgroup, split plan and merge are the bf16 kernel's
-// (attn_common.h), and so is the loop: K' and V^T parts in their own pairs of
-// LDS buffers (K' one tile ahead), and per wave the QK^T MFMAs of tile j+1
-// beside the exp2 / e4m3 packing of tile j, then O += P'V for tile j.  Per
-// 64-key tile a wave issues 4 QK^T and 4 PV MFMAs of 32x32x64 (2 * 32 * 32 *
-// 64 flop each).  Roofline: MFMA bound (fp8 peak); the softmax VALU work per
-// MFMA is four times the bf16 kernel's.
+// Work per workgroup, tile stream, split plan and merge are the bf16 kernel's
+// (attn_common.h).  Per 64-key tile a wave issues 4 QK^T and 4 PV MFMAs of
+// 32x32x64 (2 * 32 * 32 * 64 flop each).  Roofline: MFMA bound (fp8 peak).
 
 #include <hip/hip_runtime.h>
 
@@ -47,157 +43,103 @@ __device__ __forceinline__ i32x8 lds_read32(const uint4* p) {
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// Weights of four scores, 4w .. 4w + 3 of the lane's 32 (key block w / 4,
-// registers 4 (w % 4) ..): exp2, packed to e4m3 in the PV B-operand order
-// (byte j of pf = key block j / 16, register j % 16); their fp32 sum is added
-// to `sum`.  No clamp to 448: a weight above it makes the lane's sum exceed
+// exp2 of a lane's 32 scores (two key blocks), packed to e4m3 in the PV B
+// operand order (byte j = key block j/16, register j%16); fp32 sum of p'.
+// No clamp to 448: a weight above it makes the lane's sum exceed
 // F8_SUM_LIMIT, and the tile is then redone with a moved offset (p' <= 16).
-// cvt_pk replaces one half of its destination, so pf[w] of the previous tile
-// serves as the untouched half and no register has to be cleared first.
-__device__ __forceinline__ void f8_weight_quad(const f32x16 (&s)[2], int w, i32x8& pf, float& sum) {
-    const f32x16& sc = s[w >> 2];
-    const int r = (w & 3) * 4;
-    const float a = __builtin_amdgcn_exp2f(sc[r]), b = __builtin_amdgcn_exp2f(sc[r + 1]);
-    const float c = __builtin_amdgcn_exp2f(sc[r + 2]), d = __builtin_amdgcn_exp2f(sc[r + 3]);
-    sum += (a + b) + (c + d);
-    int x = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, pf[w], false);
-    pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, x, true);
+// cvt_pk replaces one half of its destination register and keeps the other,
+// so the packing needs no cleared register: the second call overwrites the
+// half the first one kept.
+__device__ __forceinline__ void f8_weights(const f32x16 (&s)[2], i32x8& pf, float& sum) {
+    float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const f32x16& sc = s[w >> 2];
+        const int r = (w & 3) * 4;
+        const float a = __builtin_amdgcn_exp2f(sc[r]), b = __builtin_amdgcn_exp2f(sc[r + 1]);
+        const float c = __builtin_amdgcn_exp2f(sc[r + 2]), d = __builtin_amdgcn_exp2f(sc[r + 3]);
+        t0 += a + b;
+        t1 += c + d;
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, pf[w], false);
+        pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+    }
+    sum = t0 + t1;
 }
 
-// K' operand of QK^T step i (key block i & 1, 64-dim step i >> 1) and V^T
-// operand of PV step db (32-dim block), for lane (n, hh): 32 bytes each.
-__device__ __forceinline__ i32x8 f8_k_operand(const uint4* kt, int i, int n, int hh) {
-    return lds_read32(kt + ((i & 1) * 32 + n) * F8_K_ROW_CHUNKS + (i >> 1) * 4 + hh * 2);
-}
-__device__ __forceinline__ i32x8 f8_v_operand(const uint4* vt, int db, int n, int hh) {
-    return lds_read32(vt + (db * 32 + n) * F8_V_ROW_CHUNKS + hh * 2);
-}
+template <bool MASKED>
+__device__ __forceinline__ void f8_tile(const uint4* kt, int j, bool first, int S, int n, int hh, int qscale,
+                                        const i32x8 (&qf)[2], f32x16 (&o)[4], f32x16& negm, float& lsum) {
+    const uint4* vt = kt + F8_K_PART_CHUNKS;
 
-// The tile copies of one pipelined step (the K' part two tiles ahead, the V^T
-// part one tile ahead), issued together at the start of the step: measured
-// slightly faster than one piece per stage-A step.
-struct F8TileCopies {
-    static constexpr int KJ = (F8_K_PART_CHUNKS / 64 + NW - 1) / NW;  // K' pieces per wave (at most)
-    static constexpr int VJ = (F8_V_PART_CHUNKS / 64 + NW - 1) / NW;  // V^T pieces per wave (at most)
-    __amdgpu_buffer_rsrc_t rsrc;
-    int ksoff, vsoff;
-    uint4* kdst;
-    uint4* vdst;
-    bool kon;
-    int wave, lane;
-    __device__ __forceinline__ void at_step(int j) const {
-        if (j < KJ) {
-            const int p = j * NW + wave;
-            if (kon && p < F8_K_PART_CHUNKS / 64) lds_piece(rsrc, ksoff + p * 1024, kdst + p * 64, lane);
-        } else if (j < KJ + VJ) {
-            const int p = (j - KJ) * NW + wave;
-            if (p < F8_V_PART_CHUNKS / 64) lds_piece(rsrc, vsoff + p * 1024, vdst + p * 64, lane);
+    // ---- S'^T = K' Q''^T * 2^e - m + 4: per key block kb, two 64-dim steps.
+    f32x16 s[2];
+    {
+        i32x8 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kb = i >> 1, kk = i & 1;
+            a[i] = lds_read32(kt + (kb * 32 + n) * F8_K_ROW_CHUNKS + kk * 4 + hh * 2);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kb = i >> 1, kk = i & 1;
+            s[kb] = mfma_f8(a[i], qf[kk], kk == 0 ? negm : s[kb], qscale);
         }
     }
-};
 
-// Stage A: QK^T MFMA step i of the next tile (K' part kn) beside weight quads
-// 2i, 2i + 1 of the current tile.
-template <bool QK, bool EXP>
-__device__ __forceinline__ void f8_stage_a(const uint4* kn, const i32x8 (&qf)[2], int qscale, const f32x16& negm,
-                                           f32x16 (&sn)[2], const f32x16 (&sc)[2], i32x8& pf, float& sum, int n,
-                                           int hh) {
-    i32x8 a[4];
-    if (QK) {
+    if (MASKED) {
+        const int base = j * KV_TILE + 8 * hh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = f8_k_operand(kn, i, n, hh);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (base + 32 * kb + 16 * (r >> 3) + (r & 7) >= S) s[kb][r] = -INFINITY;
     }
+
+    i32x8 pf = i32x8{};
+    float tsum = 0.0f;
+    bool slow = first;
+    if (!slow) {
+        f8_weights(s, pf, tsum);
+        slow = __builtin_amdgcn_ballot_w64(!(tsum <= F8_SUM_LIMIT)) != 0;
+    }
+    if (slow) {
+        // Exact row max of this tile becomes the offset: p' <= 16 afterwards.
+        float mx = s[0][0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (QK) sn[i & 1] = mfma_f8(a[i], qf[i >> 1], (i >> 1) == 0 ? negm : sn[i & 1], qscale);
-        if (EXP) {
-            f8_weight_quad(sc, 2 * i, pf, sum);
-            f8_weight_quad(sc, 2 * i + 1, pf, sum);
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        mx = swap_halves_max(mx);
+        const float shift = first ? mx - 4.0f : fmaxf(mx - 4.0f, 0.0f);
+        if (!first) {
+            const float alpha = __builtin_amdgcn_exp2f(-shift);
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[db] *= alpha;
         }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-__device__ __forceinline__ float f8_tile_max(const f32x16 (&s)[2]) {
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    return swap_halves_max(mx);
-}
-
-// Keys past S: lane half hh, register r of key block kb holds key
-// 32 kb + 16 (r >> 3) + 8 hh + (r & 7) of tile j.
-__device__ __forceinline__ void f8_mask_tail(f32x16 (&s)[2], int j, int S, int hh) {
-    const int base = j * KV_TILE + 8 * hh;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (base + 32 * kb + 16 * (r >> 3) + (r & 7) >= S) s[kb][r] = -INFINITY;
-}
-
-// Between the stages: if some lane's weights sum past F8_SUM_LIMIT, move the
-// offset to (row max - 4) of this tile (never down), rescale O and l, apply the
-// move to the next tile's scores too and redo the weights; then add the sum.
-template <bool QK>
-__device__ __forceinline__ void f8_settle(f32x16 (&sc)[2], f32x16 (&sn)[2], i32x8& pf, float sum, f32x16 (&o)[4],
-                                          f32x16& negm, float& lsum) {
-    if (__builtin_amdgcn_ballot_w64(!(sum <= F8_SUM_LIMIT)) != 0) {
-        const float shift = fmaxf(f8_tile_max(sc) - 4.0f, 0.0f);
-        const float alpha = __builtin_amdgcn_exp2f(-shift);
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-        sc[0] -= shift;
-        sc[1] -= shift;
+        s[0] -= shift;
+        s[1] -= shift;
         negm -= shift;
-        if (QK) {
-            sn[0] -= shift;
-            sn[1] -= shift;
-        }
-        sum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) f8_weight_quad(sc, w, pf, sum);
+        f8_weights(s, pf, tsum);
     }
-    lsum += sum;
-}
+    lsum += tsum;
 
-// Stage B: O^T += V^T P'^T, four 32-dim blocks of 64 keys.
-__device__ __forceinline__ void f8_stage_b(const uint4* vt, const i32x8& pf, f32x16 (&o)[4], int n, int hh) {
-    i32x8 a[4];
+    // ---- O^T += V^T P'^T: four 32-dim blocks, 64 keys each.
+    {
+        i32x8 a[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) a[db] = f8_v_operand(vt, db, n, hh);
+        for (int db = 0; db < 4; ++db) a[db] = lds_read32(vt + (db * 32 + n) * F8_V_ROW_CHUNKS + hh * 2);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        __builtin_amdgcn_sched_barrier(0);
-        o[db] = mfma_f8(a[db], pf, o[db], E8M0_ONE);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int db = 0; db < 4; ++db) o[db] = mfma_f8(a[db], pf, o[db], E8M0_ONE);
+        // The 16-pass fp8 MFMA keeps reading its A operand after it has
+        // issued, and the compiler does not hold back a later LDS load into
+        // those registers: the next tile's K' reads, right after the
+        // barrier, could land in a V^T operand still being read (seen as
+        // run-to-run differences in the output).  Pin the four products here
+        // and let 16 wait states pass before anything else issues.
+        asm volatile("s_nop 15" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
     }
-}
-
-__device__ __forceinline__ void f8_tile_step(const uint4* kn, const uint4* vt, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                                             const i32x8 (&qf)[2], int qscale, i32x8& pf, f32x16 (&o)[4],
-                                             f32x16& negm, float& lsum, int n, int hh, const F8TileCopies& cp) {
-#pragma unroll
-    for (int j = 0; j < F8TileCopies::KJ + F8TileCopies::VJ; ++j) cp.at_step(j);
-    float sum = 0.0f;
-    f8_stage_a<true, true>(kn, qf, qscale, negm, sn, sc, pf, sum, n, hh);
-    f8_settle<true>(sc, sn, pf, sum, o, negm, lsum);
-    f8_stage_b(vt, pf, o, n, hh);
-}
-
-__device__ __forceinline__ void f8_tile_step_last(const uint4* vt, f32x16 (&sc)[2], int j, int S,
-                                                  const i32x8 (&qf)[2], int qscale, i32x8& pf, f32x16 (&o)[4],
-                                                  f32x16& negm, float& lsum, int n, int hh) {
-    f8_mask_tail(sc, j, S, hh);
-    float sum = 0.0f;
-    f32x16 none[2];
-    f8_stage_a<false, true>(nullptr, qf, qscale, negm, none, sc, pf, sum, n, hh);
-    f8_settle<false>(sc, none, pf, sum, o, negm, lsum);
-    f8_stage_b(vt, pf, o, n, hh);
 }
 
 template <bool PARTIAL>
@@ -205,13 +147,8 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     const uint4* __restrict__ q, float q_scale, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
     const uint8_t* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ part, int S, int ntiles, int nqt,
     int item0, int nsplit, float qmul, int has_rope) {
-    // K' parts run one tile ahead of V^T parts, each through its own pair of
-    // buffers (as in the bf16 kernel): distinct objects and a loop unrolled by
-    // two keep every buffer static.
-    __shared__ uint4 kb0[F8_K_PART_CHUNKS];
-    __shared__ uint4 kb1[F8_K_PART_CHUNKS];
-    __shared__ uint4 vb0[F8_V_PART_CHUNKS];
-    __shared__ uint4 vb1[F8_V_PART_CHUNKS];
+    __shared__ uint4 lds0[F8_TILE_CHUNKS];
+    __shared__ uint4 lds1[F8_TILE_CHUNKS];
 
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int item = item0 + logical / nsplit;
@@ -220,7 +157,6 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     const int qt = item - (int)bh * nqt;
     const int tb = (int)((int64_t)f * ntiles / nsplit);
     const int te = (int)((int64_t)(f + 1) * ntiles / nsplit);
-    const int nt = te - tb;  // >= 1
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -233,22 +169,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     const __amdgpu_buffer_rsrc_t rsrc =
         raw_rsrc(ws + F8_HEADER_BYTES + bh * (int64_t)ntiles * F8_TILE_BYTES, (uint32_t)ntiles * F8_TILE_BYTES);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int tile0 = tb * F8_TILE_BYTES;
-    auto copies = [&](int ki, uint4* kd, bool kon, int vi, uint4* vd) {
-        F8TileCopies c;
-        c.rsrc = rsrc;
-        c.ksoff = tile0 + ki * F8_TILE_BYTES;
-        c.vsoff = tile0 + vi * F8_TILE_BYTES + F8_K_PART_CHUNKS * 16;
-        c.kdst = kd;
-        c.vdst = vd;
-        c.kon = kon;
-        c.wave = wv;
-        c.lane = lane;
-        return c;
-    };
-    copy_to_lds<NW, F8_K_PART_CHUNKS>(rsrc, tile0, kb0, wv, lane);
-    copy_to_lds<NW, F8_V_PART_CHUNKS>(rsrc, tile0 + F8_K_PART_CHUNKS * 16, vb0, wv, lane);
-    if (nt > 1) copy_to_lds<NW, F8_K_PART_CHUNKS>(rsrc, tile0 + F8_TILE_BYTES, kb1, wv, lane);
+    copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, tb * F8_TILE_BYTES, lds0, wv, lane);
 
     // ---- Q prologue.  Largest |q'| is 448 q_scale (times sqrt(2) with RoPE);
     // choose e so that it maps to at most 448 after the factor qmul * sk.
@@ -296,45 +217,28 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
 
-    // Scores of tile 0, offset so that its largest weight is 2^4, then the
-    // pipelined steps.  Step i's scores live in sA for even i and sB for odd i.
-    f32x16 sA[2], sB[2];
-    i32x8 pf = i32x8{};
+    const int last = te - 1;
+    int j = tb;
+    for (; j + 2 <= last; j += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (j + 1) * F8_TILE_BYTES, lds1, wv, lane);
+        f8_tile<false>(lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (j + 2) * F8_TILE_BYTES, lds0, wv, lane);
+        f8_tile<false>(lds1, j + 1, false, S, n, hh, qscale, qf, o, negm, lsum);
+    }
+    if (j < last) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (j + 1) * F8_TILE_BYTES, lds1, wv, lane);
+        f8_tile<false>(lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
+        ++j;
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    {
-        float sum = 0.0f;
-        f8_stage_a<true, false>(kb0, qf, qscale, negm, sA, sB, pf, sum, n, hh);
-    }
-    if (nt == 1) f8_mask_tail(sA, te - 1, S, hh);
-    {
-        const float shift = f8_tile_max(sA) - 4.0f;
-        sA[0] -= shift;
-        sA[1] -= shift;
-        negm -= shift;
-    }
-    int i = 0;
-    for (; i + 2 <= nt - 1; i += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        f8_tile_step(kb1, vb0, sA, sB, qf, qscale, pf, o, negm, lsum, n, hh, copies(i + 2, kb0, true, i + 1, vb1));
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        f8_tile_step(kb0, vb1, sB, sA, qf, qscale, pf, o, negm, lsum, n, hh,
-                     copies(i + 3, kb1, i + 3 < nt, i + 2, vb0));
-    }
-    if (i < nt - 1) {  // i = nt - 2, even: one more full step, then the last tile from sB / vb1
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        f8_tile_step(kb1, vb0, sA, sB, qf, qscale, pf, o, negm, lsum, n, hh, copies(i + 2, kb0, false, i + 1, vb1));
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        f8_tile_step_last(vb1, sB, te - 1, S, qf, qscale, pf, o, negm, lsum, n, hh);
-    } else {  // i = nt - 1, even: the last tile from sA / vb0
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        f8_tile_step_last(vb0, sA, te - 1, S, qf, qscale, pf, o, negm, lsum, n, hh);
-    }
+    f8_tile<true>(((j - tb) & 1) ? lds1 : lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
 #pragma unroll
     for (int db = 0; db < 4; ++db) settle(o[db]);
 

@@ -153,3 +153,18 @@ def test_linear_full_size_sampled():
     a_c, a_s = mxfp4_quantize(bf16_f64(xb[rows]))
     w_c, w_s = mxfp4_quantize(bf16_f64(wb))
     _gate(got, mxfp4_dequantize(a_c, a_s), mxfp4_dequantize(w_c, w_s), "flux2048_qkv")
+
+
+def test_linear_full_size_bitwise_repeatable():
+    """Two calls of the full-size QKV layer agree bit for bit (the GEMM issues
+    its FP4 MFMAs back to back while the next fragments load)."""
+    torch = _torch()
+    dj = _dj()
+    lw = W.LINEAR_WORKLOADS["flux2048_qkv"]
+    xb, wb = W.make_linear_inputs(lw)
+    x = _dev_bf16(xb)
+    wc, ws = dj.dit_mxfp4_quantize(_dev_bf16(wb))
+    a = dj.dit_mxfp4_linear(x, wc, ws)
+    b = dj.dit_mxfp4_linear(x, wc, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
