@@ -138,3 +138,18 @@ def test_fp8_bitwise_repeatable_with_tile_loop():
     for _ in range(3):
         assert np.array_equal(a, _run(w, qkv8, split=True))
     assert np.array_equal(a, _run(w, qkv8))
+
+
+def test_fp8_bitwise_repeatable_full_size():
+    """flux2048_fp8: three calls agree bit for bit."""
+    torch = _torch()
+    import dit_joint_self_amd as dj
+    w = W.get("flux2048_fp8")
+    (q8, sq), (k8, sk), (v8, sv) = _quantized(w)
+    dev = lambda c: torch.from_numpy(np.ascontiguousarray(c)).to("cuda")
+    q, k, v = dev(q8), dev(k8), dev(v8)
+    cos, sin = dj.dit_rope_tables(torch.from_numpy(W.positions(w)).to("cuda"), w.axes_dim, w.theta)
+    outs = [dj.dit_attn_forward_fp8(q, k, v, sq, sk, sv, cos, sin, S_txt=w.S_txt) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))

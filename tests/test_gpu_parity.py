@@ -279,3 +279,19 @@ def test_bitwise_repeatable_with_tile_loop():
     for _ in range(3):
         assert np.array_equal(a, _run(w, qb, kb, vb, split=True))
     assert np.array_equal(a, _run(w, qb, kb, vb))
+
+
+def test_bitwise_repeatable_full_size():
+    """The headline shape (16896 tokens x 24 heads): three calls agree bit for
+    bit, so no MFMA operand or LDS buffer is overwritten while still in use
+    anywhere in the 6.2 rounds of workgroups."""
+    torch = _torch()
+    w = W.get("flux2048")
+    qb, kb, vb = W.make_bf16_inputs(w)
+    dj = _dj()
+    q, k, v = to_device_bf16(qb), to_device_bf16(kb), to_device_bf16(vb)
+    cos, sin = _tables(w)
+    outs = [dj.dit_attn_forward(q, k, v, cos, sin, S_txt=w.S_txt) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
