@@ -36,30 +36,50 @@ __global__ __launch_bounds__(256) void prepare_kv_kernel(
     const uint4* ksrc = k + bh * (int64_t)S * 16;
     const uint4* vsrc = v + bh * (int64_t)S * 16;
 
-    // V rows into LDS (coalesced 16-byte loads).
+    // Every load of the thread is issued before any is used (V rows, K chunks
+    // and their cos/sin rows), so the HBM latency is paid about once per
+    // workgroup rather than once per chunk.
+    constexpr int KI = (K_PART_CHUNKS + 255) / 256;  // K chunks per thread (the last partly)
+    uint4 vw[4], kw[KI];
+    float4 cw[KI], sw[KI];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int x = tid + i * 256;
         const int key = key0 + (x >> 4);
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (key < S) w = vsrc[(int64_t)key * 16 + (x & 15)];
-        vtile[x] = w;
+        vw[i] = make_uint4(0, 0, 0, 0);
+        if (key < S) vw[i] = vsrc[(int64_t)key * 16 + (x & 15)];
     }
-
     // K part: output chunk x = (row rho, chunk c); chunk 16 of a row is padding.
-    for (int x = tid; x < K_PART_CHUNKS; x += 256) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+        const int x = tid + i * 256;
         const int rho = x / K_ROW_CHUNKS;
         const int c = x - rho * K_ROW_CHUNKS;
         const int key = key0 + kperm(rho);
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (c < 16 && key < S) {
-            w = ksrc[(int64_t)key * 16 + c];
+        kw[i] = make_uint4(0, 0, 0, 0);
+        if (x < K_PART_CHUNKS && c < 16 && key < S) {
+            kw[i] = ksrc[(int64_t)key * 16 + c];
             if (has_rope) {
-                float f[8];
-                unpack8(w, f);
-                rotate4(f, cos_t[(int64_t)key * 16 + c], sin_t[(int64_t)key * 16 + c]);
-                w = pack8(f);
+                cw[i] = cos_t[(int64_t)key * 16 + c];
+                sw[i] = sin_t[(int64_t)key * 16 + c];
             }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vtile[tid + i * 256] = vw[i];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+        const int x = tid + i * 256;
+        if (x >= K_PART_CHUNKS) break;
+        const int rho = x / K_ROW_CHUNKS;
+        const int c = x - rho * K_ROW_CHUNKS;
+        const int key = key0 + kperm(rho);
+        uint4 w = kw[i];
+        if (has_rope && c < 16 && key < S) {
+            float f[8];
+            unpack8(w, f);
+            rotate4(f, cw[i], sw[i]);
+            w = pack8(f);
         }
         dst[x] = w;
     }
