@@ -295,3 +295,35 @@ def test_bitwise_repeatable_full_size():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_joint_kv_permutation_without_rope():
+    """Without RoPE, permuting the key/value rows jointly only reorders the
+    sums of the softmax, so the output moves by rounding alone: both runs stay
+    within the parity gates of the oracle and within twice them of each
+    other.  The permutation crosses tile and key-range boundaries (S = 700)."""
+    w = _small(60, (20, 32), B=1, H=3, seed=5)
+    qb, kb, vb = W.make_bf16_inputs(w)
+    perm = np.random.default_rng(9).permutation(w.S)
+    a = _run(w, qb, kb, vb, rope=False)
+    b = _run(w, qb, kb[:, :, perm], vb[:, :, perm], rope=False)
+    want = _oracle(w, qb, kb, vb, rope=False)
+    _assert_close(a, want, "unpermuted")
+    _assert_close(b, want, "permuted keys")
+    d = np.abs(a - b)
+    assert d.max() <= 2 * 1e-2 and d.mean() <= 2 * 1e-3, (d.max(), d.mean())
+
+
+def test_constant_v_gives_the_constant_exactly():
+    """V with the same row for every key: every output row is that row, bit
+    for bit.  The bf16 weight times a bf16 value is exact in fp32, O / l then
+    differs from the constant by fp32 summation rounding only (~1e-6
+    relatively), far below half a bf16 step, so rounding returns the
+    constant.  RoPE on, a key-range split and its merge included (S = 3584)."""
+    w = W.get("flux1024x768")
+    qb, kb, _ = W.make_bf16_inputs(w)
+    row = W.bf16_round_bits(np.linspace(-3.0, 3.0, w.D).astype(np.float32))
+    vb = np.broadcast_to(row, (w.B, w.H, w.S, w.D)).copy()
+    got = _run(w, qb, kb, vb)
+    want = np.broadcast_to(W.bf16_bits_to_f32(row).astype(np.float64), got.shape)
+    assert np.array_equal(got, want)
