@@ -431,7 +431,7 @@ def residual_bench(args, rw, torch, dj):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU only: this library runs on one GPU (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     import torch
