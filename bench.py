@@ -553,6 +553,7 @@ def main():
                                + " (whole-range and key-range launches) + attn_merge_kernel",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "traffic_unit": "HBM bytes per dit_attn_core call (read + write)",
+                     "hbm_GBps": None if traffic is None else traffic / (core_avg * 1e-3) / 1e9,
                      "algorithmic_bytes": core_bytes, "avg_ms": core_avg, "kernel_sources": src_hash},
         "stages_ms": {"prepare_kv": prep_avg, "attn_core": core_avg,
                       "prepare_kv_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9},
