@@ -133,42 +133,65 @@ __global__ __launch_bounds__(256) void prepare_kv_fp8_kernel(
     const uint4* ksrc = k + bh * (int64_t)S * 8;
     const uint4* vsrc = v + bh * (int64_t)S * 8;
 
+    // Every load of the thread is issued before any is used, as in the bf16 kernel.
+    constexpr int KI = (F8_K_PART_CHUNKS + 255) / 256;  // K chunks per thread (the last partly)
+    uint4 vw[2], kw[KI];
+    float4 cw[KI][2], sw[KI][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int x = tid + i * 256;
         const int key = key0 + (x >> 3);
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (key < S) w = vsrc[(int64_t)key * 8 + (x & 7)];
-        vtile[x] = w;
+        vw[i] = make_uint4(0, 0, 0, 0);
+        if (key < S) vw[i] = vsrc[(int64_t)key * 8 + (x & 7)];
     }
-
     // K part: chunk x = (row rho, chunk c) holds dims 16c..16c+15; c = 8 is padding.
-    const float inv_sk = 1.0f / sk;
-    for (int x = tid; x < F8_K_PART_CHUNKS; x += 256) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+        const int x = tid + i * 256;
         const int rho = x / F8_K_ROW_CHUNKS;
         const int c = x - rho * F8_K_ROW_CHUNKS;
         const int key = key0 + kperm(rho);
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (c < 8 && key < S) {
-            w = ksrc[(int64_t)key * 8 + c];
+        kw[i] = make_uint4(0, 0, 0, 0);
+        if (x < F8_K_PART_CHUNKS && c < 8 && key < S) {
+            kw[i] = ksrc[(int64_t)key * 8 + c];
             if (has_rope) {
-                float f[16];
-                fp8x4_to_f32(w.x, f);
-                fp8x4_to_f32(w.y, f + 4);
-                fp8x4_to_f32(w.z, f + 8);
-                fp8x4_to_f32(w.w, f + 12);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    float g[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) g[e] = f[8 * h + e] * k_scale;
-                    rotate4(g, cos_t[(int64_t)key * 16 + 2 * c + h], sin_t[(int64_t)key * 16 + 2 * c + h]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) f[8 * h + e] = clamp_e4m3(g[e] * inv_sk);
+                    cw[i][h] = cos_t[(int64_t)key * 16 + 2 * c + h];
+                    sw[i][h] = sin_t[(int64_t)key * 16 + 2 * c + h];
                 }
-                w = make_uint4(f32x4_to_fp8(f[0], f[1], f[2], f[3]), f32x4_to_fp8(f[4], f[5], f[6], f[7]),
-                               f32x4_to_fp8(f[8], f[9], f[10], f[11]), f32x4_to_fp8(f[12], f[13], f[14], f[15]));
             }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) vtile[tid + i * 256] = vw[i];
+
+    const float inv_sk = 1.0f / sk;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+        const int x = tid + i * 256;
+        if (x >= F8_K_PART_CHUNKS) break;
+        const int rho = x / F8_K_ROW_CHUNKS;
+        const int c = x - rho * F8_K_ROW_CHUNKS;
+        const int key = key0 + kperm(rho);
+        uint4 w = kw[i];
+        if (has_rope && c < 8 && key < S) {
+            float f[16];
+            fp8x4_to_f32(w.x, f);
+            fp8x4_to_f32(w.y, f + 4);
+            fp8x4_to_f32(w.z, f + 8);
+            fp8x4_to_f32(w.w, f + 12);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float g[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) g[e] = f[8 * h + e] * k_scale;
+                rotate4(g, cw[i][h], sw[i][h]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[8 * h + e] = clamp_e4m3(g[e] * inv_sk);
+            }
+            w = make_uint4(f32x4_to_fp8(f[0], f[1], f[2], f[3]), f32x4_to_fp8(f[4], f[5], f[6], f[7]),
+                           f32x4_to_fp8(f[8], f[9], f[10], f[11]), f32x4_to_fp8(f[12], f[13], f[14], f[15]));
         }
         dst[x] = w;
     }
