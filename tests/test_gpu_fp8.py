@@ -153,3 +153,18 @@ def test_fp8_bitwise_repeatable_full_size():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_fp8_longest_supported_sequence():
+    """S = 2^21 on the fp8 path (one head): the last fp8 tiles sit just below
+    the 32-bit byte offsets of the tile addressing.  Sampled rows, including
+    the last tile's."""
+    torch = _torch()
+    import dit_joint_self_amd as dj
+    w = W.Workload("max8", B=1, H=1, D=128, S_txt=0, grid=(1, 1024, 2048), axes_dim=(16, 56, 56), theta=10000.0,
+                   seed=2022)
+    assert w.S == 2 ** 21
+    qkv8 = _quantized(w)
+    got_all = _run(w, qkv8)
+    rows = np.unique(np.concatenate([sample_rows(w.S, 0, 16, seed=4), [2 ** 20, w.S - 64, w.S - 2, w.S - 1]]))
+    _assert_close(got_all[:, :, rows], _oracle(w, qkv8, rows=rows), f"fp8 S=2^21 ({len(rows)} rows)")
