@@ -40,7 +40,7 @@ MEASURED_TRAFFIC = {
     ("9cce712c3c61e9a3", "flux2048"): {"read_bytes": 1102.4e6, "write_bytes": 210.1e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
     # dit_attn_core_fp8 (attn_core_fp8_kernel x 2 + attn_merge_kernel), hash over FP8_SOURCES
-    ("60d2a37d1dfa2ccd", "flux2048_fp8"): {"read_bytes": 694.2e6, "write_bytes": 136.1e6,
+    ("8098e771b4c22bc2", "flux2048_fp8"): {"read_bytes": 694.2e6, "write_bytes": 136.1e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
     ("69dde4a003be8d54", "flux2048_qkv"): {"read_bytes": 435.7e6, "write_bytes": 331.1e6,

@@ -16,9 +16,11 @@
 //     rescaled) only when a lane's step weights sum past 16 * 24, which keeps
 //     every p' below 448.  l sums the fp32 p'; O = O_acc * v_scale / l.
 //
-// Work per workgroup, tile stream, split plan and merge are the bf16 kernel's
-// (attn_common.h).  Per 64-key tile a wave issues 4 QK^T and 4 PV MFMAs of
-// 32x32x64 (2 * 32 * 32 * 64 flop each).  Roofline: MFMA bound (fp8 peak).
+// Work per workgroup, split plan and merge are the bf16 kernel's
+// (attn_common.h).  The tile stream double-buffers whole 19 KiB tiles (K'
+// then V^T), each copied one tile ahead.  Per 64-key tile a wave issues 4
+// QK^T and 4 PV MFMAs of 32x32x64 (2 * 32 * 32 * 64 flop each).  Roofline:
+// MFMA bound (fp8 peak).
 
 #include <hip/hip_runtime.h>
 
