@@ -463,3 +463,13 @@ def test_residual_diff_matches_brute_force():
     rng = np.random.default_rng(47)
     p, c = rng.standard_normal(257), rng.standard_normal(257)
     assert abs(residual_diff(p, c) - brute.residual_diff(p.tolist(), c.tolist())) <= 1e-14
+
+
+def test_residual_diff_nan_and_size_mismatch():
+    from oracle.dbcache import can_reuse, residual_diff
+    p = np.ones(64)
+    c = np.ones(64)
+    c[5] = np.nan
+    assert math.isnan(residual_diff(p, c)) and not can_reuse(p, c, 1e300)
+    with pytest.raises(ValueError):
+        residual_diff(np.ones(3), np.ones(4))
