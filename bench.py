@@ -37,7 +37,7 @@ FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/
 KERNEL_SOURCES = BF16_SOURCES
 MEASURED_TRAFFIC = {
     # dit_attn_core (attn_core_kernel x 2 + attn_merge_kernel), hash over BF16_SOURCES
-    ("9cce712c3c61e9a3", "flux2048"): {"read_bytes": 1102.4e6, "write_bytes": 210.1e6,
+    ("cf783401a4ff5820", "flux2048"): {"read_bytes": 1086.7e6, "write_bytes": 140.1e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
     # dit_attn_core_fp8 (attn_core_fp8_kernel x 2 + attn_merge_kernel), hash over FP8_SOURCES
     ("8098e771b4c22bc2", "flux2048_fp8"): {"read_bytes": 694.2e6, "write_bytes": 136.1e6,

@@ -89,6 +89,11 @@ __device__ __forceinline__ void weight_pair(const f32x16 (&sc)[2], int p, uint32
     const int r = 2 * (p & 7);
     w[p] = pack_bf16x2(__builtin_amdgcn_exp2f(a[r]), __builtin_amdgcn_exp2f(a[r + 1]));
     sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[p]), ones, sum, false);
+    // Pin the pair here.  The steps that issue tile copies end in a branch;
+    // without the pin the compiler sinks those steps' exp2 work past the
+    // branches and runs it in one burst after the last copy, instead of one
+    // pair beside each score MFMA.  The empty asm emits no instruction.
+    asm volatile("" : "+v"(w[p]), "+v"(sum));
 }
 
 // The tile copies one pipelined step issues, spread over stage A: piece j of
