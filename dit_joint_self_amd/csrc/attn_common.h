@@ -89,8 +89,11 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, int sof
 
 // How one call is laid out over the GPU: `full` items run whole-key-range
 // workgroups in full rounds; the remaining `split` items (fewer than a round)
-// run nsplit key-range workgroups each, merged afterwards.  Depends only on the
-// shape, so the workspace size is known on the host.
+// run nsplit key-range workgroups each, merged afterwards.  Both kinds share
+// one launch, whole-range workgroups first, so a CU that finishes its last
+// whole item early takes a key-range piece instead of idling until the
+// slowest workgroup of the round ends.  Depends only on the shape, so the
+// workspace size is known on the host.
 struct CorePlan {
     int nqt, ntiles, items, full, split, nsplit;
 };
@@ -113,6 +116,38 @@ inline CorePlan core_plan(int BH, int S) {
     }
     return p;
 }
+
+// The work of workgroup x of the combined launch.  Whole-range workgroups
+// [0, full) map through xcd_remap as before; key-range pieces [full, grid)
+// map through their own xcd_remap (full is a multiple of 8, so piece x - full
+// sits on the same XCD as workgroup x), which spreads the pieces evenly over
+// the XCDs.  Piece p covers key range p % nsplit of item full + p / nsplit,
+// the order the merge reads the partials in.
+struct CoreWork {
+    int item, f, nsplit, piece;
+    bool partial;
+};
+
+__device__ __forceinline__ CoreWork core_work(int x, int grid, int full, int nsplit) {
+    CoreWork w;
+    if (x < full) {
+        w.item = xcd_remap(x, full);
+        w.f = 0;
+        w.nsplit = 1;
+        w.piece = 0;
+        w.partial = false;
+    } else {
+        const int p = xcd_remap(x - full, grid - full);
+        w.item = full + p / nsplit;
+        w.f = p - (p / nsplit) * nsplit;
+        w.nsplit = nsplit;
+        w.piece = p;
+        w.partial = true;
+    }
+    return w;
+}
+
+inline int core_grid(const CorePlan& p) { return p.full + p.split * p.nsplit; }
 
 inline size_t core_partial_bytes_for(const CorePlan& p) {
     return (size_t)p.split * p.nsplit * PART_FLOATS * sizeof(float);

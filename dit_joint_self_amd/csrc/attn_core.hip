@@ -243,14 +243,13 @@ __device__ __forceinline__ void tile_step_last(const uint4* vt, f32x16 (&sc)[2],
 }
 
 // One workgroup = BM queries of one (batch, head) against the key tiles
-// [tb, te).  Items item0 + i / nsplit, key range i % nsplit of nsplit equal
-// ranges.  PARTIAL = false: the whole key range, normalised bf16 output.
-// PARTIAL = true: unnormalised O, m and l of the range to `part`.
-template <bool PARTIAL>
+// [tb, te) (core_work: whole-range items first, then the key-range pieces of
+// the `split` items).  Whole range: normalised bf16 output.  Key range:
+// unnormalised O, m and l of the range to `part`, merged afterwards.
 __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const uint4* __restrict__ q, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
     const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, int S,
-    int ntiles, int nqt, int item0, int nsplit, float qmul, int has_rope) {
+    int ntiles, int nqt, int full, int nsplit, float qmul, int has_rope) {
     static_assert(QB == 1, "one 32-query block per wave");
     // K' parts run one tile ahead of V^T parts, each through its own pair of
     // buffers: step i reads K'(i + 1) and V^T(i) while K'(i + 2) and V^T(i + 1)
@@ -261,13 +260,11 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     __shared__ uint4 vb0[V_PART_CHUNKS];
     __shared__ uint4 vb1[V_PART_CHUNKS];
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int item = item0 + logical / nsplit;
-    const int f = logical - (logical / nsplit) * nsplit;
-    const int64_t bh = item / nqt;
-    const int qt = item - (int)bh * nqt;
-    const int tb = (int)((int64_t)f * ntiles / nsplit);
-    const int te = (int)((int64_t)(f + 1) * ntiles / nsplit);
+    const CoreWork cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
+    const int64_t bh = cw.item / nqt;
+    const int qt = cw.item - (int)bh * nqt;
+    const int tb = (int)((int64_t)cw.f * ntiles / cw.nsplit);
+    const int te = (int)((int64_t)(cw.f + 1) * ntiles / cw.nsplit);
     const int nt = te - tb;  // >= 1
 
     const int lane = threadIdx.x & 63;
@@ -302,19 +299,32 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const int rloc = wave * 32 + n;
     const int row = qt * BM + rloc;
     {
+        // Every load of the lane is issued before any is used (rows past S
+        // read row S - 1 and are zeroed afterwards), so the prologue waits for
+        // one memory latency instead of one per chunk.
         const bool ok = row < S;
-        const uint4* qrow = q + (bh * S + row) * 16;
+        const int64_t rr = ok ? row : S - 1;
+        const uint4* qrow = q + (bh * S + rr) * 16;
+        uint4 qw[8];
+        float4 cw[8], sw[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qw[t] = qrow[2 * t + hh];
+        if (has_rope) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                cw[t] = cos_t[rr * 16 + 2 * t + hh];
+                sw[t] = sin_t[rr * 16 + 2 * t + hh];
+            }
+        }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const int c = 2 * t + hh;
             float fv[8];
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (ok) w = qrow[c];
-            unpack8(w, fv);
-            if (has_rope && ok) rotate4(fv, cos_t[(int64_t)row * 16 + c], sin_t[(int64_t)row * 16 + c]);
+            unpack8(qw[t], fv);
+            if (has_rope) rotate4(fv, cw[t], sw[t]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) fv[e] *= qmul;
-            qf[t] = as_bf16x8(pack8(fv));
+            const uint4 pk = pack8(fv);
+            qf[t] = as_bf16x8(ok ? pk : make_uint4(0, 0, 0, 0));
         }
     }
 
@@ -369,8 +379,8 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     // ---- epilogue: lane (n, hh), register r of dim block db holds dim
     // 32 db + 8 (r >> 2) + 4 hh + (r & 3) of query n.
     const float l = swap_halves_sum(lsum);
-    if (PARTIAL) {
-        float* pw = part + (int64_t)logical * PART_FLOATS;
+    if (cw.partial) {
+        float* pw = part + (int64_t)cw.piece * PART_FLOATS;
         float4* prow = reinterpret_cast<float4*>(pw + (int64_t)rloc * HEAD_DIM);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -449,16 +459,10 @@ hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_
     const float4* cv = reinterpret_cast<const float4*>(cos_t);
     const float4* sv = reinterpret_cast<const float4*>(sin_t);
     const int rope = cos_t != nullptr;
-    if (p.full > 0) {
-        attn_core_kernel<false><<<p.full, NW * 64, 0, stream>>>(qv, cv, sv, wsv, static_cast<uint2*>(out), lse,
-                                                               nullptr, S, p.ntiles, p.nqt, 0, 1, qmul, rope);
-    }
-    if (p.split > 0) {
-        float* pt = static_cast<float*>(part);
-        attn_core_kernel<true><<<p.split * p.nsplit, NW * 64, 0, stream>>>(
-            qv, cv, sv, wsv, nullptr, nullptr, pt, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
-        launch_merge(pt, out, lse, S, p.nqt, p.full, p.nsplit, p.split, stream);
-    }
+    float* pt = static_cast<float*>(part);
+    attn_core_kernel<<<core_grid(p), NW * 64, 0, stream>>>(qv, cv, sv, wsv, static_cast<uint2*>(out), lse, pt, S,
+                                                          p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
+    if (p.split > 0) launch_merge(pt, out, lse, S, p.nqt, p.full, p.nsplit, p.split, stream);
     return hipGetLastError();
 }
 

@@ -144,21 +144,18 @@ __device__ __forceinline__ void f8_tile(const uint4* kt, int j, bool first, int 
     }
 }
 
-template <bool PARTIAL>
 __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     const uint4* __restrict__ q, float q_scale, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
     const uint8_t* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ part, int S, int ntiles, int nqt,
-    int item0, int nsplit, float qmul, int has_rope) {
+    int full, int nsplit, float qmul, int has_rope) {
     __shared__ uint4 lds0[F8_TILE_CHUNKS];
     __shared__ uint4 lds1[F8_TILE_CHUNKS];
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int item = item0 + logical / nsplit;
-    const int f = logical - (logical / nsplit) * nsplit;
-    const int64_t bh = item / nqt;
-    const int qt = item - (int)bh * nqt;
-    const int tb = (int)((int64_t)f * ntiles / nsplit);
-    const int te = (int)((int64_t)(f + 1) * ntiles / nsplit);
+    const CoreWork cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
+    const int64_t bh = cw.item / nqt;
+    const int qt = cw.item - (int)bh * nqt;
+    const int tb = (int)((int64_t)cw.f * ntiles / cw.nsplit);
+    const int te = (int)((int64_t)(cw.f + 1) * ntiles / cw.nsplit);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -181,17 +178,30 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     const int qscale = E8M0_ONE + e;
     i32x8 qf[2];
     {
+        // Every load of the lane is issued before any is used (rows past S
+        // read row S - 1 and are zeroed afterwards).
         const int row = qt * BM + wave * 32 + n;
         const bool ok = row < S;
-        const uint4* qrow = q + (bh * S + row) * 8;
+        const int64_t rr = ok ? row : S - 1;
+        const uint4* qrow = q + (bh * S + rr) * 8;
+        uint4 qw[4];
+        float4 cw[8], sw[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qw[i] = qrow[(i >> 1) * 4 + hh * 2 + (i & 1)];
+        if (has_rope) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = ((i >> 2) * 4 + hh * 2 + ((i >> 1) & 1));
+                cw[i] = cos_t[rr * 16 + 2 * c + (i & 1)];
+                sw[i] = sin_t[rr * 16 + 2 * c + (i & 1)];
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                // dims 64 kk + 32 hh + 16 h .. +15: chunk c of the row
-                const int c = kk * 4 + hh * 2 + h;
-                uint4 w = make_uint4(0, 0, 0, 0);
-                if (ok) w = qrow[c];
+                // dims 64 kk + 32 hh + 16 h .. +15: chunk kk * 4 + hh * 2 + h of the row
+                const uint4 w = qw[2 * kk + h];
                 float fv[16];
                 fp8x4_to_f32(w.x, fv);
                 fp8x4_to_f32(w.y, fv + 4);
@@ -202,14 +212,15 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
                     float t[8];
 #pragma unroll
                     for (int x = 0; x < 8; ++x) t[x] = fv[8 * g + x] * q_scale;
-                    if (has_rope && ok)
-                        rotate4(t, cos_t[(int64_t)row * 16 + 2 * c + g], sin_t[(int64_t)row * 16 + 2 * c + g]);
+                    if (has_rope) rotate4(t, cw[4 * kk + 2 * h + g], sw[4 * kk + 2 * h + g]);
 #pragma unroll
                     for (int x = 0; x < 8; ++x) fv[8 * g + x] = clamp_e4m3(t[x] * qfac);
                 }
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    qf[kk][4 * h + x] = (int)f32x4_to_fp8(fv[4 * x], fv[4 * x + 1], fv[4 * x + 2], fv[4 * x + 3]);
+                for (int x = 0; x < 4; ++x) {
+                    const int code = (int)f32x4_to_fp8(fv[4 * x], fv[4 * x + 1], fv[4 * x + 2], fv[4 * x + 3]);
+                    qf[kk][4 * h + x] = ok ? code : 0;
+                }
             }
         }
     }
@@ -248,8 +259,8 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     const float l = swap_halves_sum(lsum);
     const int rloc = wave * 32 + n;
     const int row = qt * BM + rloc;
-    if (PARTIAL) {
-        float* pw = part + (int64_t)logical * PART_FLOATS;
+    if (cw.partial) {
+        float* pw = part + (int64_t)cw.piece * PART_FLOATS;
         float4* prow = reinterpret_cast<float4*>(pw + (int64_t)rloc * HEAD_DIM);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -283,15 +294,10 @@ hipError_t launch_attn_core_fp8(const void* q, float q_scale, const float* cos_t
     const float4* cv = reinterpret_cast<const float4*>(cos_t);
     const float4* sv = reinterpret_cast<const float4*>(sin_t);
     const int rope = cos_t != nullptr;
-    if (p.full > 0)
-        attn_core_fp8_kernel<false><<<p.full, NW * 64, 0, stream>>>(qv, q_scale, cv, sv, wsv, static_cast<uint2*>(out),
-                                                                   nullptr, S, p.ntiles, p.nqt, 0, 1, qmul, rope);
-    if (p.split > 0) {
-        float* pt = static_cast<float*>(part);
-        attn_core_fp8_kernel<true><<<p.split * p.nsplit, NW * 64, 0, stream>>>(
-            qv, q_scale, cv, sv, wsv, nullptr, pt, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
-        launch_merge(pt, out, nullptr, S, p.nqt, p.full, p.nsplit, p.split, stream);
-    }
+    float* pt = static_cast<float*>(part);
+    attn_core_fp8_kernel<<<core_grid(p), NW * 64, 0, stream>>>(qv, q_scale, cv, sv, wsv, static_cast<uint2*>(out), pt,
+                                                              S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
+    if (p.split > 0) launch_merge(pt, out, nullptr, S, p.nqt, p.full, p.nsplit, p.split, stream);
     return hipGetLastError();
 }
 
