@@ -36,17 +36,17 @@ FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/
                "dit_joint_self_amd/csrc/fp8_util.h"]
 KERNEL_SOURCES = BF16_SOURCES
 MEASURED_TRAFFIC = {
-    # dit_attn_core (attn_core_kernel x 2 + attn_merge_kernel), hash over BF16_SOURCES
-    ("cf783401a4ff5820", "flux2048"): {"read_bytes": 1086.7e6, "write_bytes": 140.1e6,
+    # dit_attn_core (attn_core_kernel + attn_merge_kernel), hash over BF16_SOURCES
+    ("b4694ae1c6a80199", "flux2048"): {"read_bytes": 1085.9e6, "write_bytes": 139.7e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
-    # dit_attn_core_fp8 (attn_core_fp8_kernel x 2 + attn_merge_kernel), hash over FP8_SOURCES
-    ("8098e771b4c22bc2", "flux2048_fp8"): {"read_bytes": 694.2e6, "write_bytes": 136.1e6,
+    # dit_attn_core_fp8 (attn_core_fp8_kernel + attn_merge_kernel), hash over FP8_SOURCES
+    ("db74dc36e77b537b", "flux2048_fp8"): {"read_bytes": 693.1e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
-    ("69dde4a003be8d54", "flux2048_qkv"): {"read_bytes": 435.7e6, "write_bytes": 331.1e6,
+    ("53fc4bb69245cb6f", "flux2048_qkv"): {"read_bytes": 435.4e6, "write_bytes": 331.1e6,
                                            "profile": "profiles/mxfp4_gemm_flux2048_qkv.md"},
     # residual_diff_partials + residual_diff_finish (hash over RESIDUAL_SOURCES)
-    ("c4af6b56612c2ae2", "flux2048_residual"): {"read_bytes": 207.80e6, "write_bytes": 0.26e6,
+    ("5f471859585fa951", "flux2048_residual"): {"read_bytes": 207.80e6, "write_bytes": 0.26e6,
                                                 "profile": "profiles/dbcache_residual_diff_flux2048.md"},
 }
 
@@ -550,7 +550,7 @@ def main():
         "pct_of_peak": 100.0 * flops / (step_ms * 1e-3) / 1e12 / peak,
         "roofline": {"bound": "mfma",
                      "kernel": ("dit_attn_core_fp8: attn_core_fp8_kernel" if fp8 else "dit_attn_core: attn_core_kernel")
-                               + " (whole-range and key-range launches) + attn_merge_kernel",
+                               + " (whole-range workgroups and key-range pieces, one launch) + attn_merge_kernel",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "traffic_unit": "HBM bytes per dit_attn_core call (read + write)",
                      "hbm_GBps": None if traffic is None else traffic / (core_avg * 1e-3) / 1e9,
