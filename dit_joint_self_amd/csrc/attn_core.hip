@@ -462,8 +462,9 @@ hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_
     float* pt = static_cast<float*>(part);
     attn_core_kernel<<<core_grid(p), NW * 64, 0, stream>>>(qv, cv, sv, wsv, static_cast<uint2*>(out), lse, pt, S,
                                                           p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
-    if (p.split > 0) launch_merge(pt, out, lse, S, p.nqt, p.full, p.nsplit, p.split, stream);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && p.split > 0) e = launch_merge(pt, out, lse, S, p.nqt, p.full, p.nsplit, p.split, stream);
+    return e;
 }
 
 }  // namespace dit

@@ -297,8 +297,9 @@ hipError_t launch_attn_core_fp8(const void* q, float q_scale, const float* cos_t
     float* pt = static_cast<float*>(part);
     attn_core_fp8_kernel<<<core_grid(p), NW * 64, 0, stream>>>(qv, q_scale, cv, sv, wsv, static_cast<uint2*>(out), pt,
                                                               S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
-    if (p.split > 0) launch_merge(pt, out, nullptr, S, p.nqt, p.full, p.nsplit, p.split, stream);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && p.split > 0) e = launch_merge(pt, out, nullptr, S, p.nqt, p.full, p.nsplit, p.split, stream);
+    return e;
 }
 
 }  // namespace dit

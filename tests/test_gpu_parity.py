@@ -165,6 +165,22 @@ def test_ragged_and_small_shapes(S_txt, grid, B, H):
         assert np.array_equal(got, bf16_f64(vb))
 
 
+def test_whole_ranges_and_key_range_pieces_in_one_launch():
+    """37 heads x ceil(1800 / 256) = 296 (head, query-tile) items: 256 whole-range
+    workgroups and 40 items split over 6 key ranges (240 pieces) share one
+    launch; the last query tile holds 8 rows and the last key tile 8 keys.
+    Every output row is compared with the oracle."""
+    w = _small(0, (30, 60), B=1, H=37, seed=1800)
+    items = w.B * w.H * math.ceil(w.S / 256)
+    rem = items % 256
+    assert (items, rem, min(256 // rem, math.ceil(w.S / 64))) == (296, 40, 6)
+    qb, kb, vb = W.make_bf16_inputs(w)
+    want = _oracle(w, qb, kb, vb)
+    for split in (False, True):
+        got = _run(w, qb, kb, vb, split=split)
+        _assert_close(got, want, f"S={w.S} H={w.H} split={split}")
+
+
 def test_no_rope_three_axis():
     w = W.get("tiny").with_(grid=(2, 8, 16), axes_dim=(16, 56, 56), H=2)
     qb, kb, vb = W.make_bf16_inputs(w)
