@@ -17,12 +17,17 @@
 //     every p' below 448.  l sums the fp32 p'; O = O_acc * v_scale / l.
 //
 // Work per workgroup, split plan and merge are the bf16 kernel's
-// (attn_common.h).  The tile stream double-buffers whole 19 KiB tiles (K'
-// then V^T), each copied one tile ahead.  Per 64-key tile a wave issues 4
-// QK^T and 4 PV MFMAs of 32x32x64 (2 * 32 * 32 * 64 flop each).  Roofline:
+// (attn_common.h).  Whole 19 KiB tiles (K' then V^T) stream through three
+// LDS buffers, each copied one tile ahead.  Per 64-key tile a wave issues 4
+// QK^T and 4 PV MFMAs of 32x32x64 (2 * 32 * 32 * 64 flop each), and between
+// them the exp2 / e4m3 work that needs the QK^T result and feeds PV.  The two
+// waves of each SIMD belong to two groups that run half a tile apart (see
+// the kernel), so one wave's exp2 work meets the other's MFMAs.  Roofline:
 // MFMA bound (fp8 peak).
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "attn_common.h"
 #include "bf16_util.h"
@@ -68,10 +73,12 @@ __device__ __forceinline__ void f8_weights(const f32x16 (&s)[2], i32x8& pf, floa
     sum = t0 + t1;
 }
 
+// First half of a tile: scores from the K' part kt, then the e4m3 weights
+// (returned in PV B-operand order) with the offset bookkeeping.
 template <bool MASKED>
-__device__ __forceinline__ void f8_tile(const uint4* kt, int j, bool first, int S, int n, int hh, int qscale,
-                                        const i32x8 (&qf)[2], f32x16 (&o)[4], f32x16& negm, float& lsum) {
-    const uint4* vt = kt + F8_K_PART_CHUNKS;
+__device__ __forceinline__ i32x8 f8_scores_weights(const uint4* kt, int j, bool first, int S, int n, int hh,
+                                                   int qscale, const i32x8 (&qf)[2], f32x16 (&o)[4], f32x16& negm,
+                                                   float& lsum) {
 
     // ---- S'^T = K' Q''^T * 2^e - m + 4: per key block kb, two 64-dim steps.
     f32x16 s[2];
@@ -126,7 +133,11 @@ __device__ __forceinline__ void f8_tile(const uint4* kt, int j, bool first, int 
         f8_weights(s, pf, tsum);
     }
     lsum += tsum;
+    return pf;
+}
 
+// Second half: O^T += V^T P'^T from the V^T part vt.
+__device__ __forceinline__ void f8_pv(const uint4* vt, const i32x8& pf, f32x16 (&o)[4], int n, int hh) {
     // ---- O^T += V^T P'^T: four 32-dim blocks, 64 keys each.
     {
         i32x8 a[4];
@@ -148,8 +159,11 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     const uint4* __restrict__ q, float q_scale, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
     const uint8_t* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ part, int S, int ntiles, int nqt,
     int full, int nsplit, float qmul, int has_rope) {
+    // Tile k of the range lives in buf[k % 3] (see the two wave groups below).
     __shared__ uint4 lds0[F8_TILE_CHUNKS];
     __shared__ uint4 lds1[F8_TILE_CHUNKS];
+    __shared__ uint4 lds2[F8_TILE_CHUNKS];
+    uint4* const buf[3] = {lds0, lds1, lds2};
 
     const CoreWork cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
     const int64_t bh = cw.item / nqt;
@@ -230,28 +244,86 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
 
-    const int last = te - 1;
-    int j = tb;
-    for (; j + 2 <= last; j += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (j + 1) * F8_TILE_BYTES, lds1, wv, lane);
-        f8_tile<false>(lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (j + 2) * F8_TILE_BYTES, lds0, wv, lane);
-        f8_tile<false>(lds1, j + 1, false, S, n, hh, qscale, qf, o, negm, lsum);
-    }
-    if (j < last) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (j + 1) * F8_TILE_BYTES, lds1, wv, lane);
-        f8_tile<false>(lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
-        ++j;
-    }
+    // Each tile is QK^T MFMAs, then exp2 / e4m3 work that needs their result,
+    // then the PV MFMAs.  Two wave groups, one wave of each per SIMD, run half
+    // a tile apart so that one wave's exp2 work meets the other wave's MFMAs.
+    // With L = nt - 1 and barriers 0..L+1, the interval after barrier k holds
+    //   group 0 (waves 0..NW/2-1): scores + weights of tile k, PV of tile k
+    //   group 1 (the other waves):  PV of tile k - 1, scores + weights of tile k
+    // so tiles k - 1 and k are read in it; the copy of tile k + 1 issued in it
+    // goes to the buffer of tile k - 2, which both groups finished before the
+    // barrier.  Both groups pass the same L + 2 barriers; group 1 carries the
+    // weights of a tile across one.
+    const int L = te - 1 - tb;
+    const bool g1 = wv >= NW / 2;
+    // The range's last tile (masked) is kept out of the loops, whose steps
+    // then all look the same to the register allocator.
+    using full_t = std::false_type;
+    using last_t = std::true_type;
+    auto scores_weights = [&](const uint4* kt, int k, auto lastc) __attribute__((always_inline)) {
+        return f8_scores_weights<decltype(lastc)::value>(kt, tb + k, k == 0, S, n, hh, qscale, qf, o, negm, lsum);
+    };
+    auto copy_tile = [&](int k, uint4* dst) __attribute__((always_inline)) {
+        if (k <= L) copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, (tb + k) * F8_TILE_BYTES, dst, wv, lane);
+    };
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    f8_tile<true>(((j - tb) & 1) ? lds1 : lds0, j, j == tb, S, n, hh, qscale, qf, o, negm, lsum);
+    if (!g1) {
+        auto step = [&](auto rc, int k, auto lastc) __attribute__((always_inline)) {
+            constexpr int R = decltype(rc)::value;  // k % 3
+            copy_tile(k + 1, buf[(R + 1) % 3]);
+            const i32x8 pf = scores_weights(buf[R], k, lastc);
+            f8_pv(buf[R] + F8_K_PART_CHUNKS, pf, o, n, hh);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        };
+        for (int k = 0;;) {
+            if (k >= L) break;
+            step(std::integral_constant<int, 0>{}, k++, full_t{});
+            if (k >= L) break;
+            step(std::integral_constant<int, 1>{}, k++, full_t{});
+            if (k >= L) break;
+            step(std::integral_constant<int, 2>{}, k++, full_t{});
+        }
+        switch (L % 3) {
+            case 0: step(std::integral_constant<int, 0>{}, L, last_t{}); break;
+            case 1: step(std::integral_constant<int, 1>{}, L, last_t{}); break;
+            default: step(std::integral_constant<int, 2>{}, L, last_t{}); break;
+        }
+    } else {
+        copy_tile(1, lds1);
+        i32x8 pf = L == 0 ? scores_weights(lds0, 0, last_t{}) : scores_weights(lds0, 0, full_t{});
+        auto step = [&](auto rc, int k, auto lastc) __attribute__((always_inline)) {
+            constexpr int R = decltype(rc)::value;  // k % 3
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            copy_tile(k + 1, buf[(R + 1) % 3]);
+            f8_pv(buf[(R + 2) % 3] + F8_K_PART_CHUNKS, pf, o, n, hh);
+            pf = scores_weights(buf[R], k, lastc);
+        };
+        for (int k = 1;;) {
+            if (k >= L) break;
+            step(std::integral_constant<int, 1>{}, k++, full_t{});
+            if (k >= L) break;
+            step(std::integral_constant<int, 2>{}, k++, full_t{});
+            if (k >= L) break;
+            step(std::integral_constant<int, 0>{}, k++, full_t{});
+        }
+        if (L > 0) {
+            switch (L % 3) {
+                case 0: step(std::integral_constant<int, 0>{}, L, last_t{}); break;
+                case 1: step(std::integral_constant<int, 1>{}, L, last_t{}); break;
+                default: step(std::integral_constant<int, 2>{}, L, last_t{}); break;
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        switch (L % 3) {
+            case 0: f8_pv(lds0 + F8_K_PART_CHUNKS, pf, o, n, hh); break;
+            case 1: f8_pv(lds1 + F8_K_PART_CHUNKS, pf, o, n, hh); break;
+            default: f8_pv(lds2 + F8_K_PART_CHUNKS, pf, o, n, hh); break;
+        }
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) settle(o[db]);
 
