@@ -37,10 +37,10 @@ FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/
 KERNEL_SOURCES = BF16_SOURCES
 MEASURED_TRAFFIC = {
     # dit_attn_core (attn_core_kernel + attn_merge_kernel), hash over BF16_SOURCES
-    ("b4694ae1c6a80199", "flux2048"): {"read_bytes": 1085.9e6, "write_bytes": 139.7e6,
+    ("08ecc11c62c0a419", "flux2048"): {"read_bytes": 1085.4e6, "write_bytes": 139.7e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
     # dit_attn_core_fp8 (attn_core_fp8_kernel + attn_merge_kernel), hash over FP8_SOURCES
-    ("db74dc36e77b537b", "flux2048_fp8"): {"read_bytes": 693.1e6, "write_bytes": 135.8e6,
+    ("fcb8c44a21eaceec", "flux2048_fp8"): {"read_bytes": 693.5e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
     ("53fc4bb69245cb6f", "flux2048_qkv"): {"read_bytes": 435.4e6, "write_bytes": 331.1e6,
