@@ -89,7 +89,7 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, int sof
 
 // How one call is laid out over the GPU: `full` items run whole-key-range
 // workgroups in full rounds; the remaining `split` items (fewer than a round)
-// run nsplit key-range workgroups each, merged afterwards.  Both kinds share
+// run nsplit key-range workgroups each (core_split), merged afterwards.  Both kinds share
 // one launch, whole-range workgroups first, so a CU that finishes its last
 // whole item early takes a key-range piece instead of idling until the
 // slowest workgroup of the round ends.  Depends only on the shape, so the
@@ -98,13 +98,32 @@ struct CorePlan {
     int nqt, ntiles, items, full, split, nsplit;
 };
 
+// Number of key ranges for the r leftover items: the F in [1, min(8, ntiles)]
+// that minimises ceil(r F / 256) rounds of pieces of 1/F item each, plus a
+// fixed cost per piece of 1/32 item (prologue, partial write, merge):
+// cost(F) = ceil(r F / 256) (32 + F) / (32 F); ties go to the smaller F.
+inline int core_split(int rem, int ntiles) {
+    int best = 1;
+    int64_t best_num = 33, best_den = 32;  // cost(1) = 1 round x 33/32
+    for (int f = 2; f <= std::min(8, ntiles); ++f) {
+        const int64_t rounds = ((int64_t)rem * f + MI355X_CUS - 1) / MI355X_CUS;
+        const int64_t num = rounds * (32 + f), den = 32 * (int64_t)f;
+        if (num * best_den < best_num * den) {
+            best = f;
+            best_num = num;
+            best_den = den;
+        }
+    }
+    return best;
+}
+
 inline CorePlan core_plan(int BH, int S) {
     CorePlan p;
     p.ntiles = (int)num_kv_tiles(S);
     p.nqt = (S + BM - 1) / BM;
     p.items = BH * p.nqt;
     const int rem = p.items % MI355X_CUS;
-    const int f = rem ? std::min(MI355X_CUS / rem, p.ntiles) : 1;
+    const int f = rem ? core_split(rem, p.ntiles) : 1;
     if (rem == 0 || f < 2) {
         p.full = p.items;
         p.split = 0;
