@@ -30,10 +30,11 @@ METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=16896,H=24,D=128 (1 GPU
 # plain-copy calibration), keyed by the hash of the sources of the kernel they were taken on
 # and by workload; reported as roofline.traffic only while those sources are unchanged.
 BF16_SOURCES = ["dit_joint_self_amd/csrc/attn_core.hip", "dit_joint_self_amd/csrc/attn_common.h",
-                "dit_joint_self_amd/csrc/tile_layout.h", "dit_joint_self_amd/csrc/bf16_util.h"]
+                "dit_joint_self_amd/csrc/gfx950.h", "dit_joint_self_amd/csrc/tile_layout.h",
+                "dit_joint_self_amd/csrc/bf16_util.h"]
 FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/csrc/attn_common.h",
-               "dit_joint_self_amd/csrc/tile_layout.h", "dit_joint_self_amd/csrc/bf16_util.h",
-               "dit_joint_self_amd/csrc/fp8_util.h"]
+               "dit_joint_self_amd/csrc/gfx950.h", "dit_joint_self_amd/csrc/tile_layout.h",
+               "dit_joint_self_amd/csrc/bf16_util.h", "dit_joint_self_amd/csrc/fp8_util.h"]
 KERNEL_SOURCES = BF16_SOURCES
 MEASURED_TRAFFIC = {
     # dit_attn_core (attn_core_kernel + attn_merge_kernel), hash over BF16_SOURCES
@@ -51,9 +52,9 @@ MEASURED_TRAFFIC = {
 }
 
 
-MXFP4_SOURCES = ["dit_joint_self_amd/csrc/mxfp4.hip", "dit_joint_self_amd/csrc/attn_common.h",
+MXFP4_SOURCES = ["dit_joint_self_amd/csrc/mxfp4.hip", "dit_joint_self_amd/csrc/gfx950.h",
                  "dit_joint_self_amd/csrc/bf16_util.h"]
-RESIDUAL_SOURCES = ["dit_joint_self_amd/csrc/dbcache.hip", "dit_joint_self_amd/csrc/attn_common.h"]
+RESIDUAL_SOURCES = ["dit_joint_self_amd/csrc/dbcache.hip", "dit_joint_self_amd/csrc/gfx950.h"]
 
 
 def kernel_sources_hash(files=None) -> str:

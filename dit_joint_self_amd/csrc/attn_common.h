@@ -1,12 +1,13 @@
 // attn_common.h - pieces shared by the bf16 and fp8 attention kernels:
-// workgroup shape, launch plan, key-range partial format, XCD-aware workgroup
-// order, direct-to-LDS copies and the half-wave reductions.
+// workgroup shape, launch plan and key-range partial format (the gfx950
+// helpers they build on are in gfx950.h).
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 
+#include "gfx950.h"
 #include "tile_layout.h"
 
 namespace dit {
@@ -14,17 +15,7 @@ namespace dit {
 constexpr int NW = 8;                 // waves per workgroup (two per SIMD)
 constexpr int QB = 1;                 // 32-query blocks per wave
 constexpr int BM = NW * 32 * QB;      // queries per workgroup
-constexpr int MI355X_CUS = 256;       // workgroups resident at once (one per CU)
 constexpr float LN2 = 0.693147180559945309f;
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));   // one 32x32 MFMA accumulator
-
-// Materialise an accumulator here, with every lane active.  An MFMA reads its
-// operands from all 64 lanes; if the compiler sank the last products into a
-// branch taken by only some lanes (the store guard row < S of the epilogue),
-// the inactive lanes' operand rows would be lost.  The empty volatile asm
-// reads and writes the value, so every product feeding it stays before it.
-__device__ __forceinline__ void settle(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 // Longest sequence the kernels accept: keeps every byte offset inside one
 // (batch, head) slice of prepared tiles below 2^31.
@@ -34,58 +25,6 @@ static_assert((int64_t)((MAX_SEQ + KV_TILE - 1) / KV_TILE) * TILE_BYTES < (int64
 // Partial results of one key-range workgroup: O (unnormalised, fp32, row-major
 // [BM][128]), then the offset m (base 2) and the weight sum l of each row.
 constexpr int PART_FLOATS = BM * HEAD_DIM + 2 * BM;
-
-// Workgroup x of a launch -> logical index.  Workgroups are dispatched
-// round-robin over the 8 XCDs; give each XCD a contiguous range of logical
-// indices so the workgroups sharing an XCD's L2 stream the same head's K/V.
-__device__ __forceinline__ int xcd_remap(int x, int total) {
-    const int xcd = x & 7, slot = x >> 3;
-    const int per = total >> 3, rem = total & 7;
-    return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
-}
-
-__device__ __forceinline__ float swap_halves_max(float x) {
-    // v_permlane32_swap exchanges lanes 0-31 of one operand with lanes 32-63 of
-    // the other; with both operands = x, the two results hold x of this lane
-    // and of lane ^ 32 (in some order).
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float swap_halves_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Buffer resource over `bytes` bytes from `base`, raw addressing (word 3 is the
-// gfx9 raw-buffer format).  Accesses at or past `bytes` read zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// One 1 KiB piece HBM -> LDS by the buffer form of the LDS DMA
-// (buffer_load_dwordx4 ... lds): lane l moves bytes [soff + 16 l, soff + 16 l + 16)
-// of the resource to lds_dst + 16 l.  The buffer form is counted on VM_CNT
-// only; with the global form in flight the compiler can only wait for all
-// outstanding LDS reads at once, which exposes the full LDS latency each time
-// an MFMA operand is needed.
-__device__ __forceinline__ void lds_piece(__amdgpu_buffer_rsrc_t rsrc, int soff, uint4* lds_dst, int lane) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, lane * 16,
-                                             soff, 0, 0);
-}
-
-// Copy CHUNKS 16-byte chunks (whole 1 KiB pieces) starting at byte soff of the
-// resource to lds_dst: wave w moves pieces w, w + NW, ...
-template <int NW, int CHUNKS>
-__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, int soff, uint4* lds_dst, int wave,
-                                            int lane) {
-    static_assert(CHUNKS % 64 == 0, "whole 1 KiB pieces");
-#pragma unroll
-    for (int i = 0; i < (CHUNKS / 64 + NW - 1) / NW; ++i) {
-        const int piece = i * NW + wave;
-        if (piece < CHUNKS / 64) lds_piece(rsrc, soff + piece * 1024, lds_dst + piece * 64, lane);
-    }
-}
 
 // How one call is laid out over the GPU: `full` items run whole-key-range
 // workgroups in full rounds; the remaining `split` items (fewer than a round)

@@ -29,7 +29,7 @@
 
 #include <cmath>
 
-#include "attn_common.h"
+#include "gfx950.h"
 
 namespace dit {
 

@@ -35,7 +35,7 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "attn_common.h"
+#include "gfx950.h"
 #include "bf16_util.h"
 
 namespace dit {
