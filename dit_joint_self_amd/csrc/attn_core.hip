@@ -15,8 +15,9 @@
 //     B operands for the whole kernel (Q-tile resident in VGPRs).
 //   * K/V stream: 64-key tiles already rotated and laid out by
 //     prepare_kv.hip, copied HBM -> LDS by buffer_load_dwordx4 ... lds into
-//     two K' and two V^T buffers; K' runs one tile ahead of V^T, and the
-//     copies of a step are issued one at a time between its MFMAs.
+//     four K' and four V^T buffers (K' three tiles ahead, V^T two), one
+//     barrier per two tiles; the copies of a step are issued one at a time
+//     between its MFMAs.
 //   * Software pipeline per wave: the QK^T MFMAs of tile j+1 run beside the
 //     exp2 / bf16 / row-sum work of tile j, then O += P V for tile j.
 //   * S^T = K' Q'^T on v_mfma_f32_32x32x16_bf16: lane (n, hh) of the
@@ -38,6 +39,8 @@
 // 4 * BM * S * 128 flop; per call 4 * B * H * S^2 * 128 flop.
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "attn_common.h"
 #include "bf16_util.h"
@@ -97,10 +100,10 @@ __device__ __forceinline__ void weight_pair(const f32x16 (&sc)[2], int p, uint32
 }
 
 // The tile copies one pipelined step issues, spread over stage A: piece j of
-// the K' part two tiles ahead at step 2j + 1, piece j of the V^T part one tile
-// ahead at step 2 (KJ + j) + 1.  Issued one at a time between MFMAs instead of
-// in a burst after the barrier, the copies do not hold up the wave's first
-// MFMAs.
+// the K' part three tiles ahead at step 2j + 1, piece j of the V^T part two
+// tiles ahead at step 2 (KJ + j) + 1.  Issued one at a time between MFMAs
+// instead of in a burst after the barrier, the copies do not hold up the
+// wave's first MFMAs.
 struct TileCopies {
     static constexpr int KJ = (K_PART_CHUNKS / 64 + NW - 1) / NW;  // K' pieces per wave (at most)
     static constexpr int VJ = (V_PART_CHUNKS / 64 + NW - 1) / NW;  // V^T pieces per wave (at most)
@@ -109,6 +112,7 @@ struct TileCopies {
     uint4* kdst;
     uint4* vdst;
     bool kon;          // the K' part exists (wave-uniform)
+    bool von;          // the V^T part exists (wave-uniform)
     int wave, lane;
     __device__ __forceinline__ void at_step(int i) const {
         if ((i & 1) == 0) return;
@@ -118,7 +122,7 @@ struct TileCopies {
             if (kon && p < K_PART_CHUNKS / 64) lds_piece(rsrc, ksoff + p * 1024, kdst + p * 64, lane);
         } else if (j < KJ + VJ) {
             const int p = (j - KJ) * NW + wave;
-            if (p < V_PART_CHUNKS / 64) lds_piece(rsrc, vsoff + p * 1024, vdst + p * 64, lane);
+            if (von && p < V_PART_CHUNKS / 64) lds_piece(rsrc, vsoff + p * 1024, vdst + p * 64, lane);
         }
     }
 };
@@ -251,14 +255,20 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, int S,
     int ntiles, int nqt, int full, int nsplit, float qmul, int has_rope) {
     static_assert(QB == 1, "one 32-query block per wave");
-    // K' parts run one tile ahead of V^T parts, each through its own pair of
-    // buffers: step i reads K'(i + 1) and V^T(i) while K'(i + 2) and V^T(i + 1)
-    // land.  Distinct objects and a loop unrolled by two keep every buffer
-    // static, so the compiler does not make LDS reads wait for the copies.
+    // Tile t's K' part lives in kbuf[t % 4] and its V^T part in vbuf[t % 4]
+    // (140 KiB of LDS).  Distinct objects and a loop unrolled by four keep
+    // every buffer static, so the compiler does not make LDS reads wait for
+    // the copies.
     __shared__ uint4 kb0[K_PART_CHUNKS];
     __shared__ uint4 kb1[K_PART_CHUNKS];
+    __shared__ uint4 kb2[K_PART_CHUNKS];
+    __shared__ uint4 kb3[K_PART_CHUNKS];
     __shared__ uint4 vb0[V_PART_CHUNKS];
     __shared__ uint4 vb1[V_PART_CHUNKS];
+    __shared__ uint4 vb2[V_PART_CHUNKS];
+    __shared__ uint4 vb3[V_PART_CHUNKS];
+    uint4* const kbuf[4] = {kb0, kb1, kb2, kb3};
+    uint4* const vbuf[4] = {vb0, vb1, vb2, vb3};
 
     const CoreWork cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
     const int64_t bh = cw.item / nqt;
@@ -278,7 +288,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
         raw_rsrc(ws + bh * (int64_t)ntiles * TILE_CHUNKS, (uint32_t)ntiles * TILE_BYTES);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int tile0 = tb * TILE_BYTES;
-    auto copies = [&](int ki, uint4* kd, bool kon, int vi, uint4* vd) {
+    auto copies = [&](int ki, uint4* kd, bool kon, int vi, uint4* vd, bool von = true) {
         TileCopies c;
         c.rsrc = rsrc;
         c.ksoff = tile0 + ki * TILE_BYTES;
@@ -286,6 +296,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
         c.kdst = kd;
         c.vdst = vd;
         c.kon = kon;
+        c.von = von;
         c.wave = wv;
         c.lane = lane;
         return c;
@@ -293,6 +304,8 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     copy_to_lds<NW, K_PART_CHUNKS>(rsrc, tile0, kb0, wv, lane);
     copy_to_lds<NW, V_PART_CHUNKS>(rsrc, tile0 + K_PART_BYTES, vb0, wv, lane);
     if (nt > 1) copy_to_lds<NW, K_PART_CHUNKS>(rsrc, tile0 + TILE_BYTES, kb1, wv, lane);
+    if (nt > 1) copy_to_lds<NW, V_PART_CHUNKS>(rsrc, tile0 + TILE_BYTES + K_PART_BYTES, vb1, wv, lane);
+    if (nt > 2) copy_to_lds<NW, K_PART_CHUNKS>(rsrc, tile0 + 2 * TILE_BYTES, kb2, wv, lane);
 
     // ---- Q prologue: RoPE, fold scale*log2(e), round to bf16, keep resident.
     bf16x8 qf[8];
@@ -333,45 +346,59 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
 
-    // Scores of tile 0 (offset 0), then the pipelined steps.  Step i's scores
-    // live in sA for even i and sB for odd i.
-    f32x16 sA[2], sB[2];
+    // Scores of tile 0 (offset 0), then the pipelined steps.  Tile t's
+    // scores live in s[t % 2].
+    f32x16 s[2][2];
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     {
         uint32_t w[16];
         float sum = 0.0f;
-        stage_a<true, false>(kb0, qf, negm, sA, sB, w, sum, n, hh);
+        stage_a<true, false>(kb0, qf, negm, s[0], s[1], w, sum, n, hh);
     }
     // Offset of the first tile = its exact row max (masked first if it is
     // also the range's last tile, so the max is over real keys only).
-    if (nt == 1) mask_tail(sA, te - 1, S, hh);
+    if (nt == 1) mask_tail(s[0], te - 1, S, hh);
     {
-        const float mx = tile_max(sA);
-        sA[0] -= mx;
-        sA[1] -= mx;
+        const float mx = tile_max(s[0]);
+        s[0][0] -= mx;
+        s[0][1] -= mx;
         negm -= mx;
     }
-    int i = 0;
-    for (; i + 2 <= nt - 1; i += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        tile_step(kb1, vb0, sA, sB, qf, o, negm, lsum, n, hh, copies(i + 2, kb0, true, i + 1, vb1));
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        tile_step(kb0, vb1, sB, sA, qf, o, negm, lsum, n, hh, copies(i + 3, kb1, i + 3 < nt, i + 2, vb0));
+    // One barrier per two tiles.  Tile t's K' part is in kbuf[t % 4], its V^T
+    // part in vbuf[t % 4]; step t issues the copies of K'(t + 3) and V^T(t + 2).
+    // Between the barriers before steps k and k + 2 (k even) the steps read
+    // K'(k + 1), K'(k + 2), V^T(k), V^T(k + 1), all copied before the first of
+    // them, and overwrite only parts read before it.
+    const int L = nt - 1;
+    auto step = [&](auto rc, int k) __attribute__((always_inline)) {
+        constexpr int R = decltype(rc)::value;  // k % 4
+        if (R % 2 == 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        tile_step(kbuf[(R + 1) % 4], vbuf[R], s[R % 2], s[(R + 1) % 2], qf, o, negm, lsum, n, hh,
+                  copies(k + 3, kbuf[(R + 3) % 4], k + 3 <= L, k + 2, vbuf[(R + 2) % 4], k + 2 <= L));
+    };
+    for (int k = 0;;) {
+        if (k >= L) break;
+        step(std::integral_constant<int, 0>{}, k++);
+        if (k >= L) break;
+        step(std::integral_constant<int, 1>{}, k++);
+        if (k >= L) break;
+        step(std::integral_constant<int, 2>{}, k++);
+        if (k >= L) break;
+        step(std::integral_constant<int, 3>{}, k++);
     }
-    if (i < nt - 1) {  // i = nt - 2, even: one more full step, then the last tile from sB / vb1
+    if ((L & 1) == 0) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        tile_step(kb1, vb0, sA, sB, qf, o, negm, lsum, n, hh, copies(i + 2, kb0, false, i + 1, vb1));
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        tile_step_last(vb1, sB, te - 1, S, qf, o, negm, lsum, n, hh);
-    } else {  // i = nt - 1, even: the last tile from sA / vb0
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        tile_step_last(vb0, sA, te - 1, S, qf, o, negm, lsum, n, hh);
+    }
+    switch (L & 3) {
+        case 0: tile_step_last(vb0, s[0], te - 1, S, qf, o, negm, lsum, n, hh); break;
+        case 1: tile_step_last(vb1, s[1], te - 1, S, qf, o, negm, lsum, n, hh); break;
+        case 2: tile_step_last(vb2, s[0], te - 1, S, qf, o, negm, lsum, n, hh); break;
+        default: tile_step_last(vb3, s[1], te - 1, S, qf, o, negm, lsum, n, hh); break;
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) settle(o[db]);

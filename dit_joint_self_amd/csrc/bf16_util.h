@@ -28,8 +28,12 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
     x[6] = bf16lo(w.w); x[7] = bf16hi(w.w);
 }
 
-// RoPE on 4 interleaved pairs: (x0 + i x1) * (c + i s), in fp32.
+// RoPE on 4 interleaved pairs: (x0 + i x1) * (c + i s), in fp32, each
+// product rounded before the sum: no multiply-add is fused, so the rounding
+// (and the bf16 value a caller rounds it to) does not depend on which product
+// the compiler would otherwise fuse in a given build.
 __device__ __forceinline__ void rotate4(float (&x)[8], float4 c, float4 s) {
+#pragma clang fp contract(off)
     const float cc[4] = {c.x, c.y, c.z, c.w};
     const float ss[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll

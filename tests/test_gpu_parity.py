@@ -181,6 +181,46 @@ def test_whole_ranges_and_key_range_pieces_in_one_launch():
         _assert_close(got, want, f"S={w.S} H={w.H} split={split}")
 
 
+def test_rotated_keys_round_like_plain_fp32():
+    """The tile preparation rotates K in plain fp32 arithmetic (each product
+    rounded, then the sum; no fused multiply-add) and rounds to bf16 to nearest
+    even.  With fp32 tables made on the host, the prepared K' rows equal that
+    evaluation bit for bit.  The tile image is private to the library; the test
+    reads it as documented in tile_layout.h: per (batch, head), 35840-byte
+    tiles of 64 keys whose first 17408 bytes are 64 rows of 272 bytes, row rho
+    holding key (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1) of the tile,
+    dims 0..127 first."""
+    torch = _torch()
+    dj = _dj()
+    w = _small(0, (10, 30), B=1, H=2, seed=300)          # S = 300: a ragged last tile
+    qb, kb, vb = W.make_bf16_inputs(w)
+    ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
+    cos32, sin32 = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    k32 = W.bf16_bits_to_f32(kb).astype(np.float32)
+    e, o = k32[..., 0::2], k32[..., 1::2]
+    rot = np.empty_like(k32)
+    rot[..., 0::2] = e * cos32 - o * sin32
+    rot[..., 1::2] = e * sin32 + o * cos32
+    u = rot.view(np.uint32).astype(np.uint64)
+    want = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF).astype(np.uint16)
+
+    k, v = to_device_bf16(kb), to_device_bf16(vb)
+    cos_d, sin_d = torch.from_numpy(cos32).cuda(), torch.from_numpy(sin32).cuda()
+    nbytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    dj.dit_attn_prepare_kv(k, v, cos_d, sin_d, ws)
+    torch.cuda.synchronize()
+    ntiles = -(-w.S // 64)
+    img = ws.cpu().numpy()[: w.B * w.H * ntiles * 35840].view(np.uint16).reshape(w.B, w.H, ntiles, 17920)
+    rows = img[..., :8704].reshape(w.B, w.H, ntiles, 64, 136)[..., :128]
+    rho = np.arange(64)
+    key_of_row = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1)
+    got = np.zeros((w.B, w.H, ntiles * 64, 128), np.uint16)
+    got[:, :, (np.arange(ntiles)[:, None] * 64 + key_of_row[None, :]).ravel()] = rows.reshape(w.B, w.H, -1, 128)
+    assert np.array_equal(got[:, :, : w.S], want)
+    assert not got[:, :, w.S:].any()                      # keys past S are zero
+
+
 def test_no_rope_three_axis():
     w = W.get("tiny").with_(grid=(2, 8, 16), axes_dim=(16, 56, 56), H=2)
     qb, kb, vb = W.make_bf16_inputs(w)
