@@ -394,12 +394,13 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
-    switch (L & 3) {
-        case 0: tile_step_last(vb0, s[0], te - 1, S, qf, o, negm, lsum, n, hh); break;
-        case 1: tile_step_last(vb1, s[1], te - 1, S, qf, o, negm, lsum, n, hh); break;
-        case 2: tile_step_last(vb2, s[0], te - 1, S, qf, o, negm, lsum, n, hh); break;
-        default: tile_step_last(vb3, s[1], te - 1, S, qf, o, negm, lsum, n, hh); break;
-    }
+    // No copy is in flight any more, so the last V^T part may be picked at
+    // run time; only the score registers need a static choice.
+    const uint4* vlast = (L & 2) ? ((L & 1) ? vb3 : vb2) : ((L & 1) ? vb1 : vb0);
+    if (L & 1)
+        tile_step_last(vlast, s[1], te - 1, S, qf, o, negm, lsum, n, hh);
+    else
+        tile_step_last(vlast, s[0], te - 1, S, qf, o, negm, lsum, n, hh);
 #pragma unroll
     for (int db = 0; db < 4; ++db) settle(o[db]);
 
