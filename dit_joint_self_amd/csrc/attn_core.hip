@@ -28,7 +28,7 @@
 //     folded into the QK^T accumulator's initial value, the row max is only
 //     taken for the first tile and when a tile's weights overflow 2^20, and
 //     the row sum is accumulated from the bf16 weights with v_dot2c (see
-//     attn_tile).  Weights stay <= 2^20, so fp32 and bf16 hold them with
+//     weight_pair and settle_weights).  Weights stay <= 2^20, so fp32 and bf16 hold them with
 //     their usual relative precision, and the final O / l is unchanged.
 //   * O^T += V^T P^T on the same MFMA: P leaves the S accumulator already in
 //     B-operand layout (see tile_layout.h), V^T comes from LDS.
@@ -319,21 +319,21 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
         const int64_t rr = ok ? row : S - 1;
         const uint4* qrow = q + (bh * S + rr) * 16;
         uint4 qw[8];
-        float4 cw[8], sw[8];
+        float4 cosw[8], sinw[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) qw[t] = qrow[2 * t + hh];
         if (has_rope) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                cw[t] = cos_t[rr * 16 + 2 * t + hh];
-                sw[t] = sin_t[rr * 16 + 2 * t + hh];
+                cosw[t] = cos_t[rr * 16 + 2 * t + hh];
+                sinw[t] = sin_t[rr * 16 + 2 * t + hh];
             }
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             float fv[8];
             unpack8(qw[t], fv);
-            if (has_rope) rotate4(fv, cw[t], sw[t]);
+            if (has_rope) rotate4(fv, cosw[t], sinw[t]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) fv[e] *= qmul;
             const uint4 pk = pack8(fv);

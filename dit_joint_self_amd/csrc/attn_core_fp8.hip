@@ -199,15 +199,15 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
         const int64_t rr = ok ? row : S - 1;
         const uint4* qrow = q + (bh * S + rr) * 8;
         uint4 qw[4];
-        float4 cw[8], sw[8];
+        float4 cosw[8], sinw[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) qw[i] = qrow[(i >> 1) * 4 + hh * 2 + (i & 1)];
         if (has_rope) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int c = ((i >> 2) * 4 + hh * 2 + ((i >> 1) & 1));
-                cw[i] = cos_t[rr * 16 + 2 * c + (i & 1)];
-                sw[i] = sin_t[rr * 16 + 2 * c + (i & 1)];
+                cosw[i] = cos_t[rr * 16 + 2 * c + (i & 1)];
+                sinw[i] = sin_t[rr * 16 + 2 * c + (i & 1)];
             }
         }
 #pragma unroll
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
                     float t[8];
 #pragma unroll
                     for (int x = 0; x < 8; ++x) t[x] = fv[8 * g + x] * q_scale;
-                    if (has_rope) rotate4(t, cw[4 * kk + 2 * h + g], sw[4 * kk + 2 * h + g]);
+                    if (has_rope) rotate4(t, cosw[4 * kk + 2 * h + g], sinw[4 * kk + 2 * h + g]);
 #pragma unroll
                     for (int x = 0; x < 8; ++x) fv[8 * g + x] = clamp_e4m3(t[x] * qfac);
                 }
