@@ -38,10 +38,10 @@ FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/
 KERNEL_SOURCES = BF16_SOURCES
 MEASURED_TRAFFIC = {
     # dit_attn_core (attn_core_kernel + attn_merge_kernel), hash over BF16_SOURCES
-    ("8f3e9690c2b2f59f", "flux2048"): {"read_bytes": 1082.3e6, "write_bytes": 135.8e6,
+    ("c3d9694f14615563", "flux2048"): {"read_bytes": 1082.3e6, "write_bytes": 135.8e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
     # dit_attn_core_fp8 (attn_core_fp8_kernel + attn_merge_kernel), hash over FP8_SOURCES
-    ("ac498260097cb724", "flux2048_fp8"): {"read_bytes": 693.5e6, "write_bytes": 135.8e6,
+    ("589431f18f58cffb", "flux2048_fp8"): {"read_bytes": 693.5e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
     ("97d06d7abed0bc27", "flux2048_qkv"): {"read_bytes": 435.8e6, "write_bytes": 331.1e6,
