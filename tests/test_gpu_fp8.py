@@ -88,6 +88,17 @@ def test_fp8_full_parity(name):
     _assert_close(_run(w, qkv8), _oracle(w, qkv8), name)
 
 
+def test_fp8_whole_ranges_and_key_range_pieces_in_one_launch():
+    """37 heads x ceil(1800 / 256) = 296 items: 256 whole-range workgroups and 40
+    items x 6 key ranges in one launch of the fp8 kernel (its two wave groups
+    half a tile apart), with 8-row and 8-key tails; every row compared."""
+    w = W.Workload("edge8", B=1, H=37, D=128, S_txt=0, grid=(30, 60), axes_dim=(64, 64), theta=10000.0, seed=1801)
+    qkv8 = _quantized(w)
+    want = _oracle(w, qkv8)
+    for split in (False, True):
+        _assert_close(_run(w, qkv8, split=split), want, f"S={w.S} H={w.H} split={split}")
+
+
 @pytest.mark.parametrize("name,n_random", [("flux2048_fp8", 96), ("video_ulysses4", 32)])
 def test_fp8_sampled_parity_full_size(name, n_random):
     w = W.get(name)

@@ -165,15 +165,20 @@ def test_ragged_and_small_shapes(S_txt, grid, B, H):
         assert np.array_equal(got, bf16_f64(vb))
 
 
-def test_whole_ranges_and_key_range_pieces_in_one_launch():
-    """37 heads x ceil(1800 / 256) = 296 (head, query-tile) items: 256 whole-range
-    workgroups and 40 items split over 6 key ranges (240 pieces) share one
-    launch; the last query tile holds 8 rows and the last key tile 8 keys.
-    Every output row is compared with the oracle."""
-    w = _small(0, (30, 60), B=1, H=37, seed=1800)
+@pytest.mark.parametrize("B,H,split_ranges", [(1, 37, 6), (2, 20, 4)])
+def test_whole_ranges_and_key_range_pieces_in_one_launch(B, H, split_ranges):
+    """B x H x ceil(1800 / 256) (batch, head, query-tile) items: 256 whole-range
+    workgroups and the leftover items split over key ranges share one launch
+    (37 heads: 40 items x 6 ranges; 2 x 20 heads, items of both batches: 64 x 4);
+    the last query tile holds 8 rows and the last key tile 8 keys.  Every
+    output row is compared with the oracle."""
+    w = _small(0, (30, 60), B=B, H=H, seed=1800 + B)
     items = w.B * w.H * math.ceil(w.S / 256)
     rem = items % 256
-    assert (items, rem, min(256 // rem, math.ceil(w.S / 64))) == (296, 40, 6)
+    assert items > 256 and rem > 0
+    # the split the plan picks: fewest rounds of pieces, each piece 1/f item plus 1/32
+    cost = lambda f: math.ceil(rem * f / 256) * (1 / f + 1 / 32)
+    assert min(range(1, 9), key=lambda f: (cost(f), f)) == split_ranges
     qb, kb, vb = W.make_bf16_inputs(w)
     want = _oracle(w, qb, kb, vb)
     for split in (False, True):
