@@ -88,7 +88,8 @@ def _o_close(got, want, tag):
                                                  ("edge", 1, (0, 0), 1, 1),      # S = 1: L = the one score
                                                  ("edge", 1, (4, 8), 1, 2),      # S = 33, one ragged tile
                                                  ("edge", 13, (12, 20), 2, 2),   # S = 253, split key ranges
-                                                 ("edge", 0, (8, 8), 1, 256)])   # 256 items: one whole round
+                                                 ("edge", 0, (8, 8), 1, 256),    # 256 items: one whole round
+                                                 ("edge", 0, (30, 60), 2, 20)])  # 320 items: round + 64 x 4 pieces
 def test_core_lse_matches_oracle(name, S_txt, grid, B, H):
     torch = _torch()
     dj = _dj()
