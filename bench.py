@@ -93,7 +93,7 @@ def _traffic(files, workload):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="flux2048",
                     choices=list(W.WORKLOADS) + list(W.LINEAR_WORKLOADS) + list(W.RESIDUAL_WORKLOADS),
