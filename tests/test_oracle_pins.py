@@ -473,3 +473,72 @@ def test_residual_diff_nan_and_size_mismatch():
     assert math.isnan(residual_diff(p, c)) and not can_reuse(p, c, 1e300)
     with pytest.raises(ValueError):
         residual_diff(np.ones(3), np.ones(4))
+
+
+# ---------------------------------------------------------------- pins of the remaining exported helpers
+
+def test_oracle_lse_matches_brute_force_and_closed_form():
+    """oracle.attention.lse (natural-log row log-sum-exp of the scaled scores)
+    against the pure-Python math.fsum version, and the identical-keys closed
+    form L = s + log n."""
+    from oracle import lse
+    rng = np.random.default_rng(48)
+    q, k = _rand(rng, 2, 2, 5, 8), _rand(rng, 2, 2, 7, 8)
+    got = lse(q, k, 0.45)
+    want = np.array(brute.row_lse(q.tolist(), k.tolist(), scale=0.45))
+    assert got.shape == (2, 2, 5)
+    assert np.max(np.abs(got - want)) <= 1e-12
+    got = lse(q, k)                                     # default scale 1/sqrt(D)
+    want = np.array(brute.row_lse(q.tolist(), k.tolist()))
+    assert np.max(np.abs(got - want)) <= 1e-12
+    krow = _rand(rng, 1, 1, 1, 8)
+    kk = np.repeat(krow, 9, axis=2)
+    qq = _rand(rng, 1, 1, 3, 8)
+    s = (qq[0, 0] @ krow[0, 0, 0]) / math.sqrt(8)
+    assert np.max(np.abs(lse(qq, kk)[0, 0] - (s + math.log(9)))) <= 1e-13
+
+
+def test_mx_linear_from_float_exact_on_representable_activations():
+    """The dynamic-activation path on activations that MXFP4 represents
+    exactly (every 32-block holds a +-6 * 2^X element, so the block scale is
+    2^X, and the rest are E2M1 magnitudes times 2^X): quantising loses
+    nothing, and the result must equal the exact dyadic sum of x times the
+    dequantised weight, computed with Python fractions."""
+    from fractions import Fraction
+    from oracle.mx import mx_linear_from_float
+    rng = np.random.default_rng(49)
+    M, N, K = 3, 2, 64
+    mags = np.array(E2M1_TABLE)
+    x = np.empty((M, K))
+    for m in range(M):
+        for b in range(K // 32):
+            ex = int(rng.integers(-6, 6))
+            blk = mags[rng.integers(0, 8, size=32)] * rng.choice([-1.0, 1.0], size=32)
+            blk[int(rng.integers(0, 32))] = 6.0 * (1 if rng.random() < 0.5 else -1)
+            x[m, 32 * b:32 * b + 32] = blk * 2.0 ** ex
+    wc = rng.integers(0, 16, size=(N, K))
+    wsc = rng.integers(122, 132, size=(N, K // 32))
+    val = lambda code: Fraction(E2M1_TABLE[code & 7]) * (-1 if code & 8 else 1)
+    got = mx_linear_from_float(x, wc, wsc)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(x[m, kk])) * val(int(wc[n, kk])) * Fraction(2) ** (int(wsc[n, kk // 32]) - 127)
+                        for kk in range(K))
+            assert got[m, n] == float(exact)
+
+
+def test_mx_linear_from_float_rounds_the_activations():
+    """A hand-worked block: x = (7, 1.25, -0.75, 0, ...) has max 7, so
+    X = floor(log2 7) - 2 = 0; 7 saturates to 6, 1.25 ties to the even code
+    (1.0) and -0.75 ties to the even code (-1.0).  With a weight row of
+    E2M1 1.0 (code 2) at scale 2^1 the product is 2 (6 + 1 - 1) = 12; a
+    weight row of -0.5 (code 9) at scale 2^0 gives -0.5 (6 + 1 - 1) = -3."""
+    from oracle.mx import mx_linear_from_float
+    x = np.zeros((1, 32))
+    x[0, :3] = [7.0, 1.25, -0.75]
+    wc = np.zeros((2, 32), np.int64)
+    wc[0, :3] = 2
+    wc[1, :3] = 9
+    wsc = np.array([[128], [127]])
+    got = mx_linear_from_float(x, wc, wsc)
+    assert got.tolist() == [[12.0, -3.0]]
