@@ -100,6 +100,9 @@ def parse():
                     help="an attention workload, or an MXFP4 linear-layer shape (quantise + A4W4 GEMM)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-config", action="store_true",
+                    help="time only --workload (by default an attention run also times every other attention "
+                         "workload and reports them under `configs`)")
     ap.add_argument("--ring", type=int, default=1,
                     help="time one rank's share of a ring of this many ranks (bf16 workloads): its query shard "
                          "against every key/value block, folded with the LSE merge")
@@ -139,32 +142,58 @@ def bf16_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
 
 
+def host_info():
+    """CPU model, usable host cores and the BLAS thread count numpy runs its
+    products with (the oracle's matrix products are its multi-threaded part)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas_threads, blas = 1, "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            blas_threads = max(int(p.get("num_threads", 1)) for p in libs)
+            blas = ",".join(sorted({str(p.get("internal_api", "?")) for p in libs}))
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    return {"cpu_model": model, "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": blas_threads,
+            "blas": blas}
+
+
 def cpu_baseline(w, f64_head, budget_s, gpu_rows=None):
     """The float64 oracle as it stands, on the first query rows of successive
     heads until the time budget is spent; TFLOP/s at 4 * rows * S * D flop.
     ``f64_head(h)`` returns the head's (q, k, v) as float64 [1, 1, S, D].
     ``gpu_rows(h, rows)`` returns the timed GPU output of those rows of head h
-    ([1, 1, R, D], float64): the oracle rows computed for the timing are also
-    compared with it (max |diff|, reported as the sample's parity)."""
+    ([1, 1, R, D], float64): every oracle row computed for the timing, in every
+    head reached, is compared with it (max and mean |diff|, outside the timed
+    oracle time)."""
     from oracle import joint_attention, rope_angles
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
+    info = host_info()
     ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
     rows_per_head = min(w.S, 8192)
     rows = np.arange(rows_per_head)
     t0 = time.perf_counter()
     done_rows = 0
     heads = 0
-    parity = None
+    dmax, dsum, dn, osum = 0.0, 0.0, 0, 0.0
     for h in range(w.H):
         q, k, v = f64_head(h)
         ref = joint_attention(q, k, v, ang, rows=rows)
-        if gpu_rows is not None and h == 0:
+        if gpu_rows is not None:
             tc = time.perf_counter()
-            parity = float(np.abs(gpu_rows(h, rows) - ref).max())
+            d = np.abs(gpu_rows(h, rows) - ref)
+            dmax = max(dmax, float(d.max()))
+            dsum += float(d.sum())
+            osum += float(np.abs(ref).sum())
+            dn += d.size
             t0 += time.perf_counter() - tc  # the comparison is not oracle time
         done_rows += rows_per_head
         heads += 1
@@ -172,10 +201,16 @@ def cpu_baseline(w, f64_head, budget_s, gpu_rows=None):
             break
     dt = time.perf_counter() - t0
     flops = 4.0 * done_rows * w.S * w.D
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{w.name}: first {rows_per_head} query rows x {heads} of {w.H} heads vs all {w.S} keys, "
-                      f"float64 numpy (incl. RoPE of the head's K), {dt:.1f} s",
-            "host_cpus": len(os.sched_getaffinity(0)), "sample_parity_max_abs": parity}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(info["blas_threads"]), "kind": "oracle",
+           "sample": f"{w.name}: first {rows_per_head} query rows x {heads} of {w.H} heads vs all {w.S} keys, "
+                     f"float64 numpy (incl. RoPE of the head's K), {dt:.1f} s; cores = numpy's BLAS threads "
+                     f"(the products), the softmax passes run on one",
+           **info}
+    if gpu_rows is not None:
+        rec["sample_parity"] = {"compared": f"all {done_rows} rows x {w.D} dims computed ({heads} heads)",
+                                "max_abs": dmax, "mean_abs": dsum / max(dn, 1),
+                                "rel_mean": dsum / max(osum, 1e-300)}
+    return rec
 
 
 def ring_bench(args, w, torch, dj):
@@ -346,17 +381,12 @@ def gemm_bench(args, lw, torch, dj):
                 t0 += time.perf_counter() - tc
             rows += 64
         dt = time.perf_counter() - t0
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-        except Exception:  # pragma: no cover
-            threads = 1
+        info = host_info()
         rec["cpu_baseline"] = {"value": 2.0 * rows * lw.N * lw.K / dt / 1e12, "unit": "TFLOP/s",
-                               "cores": int(threads), "kind": "oracle",
+                               "cores": int(info["blas_threads"]), "kind": "oracle",
                                "sample": f"{lw.name}: quantise + float64 product of the first {rows} of {lw.M} rows "
                                          f"(weight quantised beforehand), {dt:.1f} s",
-                               "host_cpus": len(os.sched_getaffinity(0)),
-                               "sample_parity_max_rel": parity}
+                               **info, "sample_parity_max_rel": parity}
     print(json.dumps(rec), flush=True)
 
 
@@ -424,8 +454,9 @@ def residual_bench(args, rw, torch, dj):
         rec["cpu_baseline"] = {"value": 4.0 * rows * rw.hidden / dt / 1e9, "unit": "GB/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"{rw.name}: the float64 difference over the first {rows} of {rw.tokens} "
-                                         f"tokens in chunks of {chunk}, {dt:.1f} s",
-                               "host_cpus": len(os.sched_getaffinity(0))}
+                                         f"tokens in chunks of {chunk}, {dt:.1f} s (numpy element-wise passes: "
+                                         f"one thread)",
+                               **host_info()}
     print(json.dumps(rec), flush=True)
 
 
@@ -454,93 +485,31 @@ def main():
     if args.ring > 1:
         ring_bench(args, w, torch, dj)
         return
-    fp8 = w.dtype == "fp8_e4m3"
     print(f"[bench] workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype}", file=sys.stderr, flush=True)
-    pos = torch.from_numpy(W.positions(w)).to("cuda")
-    cos, sin = dj.dit_rope_tables(pos, w.axes_dim, w.theta)
-    scale = 1.0 / math.sqrt(w.D)
-    stream = torch.cuda.current_stream()
-    if fp8:
-        (q8, sq), (k8, sk), (v8, sv) = [W.fp8_e4m3_quantize(x) for x in W.draw_qkv_f32(w)]
-        q, k, v = (torch.from_numpy(np.ascontiguousarray(c)).to("cuda") for c in (q8, k8, v8))
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
-        ws_bytes = dj.dit_attn_workspace_bytes_fp8(w.B, w.H, w.S, w.D)
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-        prep = lambda: dj.dit_attn_prepare_kv_fp8(k, v, sk, sv, cos, sin, ws, ws_bytes, stream=stream)
-        core = lambda: dj.dit_attn_core_fp8(q, sq, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes,
-                                            stream=stream)
-        forward = lambda: dj.dit_attn_forward_fp8(q, k, v, sq, sk, sv, cos, sin, out=out, S_txt=w.S_txt,
-                                                  scale=scale)
-        def f64_head(h):  # the oracle's dequantisation, for the CPU baseline leg only
-            from oracle.fp8 import dequantize
-            return tuple(dequantize(c[:, h:h + 1], s_) for c, s_ in ((q8, sq), (k8, sk), (v8, sv)))
-        peak = FP8_PEAK_TFLOPS
-    else:
-        qb, kb, vb = W.make_bf16_inputs(w)
-        q, k, v = bf16_dev(qb, torch), bf16_dev(kb, torch), bf16_dev(vb, torch)
-        out = torch.empty_like(q)
-        ws_bytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-        prep = lambda: dj.dit_attn_prepare_kv(k, v, cos, sin, ws, ws_bytes, stream=stream)
-        core = lambda: dj.dit_attn_core(q, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes, stream=stream)
-        forward = lambda: dj.dit_attn_forward(q, k, v, cos, sin, out=out, S_txt=w.S_txt, scale=scale)
-        f64_head = lambda h: tuple(W.bf16_bits_to_f32(b[:, h:h + 1]).astype(np.float64) for b in (qb, kb, vb))
-        peak = BF16_PEAK_TFLOPS
-
-    for _ in range(args.warmup):
-        prep()
-        core()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        prep()
-        ev[i][1].record(stream)
-        core()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    prep_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    core_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
-    step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
-    steps_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
-
-    # The allocating entry point itself (workspace from the stream pool), for reference.
-    for _ in range(2):
-        forward()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(K):
-        forward()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = e0.elapsed_time(e1) / K
-
-    flops = w.flops
+    run = AttentionRun(w, torch, dj)
+    timing = run.time_steps(args.steps, args.warmup)
+    fwd_ms = run.time_forward(args.steps)
+    fp8, flops, peak = run.fp8, w.flops, run.peak
+    step_ms, core_avg, prep_avg = timing["step_ms"], timing["core_ms"], timing["prep_ms"]
     src_hash = kernel_sources_hash(FP8_SOURCES if fp8 else BF16_SOURCES)
     meas = MEASURED_TRAFFIC.get((src_hash, w.name))
     traffic = None if meas is None else meas["read_bytes"] + meas["write_bytes"]
-    core_avg = float(np.mean(core_ms))
-    prep_avg = float(np.mean(prep_ms))
     achieved = flops / (core_avg * 1e-3) / 1e12
     tensor_bytes = w.B * w.H * w.S * w.D * (1 if fp8 else 2)
     # read Q, the prepared tiles and the two tables; write the bf16 output
     core_bytes = tensor_bytes + ws_bytes_tiles(w, fp8) + 2 * w.S * (w.D // 2) * 4 + w.B * w.H * w.S * w.D * 2
-    prep_bytes = 4 * tensor_bytes + 2 * w.S * (w.D // 2) * 4  # read K, V, cos, sin; write 2 tensors of tiles
+    # read K, V, cos, sin; write the prepared tiles
+    prep_bytes = 2 * tensor_bytes + 2 * w.S * (w.D // 2) * 4 + ws_bytes_tiles(w, fp8)
     rec = {
         "metric": METRIC,
         "value": flops / (step_ms * 1e-3) / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": step_ms,
-        "ms_per_step_median": float(np.median(steps_ms)),
-        "ms_per_step_min": float(np.min(steps_ms)),
+        "ms_per_step_median": timing["step_median_ms"],
+        "ms_per_step_min": timing["step_min_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -553,18 +522,25 @@ def main():
                      "kernel": ("dit_attn_core_fp8: attn_core_fp8_kernel" if fp8 else "dit_attn_core: attn_core_kernel")
                                + " (whole-range workgroups and key-range pieces, one launch) + attn_merge_kernel",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "frac_timing": "HIP events on the launch stream around each dit_attn_core call, mean over the "
+                                    "timed steps (a rocprofv3 kernel trace of the same command is in profiles/)",
                      "traffic": traffic, "traffic_unit": "HBM bytes per dit_attn_core call (read + write)",
                      "hbm_GBps": None if traffic is None else traffic / (core_avg * 1e-3) / 1e9,
                      "algorithmic_bytes": core_bytes, "avg_ms": core_avg, "kernel_sources": src_hash},
         "stages_ms": {"prepare_kv": prep_avg, "attn_core": core_avg,
-                      "prepare_kv_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9},
+                      "prepare_kv_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9,
+                      "prepare_kv_algorithmic_bytes": prep_bytes},
         "forward_ms": fwd_ms,
-        "wall_s": wall,
+        "wall_s": timing["wall_s"],
         "clock": clock_record(torch, dj, achieved, flops / (step_ms * 1e-3) / 1e12, 8192 if fp8 else 4096),
     }
+    out_host = run.out.cpu()
+    f64_head = run.f64_head
+    run.release()
+    if not args.single_config:
+        rec["configs"] = other_configs(w, args, torch, dj)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out_host = out.cpu()
 
         def gpu_rows(h, rows):
             bits = out_host[:, h:h + 1, torch.from_numpy(rows)].view(torch.int16).numpy().view(np.uint16)
@@ -572,6 +548,114 @@ def main():
 
         rec["cpu_baseline"] = cpu_baseline(w, f64_head, args.cpu_seconds, gpu_rows)
     print(json.dumps(rec), flush=True)
+
+
+class AttentionRun:
+    """Device inputs, RoPE tables, workspace and output of one attention
+    workload, with the two stages of a step (prepare_kv, core) as closures."""
+
+    def __init__(self, w, torch, dj):
+        self.w, self.torch, self.dj = w, torch, dj
+        self.fp8 = w.dtype == "fp8_e4m3"
+        pos = torch.from_numpy(W.positions(w)).to("cuda")
+        cos, sin = dj.dit_rope_tables(pos, w.axes_dim, w.theta)
+        scale = 1.0 / math.sqrt(w.D)
+        stream = self.stream = torch.cuda.current_stream()
+        if self.fp8:
+            (q8, sq), (k8, sk), (v8, sv) = [W.fp8_e4m3_quantize(x) for x in W.draw_qkv_f32(w)]
+            q, k, v = (torch.from_numpy(np.ascontiguousarray(c)).to("cuda") for c in (q8, k8, v8))
+            self.out = out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+            ws_bytes = dj.dit_attn_workspace_bytes_fp8(w.B, w.H, w.S, w.D)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+            self.prep = lambda: dj.dit_attn_prepare_kv_fp8(k, v, sk, sv, cos, sin, ws, ws_bytes, stream=stream)
+            self.core = lambda: dj.dit_attn_core_fp8(q, sq, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes,
+                                                     stream=stream)
+            self.forward = lambda: dj.dit_attn_forward_fp8(q, k, v, sq, sk, sv, cos, sin, out=out, S_txt=w.S_txt,
+                                                           scale=scale)
+
+            def f64_head(h):  # the oracle's dequantisation, for the CPU baseline leg only
+                from oracle.fp8 import dequantize
+                return tuple(dequantize(c[:, h:h + 1], s_) for c, s_ in ((q8, sq), (k8, sk), (v8, sv)))
+            self.f64_head = f64_head
+            self.peak = FP8_PEAK_TFLOPS
+        else:
+            qb, kb, vb = W.make_bf16_inputs(w)
+            q, k, v = bf16_dev(qb, torch), bf16_dev(kb, torch), bf16_dev(vb, torch)
+            self.out = out = torch.empty_like(q)
+            ws_bytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+            self.prep = lambda: dj.dit_attn_prepare_kv(k, v, cos, sin, ws, ws_bytes, stream=stream)
+            self.core = lambda: dj.dit_attn_core(q, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes,
+                                                 stream=stream)
+            self.forward = lambda: dj.dit_attn_forward(q, k, v, cos, sin, out=out, S_txt=w.S_txt, scale=scale)
+            self.f64_head = lambda h: tuple(W.bf16_bits_to_f32(b[:, h:h + 1]).astype(np.float64) for b in (qb, kb, vb))
+            self.peak = BF16_PEAK_TFLOPS
+
+    def time_steps(self, K, warmup):
+        """`warmup` untimed steps, then K steps; each stage bracketed by HIP
+        events on the launch stream."""
+        torch, stream = self.torch, self.stream
+        for _ in range(warmup):
+            self.prep()
+            self.core()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        t0 = time.perf_counter()
+        for i in range(K):
+            ev[i][0].record(stream)
+            self.prep()
+            ev[i][1].record(stream)
+            self.core()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        steps_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
+        return {"step_ms": ev[0][0].elapsed_time(ev[K - 1][2]) / K,
+                "step_median_ms": float(np.median(steps_ms)), "step_min_ms": float(np.min(steps_ms)),
+                "prep_ms": float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])),
+                "core_ms": float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])),
+                "wall_s": wall}
+
+    def time_forward(self, K):
+        """The allocating entry point itself (workspace from the stream pool), for reference."""
+        torch = self.torch
+        for _ in range(2):
+            self.forward()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(K):
+            self.forward()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    def release(self):
+        self.prep = self.core = self.forward = None
+        self.out = None
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def other_configs(headline, args, torch, dj):
+    """Every other attention workload timed the same way in the same run (at
+    least 10 steps for the long video share): step and kernel time, TFLOP/s and
+    the fraction of the dense MFMA peak of the workload's dtype."""
+    res = {}
+    for name, w in W.WORKLOADS.items():
+        if name == headline.name:
+            continue
+        print(f"[bench] also timing {name}", file=sys.stderr, flush=True)
+        run = AttentionRun(w, torch, dj)
+        K = max(10, args.steps // 5) if w.S > 50000 else args.steps
+        t = run.time_steps(K, args.warmup)
+        run.release()
+        res[name] = {"B": w.B, "H": w.H, "S": w.S, "dtype": w.dtype, "steps": K,
+                     "step_ms": t["step_ms"], "step_median_ms": t["step_median_ms"], "prepare_kv_ms": t["prep_ms"],
+                     "kernel_ms": t["core_ms"], "value": w.flops / (t["step_ms"] * 1e-3) / 1e12,
+                     "kernel_TFLOPs": w.flops / (t["core_ms"] * 1e-3) / 1e12,
+                     "pct_of_peak": 100.0 * w.flops / (t["step_ms"] * 1e-3) / 1e12 / run.peak,
+                     "kernel_frac": w.flops / (t["core_ms"] * 1e-3) / 1e12 / run.peak, "peak": run.peak}
+    return res
 
 
 if __name__ == "__main__":

@@ -5,8 +5,9 @@ kernels.  Functions keep the C names (``dit_attn_forward``, ``dit_rope_tables``,
 ``dit_attn_workspace_bytes``, ``dit_attn_prepare_kv``, ``dit_attn_core``,
 ``dit_attn_core_lse``, ``dit_attn_merge_lse``, the ``_fp8`` entries, the
 MXFP4 linear-layer entries and the DBCache decision) and
-take torch tensors (their device pointers are passed) or plain integers as
-pointers.  A missing library raises ``RuntimeError``: there is no fallback.
+take torch tensors, whose device pointers are passed after the checks the
+C ABI cannot make (dtype, contiguity, shapes, one GPU).  A missing library
+raises ``RuntimeError``: there is no fallback.
 """
 from __future__ import annotations
 
@@ -102,12 +103,87 @@ def lib_loaded() -> bool:
 
 
 def _ptr(x) -> Optional[int]:
-    """Device pointer of a tensor, an int pointer, or None."""
+    """Device pointer of a validated tensor, or None."""
     if x is None:
         return None
-    if isinstance(x, int):
-        return x
     return x.data_ptr()
+
+
+# ---------------------------------------------------------------- argument checks
+#
+# The C ABI sees pointers and sizes only.  Every wrapper below checks, before
+# calling the library, what it cannot see: that each argument is a contiguous
+# torch tensor of the right dtype and shape, that shapes agree across
+# arguments, and that every tensor lives on one GPU.  Violations raise
+# ValueError (TypeError for a non-tensor) and nothing is enqueued.
+
+def _dt(name):
+    import torch
+    return getattr(torch, name)
+
+
+def _tensor(t, name, dtypes, shape=None, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor (got {type(t).__name__})")
+    allowed = tuple(_dt(d) for d in dtypes)
+    if t.dtype not in allowed:
+        raise ValueError(f"{name} must have dtype {' or '.join(dtypes)} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
+    if shape is not None and tuple(int(x) for x in t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _same_gpu(**named):
+    """All given tensors (None skipped) on one GPU; returns that device."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU (got {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other arguments on {dev}")
+    return dev
+
+
+def _tables(rope_cos, rope_sin, S, D):
+    """Both None (no RoPE), or float32 [S, D/2] each."""
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("give both rope_cos and rope_sin, or neither")
+    if rope_cos is not None:
+        _tensor(rope_cos, "rope_cos", ["float32"], shape=(S, D // 2))
+        _tensor(rope_sin, "rope_sin", ["float32"], shape=(S, D // 2))
+
+
+def _workspace(ws, ws_bytes, name="workspace"):
+    """A contiguous device buffer; returns the byte count passed to the library
+    (at most the buffer's own size)."""
+    import torch
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor (got {type(ws).__name__})")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = ws.numel() * ws.element_size()
+    if ws_bytes is None:
+        return have
+    if int(ws_bytes) > have:
+        raise ValueError(f"{name}_bytes = {int(ws_bytes)} exceeds the buffer's {have} bytes")
+    return int(ws_bytes)
+
+
+def _bhsd(t, name, dtypes):
+    _tensor(t, name, dtypes, ndim=4)
+    return tuple(int(x) for x in t.shape)
+
+
+_F8 = ["uint8", "float8_e4m3fn"]
 
 
 def _stream(stream) -> Optional[int]:
@@ -138,12 +214,18 @@ def dit_rope_tables(pos, axes_dim: Sequence[int], theta: float, rope_cos=None, r
     Allocates the outputs when not given; returns (rope_cos, rope_sin).
     """
     import torch
+    _tensor(pos, "pos", ["int32"], ndim=2)
     S, n_axes = int(pos.shape[0]), int(pos.shape[1])
+    if len(axes_dim) != n_axes:
+        raise ValueError(f"axes_dim has {len(axes_dim)} entries, pos has {n_axes} axes")
     half = sum(int(a) for a in axes_dim) // 2
     if rope_cos is None:
         rope_cos = torch.empty((S, half), dtype=torch.float32, device=pos.device)
     if rope_sin is None:
         rope_sin = torch.empty((S, half), dtype=torch.float32, device=pos.device)
+    _tensor(rope_cos, "rope_cos", ["float32"], shape=(S, half))
+    _tensor(rope_sin, "rope_sin", ["float32"], shape=(S, half))
+    _same_gpu(pos=pos, rope_cos=rope_cos, rope_sin=rope_sin)
     dims = (ctypes.c_int32 * len(axes_dim))(*[int(a) for a in axes_dim])
     _check(lib().dit_rope_tables(_ptr(pos), S, n_axes, dims, float(theta), _ptr(rope_cos), _ptr(rope_sin),
                                  _stream(stream)))
@@ -157,13 +239,20 @@ def dit_attn_forward(q, k, v, rope_cos=None, rope_sin=None, out=None, S_txt: int
     S_img defaults to S - S_txt; scale defaults to 1/sqrt(D).  Returns ``out``.
     """
     import torch
-    B, H, S, D = (int(s) for s in q.shape)
+    B, H, S, D = shp = _bhsd(q, "q", ["bfloat16"])
+    _tensor(k, "k", ["bfloat16"], shape=shp)
+    _tensor(v, "v", ["bfloat16"], shape=shp)
+    _tables(rope_cos, rope_sin, S, D)
     if S_img is None:
         S_img = S - S_txt
+    if int(S_txt) < 0 or int(S_txt) + int(S_img) != S:
+        raise ValueError(f"S_txt + S_img = {int(S_txt)} + {int(S_img)} does not match the sequence length {S}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    _tensor(out, "out", ["bfloat16"], shape=shp)
+    _same_gpu(q=q, k=k, v=v, rope_cos=rope_cos, rope_sin=rope_sin, out=out)
     _check(lib().dit_attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(rope_cos), _ptr(rope_sin), _ptr(out),
                                   B, H, S_txt, S_img, D, float(scale), int(dtype), _stream(stream)))
     return out
@@ -174,20 +263,24 @@ def dit_attn_workspace_bytes(B: int, H: int, S: int, D: int) -> int:
 
 
 def dit_attn_prepare_kv(k, v, rope_cos, rope_sin, workspace, workspace_bytes: Optional[int] = None, stream=None):
-    B, H, S, D = (int(s) for s in k.shape)
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
+    B, H, S, D = shp = _bhsd(k, "k", ["bfloat16"])
+    _tensor(v, "v", ["bfloat16"], shape=shp)
+    _tables(rope_cos, rope_sin, S, D)
+    workspace_bytes = _workspace(workspace, workspace_bytes)
+    _same_gpu(k=k, v=v, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace)
     _check(lib().dit_attn_prepare_kv(_ptr(k), _ptr(v), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace),
                                      int(workspace_bytes), B, H, S, D, _stream(stream)))
 
 
 def dit_attn_core(q, rope_cos, rope_sin, workspace, out, scale: Optional[float] = None,
                   workspace_bytes: Optional[int] = None, stream=None):
-    B, H, S, D = (int(s) for s in q.shape)
+    B, H, S, D = shp = _bhsd(q, "q", ["bfloat16"])
+    _tables(rope_cos, rope_sin, S, D)
+    _tensor(out, "out", ["bfloat16"], shape=shp)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
+    workspace_bytes = _workspace(workspace, workspace_bytes)
+    _same_gpu(q=q, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace, out=out)
     _check(lib().dit_attn_core(_ptr(q), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace), int(workspace_bytes),
                                _ptr(out), B, H, S, D, float(scale), _stream(stream)))
     return out
@@ -197,13 +290,16 @@ def dit_attn_core_lse(q, rope_cos, rope_sin, workspace, out, lse=None, scale: Op
                       workspace_bytes: Optional[int] = None, stream=None):
     """dit_attn_core plus the row log-sum-exp [B, H, S] fp32 (allocated when not given); returns (out, lse)."""
     import torch
-    B, H, S, D = (int(s) for s in q.shape)
+    B, H, S, D = shp = _bhsd(q, "q", ["bfloat16"])
+    _tables(rope_cos, rope_sin, S, D)
+    _tensor(out, "out", ["bfloat16"], shape=shp)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
+    workspace_bytes = _workspace(workspace, workspace_bytes)
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _tensor(lse, "lse", ["float32"], shape=(B, H, S))
+    _same_gpu(q=q, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace, out=out, lse=lse)
     _check(lib().dit_attn_core_lse(_ptr(q), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace), int(workspace_bytes),
                                    _ptr(out), _ptr(lse), B, H, S, D, float(scale), _stream(stream)))
     return out, lse
@@ -212,11 +308,17 @@ def dit_attn_core_lse(q, rope_cos, rope_sin, workspace, out, lse=None, scale: Op
 def dit_attn_merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
     """Fold two partial results over disjoint key blocks; out / lse_out may be o_a / lse_a (in place)."""
     import torch
-    B, H, S, D = (int(s) for s in o_a.shape)
+    B, H, S, D = shp = _bhsd(o_a, "o_a", ["bfloat16"])
+    _tensor(o_b, "o_b", ["bfloat16"], shape=shp)
+    _tensor(lse_a, "lse_a", ["float32"], shape=(B, H, S))
+    _tensor(lse_b, "lse_b", ["float32"], shape=(B, H, S))
     if out is None:
         out = torch.empty_like(o_a)
     if lse_out is None:
         lse_out = torch.empty_like(lse_a)
+    _tensor(out, "out", ["bfloat16"], shape=shp)
+    _tensor(lse_out, "lse_out", ["float32"], shape=(B, H, S))
+    _same_gpu(o_a=o_a, lse_a=lse_a, o_b=o_b, lse_b=lse_b, out=out, lse_out=lse_out)
     _check(lib().dit_attn_merge_lse(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse_out),
                                     B, H, S, D, _stream(stream)))
     return out, lse_out
@@ -227,11 +329,17 @@ def dit_attn_merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=No
 def dit_mxfp4_quantize(x, codes=None, scales=None, stream=None):
     """bf16 [rows, K] -> (codes uint8 [rows, K/2], scales uint8 [rows, K/32]) on the device."""
     import torch
+    _tensor(x, "x", ["bfloat16"], ndim=2)
     rows, K = (int(s) for s in x.shape)
+    if K % 32:
+        raise ValueError(f"K = {K} must be a multiple of 32")
     if codes is None:
         codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _tensor(codes, "codes", ["uint8"], shape=(rows, K // 2))
+    _tensor(scales, "scales", ["uint8"], shape=(rows, K // 32))
+    _same_gpu(x=x, codes=codes, scales=scales)
     _check(lib().dit_mxfp4_quantize(_ptr(x), _ptr(codes), _ptr(scales), rows, K, _stream(stream)))
     return codes, scales
 
@@ -239,9 +347,18 @@ def dit_mxfp4_quantize(x, codes=None, scales=None, stream=None):
 def dit_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out=None, stream=None):
     """out [M, N] bf16 = deq(A) deq(W)^T from MXFP4 codes/scales ([M, K/2], [M, K/32], [N, K/2], [N, K/32])."""
     import torch
+    _tensor(a_codes, "a_codes", ["uint8"], ndim=2)
+    _tensor(w_codes, "w_codes", ["uint8"], ndim=2)
     M, N, K = int(a_codes.shape[0]), int(w_codes.shape[0]), 2 * int(a_codes.shape[1])
+    if K % 32:
+        raise ValueError(f"K = {K} must be a multiple of 32")
+    _tensor(w_codes, "w_codes", ["uint8"], shape=(N, K // 2))
+    _tensor(a_scales, "a_scales", ["uint8"], shape=(M, K // 32))
+    _tensor(w_scales, "w_scales", ["uint8"], shape=(N, K // 32))
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
+    _tensor(out, "out", ["bfloat16"], shape=(M, N))
+    _same_gpu(a_codes=a_codes, a_scales=a_scales, w_codes=w_codes, w_scales=w_scales, out=out)
     _check(lib().dit_mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), _ptr(out), M, N, K,
                                 _stream(stream)))
     return out
@@ -250,10 +367,18 @@ def dit_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out=None, stream=None):
 def dit_mxfp4_linear(x, w_codes, w_scales, out=None, stream=None):
     """x bf16 [M, K] times the MXFP4 weight [N, K]^T: dynamic per-1x32 quantisation + A4W4 GEMM."""
     import torch
+    _tensor(x, "x", ["bfloat16"], ndim=2)
     M, K = (int(s) for s in x.shape)
+    if K % 32:
+        raise ValueError(f"K = {K} must be a multiple of 32")
+    _tensor(w_codes, "w_codes", ["uint8"], ndim=2)
     N = int(w_codes.shape[0])
+    _tensor(w_codes, "w_codes", ["uint8"], shape=(N, K // 2))
+    _tensor(w_scales, "w_scales", ["uint8"], shape=(N, K // 32))
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _tensor(out, "out", ["bfloat16"], shape=(M, N))
+    _same_gpu(x=x, w_codes=w_codes, w_scales=w_scales, out=out)
     _check(lib().dit_mxfp4_linear(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(out), M, N, K, _stream(stream)))
     return out
 
@@ -269,6 +394,8 @@ def dit_dbcache_residual_diff(prev, cur, threshold: float, ws=None, diff=None, r
     decision diff < threshold, both left on the device: (diff float64 [1],
     reuse int32 [1])."""
     import torch
+    _tensor(prev, "prev", ["bfloat16"])
+    _tensor(cur, "cur", ["bfloat16"])
     n = int(prev.numel())
     if int(cur.numel()) != n:
         raise ValueError("prev and cur must have the same number of elements")
@@ -278,7 +405,12 @@ def dit_dbcache_residual_diff(prev, cur, threshold: float, ws=None, diff=None, r
         diff = torch.empty(1, dtype=torch.float64, device=prev.device)
     if reuse is None:
         reuse = torch.empty(1, dtype=torch.int32, device=prev.device)
-    ws_bytes = int(ws.numel() * ws.element_size()) if hasattr(ws, "numel") else 0
+    ws_bytes = _workspace(ws, None, "ws")
+    _tensor(diff, "diff", ["float64"])
+    _tensor(reuse, "reuse", ["int32"])
+    if diff.numel() < 1 or reuse.numel() < 1:
+        raise ValueError("diff and reuse must hold at least one element")
+    _same_gpu(prev=prev, cur=cur, ws=ws, diff=diff, reuse=reuse)
     _check(lib().dit_dbcache_residual_diff(_ptr(prev), _ptr(cur), n, float(threshold), _ptr(ws), ws_bytes,
                                            _ptr(diff), _ptr(reuse), _stream(stream)))
     return diff, reuse
@@ -312,9 +444,9 @@ def dit_clock_probe(blocks: int = 512, iters: int = 20000, stream=None):
 
 # ---------------------------------------------------------------- fp8 (e4m3 codes + per-tensor scales)
 
-def _shape8(t):
+def _shape8(t, name="q8"):
     """[B, H, S, D] of an e4m3 code tensor (uint8 or float8_e4m3fn)."""
-    return tuple(int(x) for x in t.shape)
+    return _bhsd(t, name, _F8)
 
 
 def dit_attn_workspace_bytes_fp8(B: int, H: int, S: int, D: int) -> int:
@@ -323,9 +455,11 @@ def dit_attn_workspace_bytes_fp8(B: int, H: int, S: int, D: int) -> int:
 
 def dit_attn_prepare_kv_fp8(k8, v8, k_scale: float, v_scale: float, rope_cos, rope_sin, workspace,
                             workspace_bytes: Optional[int] = None, stream=None):
-    B, H, S, D = _shape8(k8)
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
+    B, H, S, D = shp = _shape8(k8, "k8")
+    _tensor(v8, "v8", _F8, shape=shp)
+    _tables(rope_cos, rope_sin, S, D)
+    workspace_bytes = _workspace(workspace, workspace_bytes)
+    _same_gpu(k8=k8, v8=v8, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace)
     _check(lib().dit_attn_prepare_kv_fp8(_ptr(k8), _ptr(v8), float(k_scale), float(v_scale), _ptr(rope_cos),
                                          _ptr(rope_sin), _ptr(workspace), int(workspace_bytes), B, H, S, D,
                                          _stream(stream)))
@@ -333,11 +467,13 @@ def dit_attn_prepare_kv_fp8(k8, v8, k_scale: float, v_scale: float, rope_cos, ro
 
 def dit_attn_core_fp8(q8, q_scale: float, rope_cos, rope_sin, workspace, out, scale: Optional[float] = None,
                       workspace_bytes: Optional[int] = None, stream=None):
-    B, H, S, D = _shape8(q8)
+    B, H, S, D = shp = _shape8(q8)
+    _tables(rope_cos, rope_sin, S, D)
+    _tensor(out, "out", ["bfloat16"], shape=shp)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
+    workspace_bytes = _workspace(workspace, workspace_bytes)
+    _same_gpu(q8=q8, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace, out=out)
     _check(lib().dit_attn_core_fp8(_ptr(q8), float(q_scale), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace),
                                    int(workspace_bytes), _ptr(out), B, H, S, D, float(scale), _stream(stream)))
     return out
@@ -348,13 +484,20 @@ def dit_attn_forward_fp8(q8, k8, v8, q_scale: float, k_scale: float, v_scale: fl
                          stream=None):
     """Joint self-attention on e4m3 codes [B, H, S, D] with per-tensor scales; bf16 output."""
     import torch
-    B, H, S, D = _shape8(q8)
+    B, H, S, D = shp = _shape8(q8)
+    _tensor(k8, "k8", _F8, shape=shp)
+    _tensor(v8, "v8", _F8, shape=shp)
+    _tables(rope_cos, rope_sin, S, D)
     if S_img is None:
         S_img = S - S_txt
+    if int(S_txt) < 0 or int(S_txt) + int(S_img) != S:
+        raise ValueError(f"S_txt + S_img = {int(S_txt)} + {int(S_img)} does not match the sequence length {S}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=q8.device)
+    _tensor(out, "out", ["bfloat16"], shape=shp)
+    _same_gpu(q8=q8, k8=k8, v8=v8, rope_cos=rope_cos, rope_sin=rope_sin, out=out)
     _check(lib().dit_attn_forward_fp8(_ptr(q8), _ptr(k8), _ptr(v8), float(q_scale), float(k_scale), float(v_scale),
                                       _ptr(rope_cos), _ptr(rope_sin), _ptr(out), B, H, S_txt, S_img, D,
                                       float(scale), _stream(stream)))

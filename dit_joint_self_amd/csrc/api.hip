@@ -45,7 +45,7 @@ hipError_t launch_rope_tables(const int32_t* pos, int S, int n_axes, const int32
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kMaxDevices = 64;
 // Smallest query tile any kernel variant uses; bounds the workgroup count.
 constexpr int kMinBlockM = 128;
@@ -92,6 +92,16 @@ dit_status_t check_rope(const float* c, const float* s) {
         return fail(DIT_ERR_INVALID_ARG, "rope_cos and rope_sin must both be NULL or both non-NULL");
     if (c && (!aligned16(c) || !aligned16(s)))
         return fail(DIT_ERR_INVALID_ARG, "rope tables must be 16-byte aligned");
+    return DIT_OK;
+}
+
+// The rope tables (when given) against up to two regions the call writes.
+dit_status_t check_tables_apart(const float* c, const float* s, int S, const void* a, size_t na, const void* b,
+                                size_t nb) {
+    if (!c) return DIT_OK;
+    const size_t tb = (size_t)S * (dit::HEAD_DIM / 2) * sizeof(float);
+    if (overlaps(c, tb, a, na) || overlaps(s, tb, a, na) || (b && (overlaps(c, tb, b, nb) || overlaps(s, tb, b, nb))))
+        return fail(DIT_ERR_INVALID_ARG, "a rope table overlaps a region the call writes");
     return DIT_OK;
 }
 
@@ -195,13 +205,14 @@ dit_status_t dit_attn_prepare_kv(const void* k, const void* v, const float* rope
     const size_t tbytes = (size_t)B * H * S * D * 2;
     if (overlaps(workspace, need, k, tbytes) || overlaps(workspace, need, v, tbytes))
         return fail(DIT_ERR_INVALID_ARG, "workspace overlaps k or v");
+    if ((st = check_tables_apart(rope_cos, rope_sin, S, workspace, need, nullptr, 0)) != DIT_OK) return st;
     if ((st = check_device()) != DIT_OK) return st;
     return launched(dit::launch_prepare_kv(k, v, rope_cos, rope_sin, workspace, B * H, S,
                                            static_cast<hipStream_t>(stream)),
                     "prepare_kv_kernel");
 }
 
-static dit_status_t core_impl(const void* q, const float* rope_cos, const float* rope_sin, const void* workspace,
+static dit_status_t core_impl(const void* q, const float* rope_cos, const float* rope_sin, void* workspace,
                               size_t workspace_bytes, void* out, float* lse, int B, int H, int S, int D, float scale,
                               void* stream) {
     if (!q || !workspace || !out) return fail(DIT_ERR_INVALID_ARG, "q, workspace and out must be non-NULL");
@@ -216,28 +227,33 @@ static dit_status_t core_impl(const void* q, const float* rope_cos, const float*
     const size_t tbytes = (size_t)B * H * S * D * 2;
     if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, workspace, need))
         return fail(DIT_ERR_INVALID_ARG, "out overlaps q or the workspace");
+    // The call writes key-range partials into the workspace while other
+    // workgroups still read q and the tables.
+    if (overlaps(q, tbytes, workspace, need)) return fail(DIT_ERR_INVALID_ARG, "q overlaps the workspace");
+    if ((st = check_tables_apart(rope_cos, rope_sin, S, workspace, need, out, tbytes)) != DIT_OK) return st;
     if (lse) {
         const size_t lbytes = (size_t)B * H * S * 4;
         if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(DIT_ERR_INVALID_ARG, "lse must be 4-byte aligned");
         if (overlaps(lse, lbytes, out, tbytes) || overlaps(lse, lbytes, q, tbytes) ||
             overlaps(lse, lbytes, workspace, need))
             return fail(DIT_ERR_INVALID_ARG, "lse overlaps q, out or the workspace");
+        if ((st = check_tables_apart(rope_cos, rope_sin, S, lse, lbytes, nullptr, 0)) != DIT_OK) return st;
     }
     if ((st = check_device()) != DIT_OK) return st;
     const float qmul = (float)((double)scale * 1.4426950408889634073599);  // scale * log2(e)
-    void* part = static_cast<char*>(const_cast<void*>(workspace)) + tiles_bytes(B, H, S);
+    void* part = static_cast<char*>(workspace) + tiles_bytes(B, H, S);
     return launched(dit::launch_attn_core(q, rope_cos, rope_sin, workspace, part, out, lse, B * H, S, qmul,
                                           static_cast<hipStream_t>(stream)),
                     "attn_core_kernel");
 }
 
-dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin, const void* workspace,
+dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin, void* workspace,
                            size_t workspace_bytes, void* out, int B, int H, int S, int D, float scale,
                            void* stream) {
     return core_impl(q, rope_cos, rope_sin, workspace, workspace_bytes, out, nullptr, B, H, S, D, scale, stream);
 }
 
-dit_status_t dit_attn_core_lse(const void* q, const float* rope_cos, const float* rope_sin, const void* workspace,
+dit_status_t dit_attn_core_lse(const void* q, const float* rope_cos, const float* rope_sin, void* workspace,
                                size_t workspace_bytes, void* out, float* lse, int B, int H, int S, int D,
                                float scale, void* stream) {
     if (!lse) return fail(DIT_ERR_INVALID_ARG, "lse must be non-NULL");
@@ -311,6 +327,7 @@ dit_status_t dit_attn_prepare_kv_fp8(const void* k8, const void* v8, float k_sca
     const size_t tbytes = (size_t)B * H * S * D;
     if (overlaps(workspace, need, k8, tbytes) || overlaps(workspace, need, v8, tbytes))
         return fail(DIT_ERR_INVALID_ARG, "workspace overlaps k8 or v8");
+    if ((st = check_tables_apart(rope_cos, rope_sin, S, workspace, need, nullptr, 0)) != DIT_OK) return st;
     if ((st = check_device()) != DIT_OK) return st;
     return launched(dit::launch_prepare_kv_fp8(k8, v8, rope_cos, rope_sin, workspace, B * H, S, k_scale, v_scale,
                                                static_cast<hipStream_t>(stream)),
@@ -318,7 +335,7 @@ dit_status_t dit_attn_prepare_kv_fp8(const void* k8, const void* v8, float k_sca
 }
 
 dit_status_t dit_attn_core_fp8(const void* q8, float q_scale, const float* rope_cos, const float* rope_sin,
-                               const void* workspace, size_t workspace_bytes, void* out, int B, int H, int S, int D,
+                               void* workspace, size_t workspace_bytes, void* out, int B, int H, int S, int D,
                                float scale, void* stream) {
     if (!q8 || !workspace || !out) return fail(DIT_ERR_INVALID_ARG, "q8, workspace and out must be non-NULL");
     dit_status_t st = check_shape(B, H, S, D);
@@ -333,9 +350,12 @@ dit_status_t dit_attn_core_fp8(const void* q8, float q_scale, const float* rope_
     const size_t obytes = (size_t)B * H * S * D * 2;
     if (overlaps(out, obytes, q8, (size_t)B * H * S * D) || overlaps(out, obytes, workspace, need))
         return fail(DIT_ERR_INVALID_ARG, "out overlaps q8 or the workspace");
+    if (overlaps(q8, (size_t)B * H * S * D, workspace, need))
+        return fail(DIT_ERR_INVALID_ARG, "q8 overlaps the workspace");
+    if ((st = check_tables_apart(rope_cos, rope_sin, S, workspace, need, out, obytes)) != DIT_OK) return st;
     if ((st = check_device()) != DIT_OK) return st;
     const float qmul = (float)((double)scale * 1.4426950408889634073599);
-    void* part = static_cast<char*>(const_cast<void*>(workspace)) + fp8_tiles_bytes(B, H, S);
+    void* part = static_cast<char*>(workspace) + fp8_tiles_bytes(B, H, S);
     return launched(dit::launch_attn_core_fp8(q8, q_scale, rope_cos, rope_sin, workspace, part, out, B * H, S, qmul,
                                               static_cast<hipStream_t>(stream)),
                     "attn_core_fp8_kernel");
@@ -361,6 +381,7 @@ dit_status_t dit_attn_forward_fp8(const void* q8, const void* k8, const void* v8
     const size_t ibytes = (size_t)B * H * S * D, obytes = ibytes * 2;
     if (overlaps(out, obytes, q8, ibytes) || overlaps(out, obytes, k8, ibytes) || overlaps(out, obytes, v8, ibytes))
         return fail(DIT_ERR_INVALID_ARG, "out overlaps an input");
+    if ((st = check_tables_apart(rope_cos, rope_sin, S, out, obytes, nullptr, 0)) != DIT_OK) return st;
     if ((st = check_device()) != DIT_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -401,6 +422,7 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const
     const size_t tbytes = (size_t)B * H * S * D * 2;
     if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) || overlaps(out, tbytes, v, tbytes))
         return fail(DIT_ERR_INVALID_ARG, "out overlaps an input");
+    if ((st = check_tables_apart(rope_cos, rope_sin, S, out, tbytes, nullptr, 0)) != DIT_OK) return st;
     if ((st = check_device()) != DIT_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -185,8 +185,10 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     copy_to_lds<NW, F8_TILE_CHUNKS>(rsrc, tb * F8_TILE_BYTES, lds0, wv, lane);
 
     // ---- Q prologue.  Largest |q'| is 448 q_scale (times sqrt(2) with RoPE);
-    // choose e so that it maps to at most 448 after the factor qmul * sk.
-    const float qbound = E4M3_MAX * q_scale * (has_rope ? 1.41421356237309515f : 1.0f) * qmul * sk;
+    // choose e so that it maps to at most 448 in magnitude after the factor
+    // qmul * sk (qmul carries the sign of the softmax scale, which may be
+    // negative).
+    const float qbound = fabsf(E4M3_MAX * q_scale * (has_rope ? 1.41421356237309515f : 1.0f) * qmul * sk);
     const int e = qbound > 0.0f ? min(max((int)ceilf(log2f(qbound / E4M3_MAX)), -126), 126) : 0;
     const float qfac = qmul * sk * ldexpf(1.0f, -e);
     const int qscale = E8M0_ONE + e;

@@ -22,11 +22,19 @@
 
 namespace dit {
 
+// Every global store of a workgroup is coalesced: consecutive threads write
+// consecutive 16-byte chunks of the tile image (K' part, then V^T part), so
+// each wave store covers one contiguous 1 KiB run.  For the V^T part that
+// means consecutive lanes take consecutive (d, c) chunks; to keep their LDS
+// gathers apart, V is kept in LDS with its 16-byte chunks XOR-swizzled by
+// the key's 8-key group (chunk ch of key r sits at ch ^ (r >> 3)).
+__device__ __forceinline__ int vswz(int key, int ch) { return key * 16 + (ch ^ ((key >> 3) & 15)); }
+
 __global__ __launch_bounds__(256) void prepare_kv_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v,
     const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
     uint4* __restrict__ ws, int S, int ntiles, int has_rope) {
-    __shared__ uint4 vtile[KV_TILE * 16];  // 64 keys x 128 dims, key-major
+    __shared__ uint4 vtile[KV_TILE * 16];  // 64 keys x 128 dims, chunks swizzled (vswz)
 
     const int tile = blockIdx.x;
     const int64_t bh = blockIdx.y;
@@ -66,7 +74,10 @@ __global__ __launch_bounds__(256) void prepare_kv_kernel(
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vtile[tid + i * 256] = vw[i];
+    for (int i = 0; i < 4; ++i) {
+        const int x = tid + i * 256;
+        vtile[vswz(x >> 4, x & 15)] = vw[i];
+    }
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
         const int x = tid + i * 256;
@@ -86,25 +97,32 @@ __global__ __launch_bounds__(256) void prepare_kv_kernel(
 
     __syncthreads();
 
-    // V^T part: chunk (d, c) = keys 8c..8c+7 of head dim d.  Lanes run over d
-    // so the 2-byte LDS gathers of one instruction hit one row.
+    // V^T part: chunk q = (d, c) = keys 8c..8c+7 of head dim d (c = 8 is
+    // padding), q = d * 9 + c running over consecutive threads.
     const unsigned short* vt16 = reinterpret_cast<const unsigned short*>(vtile);
     uint4* vdst = dst + K_PART_CHUNKS;
+    constexpr int VI = (V_PART_CHUNKS + 255) / 256;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int y = tid + i * 256;
-        const int d = y & 127;
-        const int c = y >> 7;
-        uint32_t w[4];
+    for (int i = 0; i < VI; ++i) {
+        const int q = tid + i * 256;
+        if (q >= V_PART_CHUNKS) break;
+        const int d = q / V_ROW_CHUNKS;
+        const int c = q - d * V_ROW_CHUNKS;
+        uint4 out = make_uint4(0, 0, 0, 0);
+        if (c < 8) {
+            // keys 8c + j share the swizzle c, so dim d sits in chunk (d >> 3) ^ c of each row
+            const int col = (((d >> 3) ^ c) << 3) | (d & 7);
+            uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = vt16[(c * 8 + 2 * e) * 128 + d];
-            const uint32_t hi = vt16[(c * 8 + 2 * e + 1) * 128 + d];
-            w[e] = lo | (hi << 16);
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = vt16[(c * 8 + 2 * e) * 128 + col];
+                const uint32_t hi = vt16[(c * 8 + 2 * e + 1) * 128 + col];
+                w[e] = lo | (hi << 16);
+            }
+            out = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        vdst[v_chunk(d, c)] = make_uint4(w[0], w[1], w[2], w[3]);
+        vdst[q] = out;
     }
-    if (tid < HEAD_DIM) vdst[v_chunk(tid, 8)] = make_uint4(0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------

@@ -127,6 +127,13 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v,
  *
  * dit_attn_core  attention of q (rotated and scaled in its prologue) against
  *   the prepared workspace; rope tables must be the ones given to prepare_kv.
+ *   The call also WRITES the workspace: past the prepared tiles it keeps the
+ *   partial results of the query tiles whose keys it splits into ranges
+ *   (shapes whose work does not fill whole rounds of the GPU's compute
+ *   units; 24 heads of 16896 tokens is one).  Core calls that may run
+ *   at the same time (on different streams) must therefore not share a
+ *   workspace, even when they read the same prepared keys.  q, out and the
+ *   rope tables must not overlap the workspace.
  */
 size_t dit_attn_workspace_bytes(int B, int H, int S, int D);
 
@@ -136,7 +143,7 @@ dit_status_t dit_attn_prepare_kv(const void* k, const void* v,
                                  int B, int H, int S, int D, void* stream);
 
 dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin,
-                           const void* workspace, size_t workspace_bytes, void* out,
+                           void* workspace, size_t workspace_bytes, void* out,
                            int B, int H, int S, int D, float scale, void* stream);
 
 /*
@@ -153,8 +160,10 @@ dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* ro
  *   weights as out).  For a ring step, prepare the key/value block with the
  *   block's own RoPE tables (dit_attn_prepare_kv) and pass the query shard's
  *   tables here: RoPE of a row depends only on its own position.  The shard
- *   and the block have the same length S.  lse must not overlap q, out or the
- *   workspace.
+ *   and the block have the same length S.  lse must not overlap q, out, the
+ *   rope tables or the workspace.  Like dit_attn_core it writes key-range
+ *   partials into the workspace, so ring steps that run concurrently need
+ *   one workspace each.
  *
  * dit_attn_merge_lse  folds two partial results over disjoint key blocks:
  *   out = w_a o_a + w_b o_b with w_x = exp(lse_x - lse_out) and
@@ -166,7 +175,7 @@ dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* ro
  *   -inf (no keys on either side) yields NaN.
  */
 dit_status_t dit_attn_core_lse(const void* q, const float* rope_cos, const float* rope_sin,
-                               const void* workspace, size_t workspace_bytes, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* out, float* lse,
                                int B, int H, int S, int D, float scale, void* stream);
 
 dit_status_t dit_attn_merge_lse(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
@@ -180,7 +189,9 @@ dit_status_t dit_attn_merge_lse(const void* o_a, const float* lse_a, const void*
  *   q8, k8, v8  device e4m3 [B, H, S, D] (one byte per element), 16-byte aligned.
  *   q_scale, k_scale, v_scale  finite, > 0.
  *   rope_cos, rope_sin, scale, out (bf16), S_txt, S_img, D, stream: as in
- *               dit_attn_forward.
+ *               dit_attn_forward (scale may have either sign).
+ *   dit_attn_core_fp8 writes key-range partials into the workspace exactly as
+ *   dit_attn_core does (same rule for concurrent calls).
  *
  * RoPE is applied to the dequantised values in fp32; rotated K is re-quantised
  * with step k_scale*sqrt(2) and rotated, scaled Q with a power-of-two-adjusted
@@ -196,7 +207,7 @@ dit_status_t dit_attn_prepare_kv_fp8(const void* k8, const void* v8, float k_sca
                                      int B, int H, int S, int D, void* stream);
 
 dit_status_t dit_attn_core_fp8(const void* q8, float q_scale, const float* rope_cos, const float* rope_sin,
-                               const void* workspace, size_t workspace_bytes, void* out,
+                               void* workspace, size_t workspace_bytes, void* out,
                                int B, int H, int S, int D, float scale, void* stream);
 
 dit_status_t dit_attn_forward_fp8(const void* q8, const void* k8, const void* v8,

@@ -36,3 +36,16 @@ def err_stats(got: np.ndarray, want: np.ndarray) -> dict:
     d = np.abs(got - want)
     return {"max_abs": float(d.max()), "mean_abs": float(d.mean()),
             "rel_mean": float(d.mean() / max(np.abs(want).mean(), 1e-300))}
+
+
+def tile_rows(S: int, seed: int, per_tile_random: int = 2, tile: int = 256) -> np.ndarray:
+    """First and last row of every `tile`-row query tile of a sequence, plus
+    `per_tile_random` seeded random rows inside each tile (the ragged last tile
+    included).  Every workgroup of the attention launch owns one such tile, so
+    every workgroup's output is compared."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for t0 in range(0, S, tile):
+        t1 = min(S, t0 + tile)
+        rows += [t0, t1 - 1] + rng.integers(t0, t1, size=per_tile_random).tolist()
+    return np.unique(np.array(rows, dtype=np.int64))

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     lib = dj.lib()
     for name in dj.EXPORTED_SYMBOLS:
         assert getattr(lib, name) is not None
-    assert dj.dit_abi_version() == 3
+    assert dj.dit_abi_version() == 4
 
 
 def _expected_workspace(B, H, S):
@@ -130,6 +130,15 @@ def test_split_entry_points_reject_bad_arguments():
     assert L.dit_attn_core(FAKE, FAKE * 2, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
     assert L.dit_attn_core(FAKE, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, float("nan"), None) == dj.DIT_ERR_INVALID_ARG
     assert L.dit_attn_core(FAKE, None, None, ws, need - 1, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    # core writes key-range partials into its workspace: q and the tables must lie outside it
+    assert L.dit_attn_core(ws + 256, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert "q overlaps" in dj.dit_last_error()
+    assert L.dit_attn_core(FAKE, ws + 512, FAKE * 5, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, FAKE * 5, FAKE * 3 + 64, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, ws + 512, FAKE * 5, ws, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert _fwd(cos=FAKE * 4 + 256, sin=FAKE * 6) == dj.DIT_ERR_INVALID_ARG      # a table inside out
+    if _no_device():                                                             # tables apart: valid
+        assert L.dit_attn_core(FAKE, FAKE * 5, FAKE * 6, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_NO_DEVICE
 
 
 def test_rope_tables_reject_bad_arguments():
@@ -181,6 +190,10 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert L.dit_attn_prepare_kv_fp8(FAKE, FAKE * 2, 0.0, 0.1, None, None, ws, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
     assert L.dit_attn_core_fp8(FAKE, 0.1, None, None, ws, need, FAKE * 3, 1, 2, 8, 96, 0.1, None) == dj.DIT_ERR_UNSUPPORTED
     assert L.dit_attn_core_fp8(FAKE, float("inf"), None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core_fp8(ws + 1024, 0.1, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    if _no_device():                                  # a negative softmax scale is valid (either sign)
+        assert L.dit_attn_core_fp8(FAKE, 0.1, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, -0.1, None) == dj.DIT_ERR_NO_DEVICE
+        assert F(FAKE, FAKE * 2, FAKE * 3, 0.1, 0.1, 0.1, None, None, FAKE * 4, 1, 2, 3, 5, 128, -0.1, None) == dj.DIT_ERR_NO_DEVICE
     if _no_device():
         assert call() == dj.DIT_ERR_NO_DEVICE
 

@@ -24,7 +24,7 @@ import pytest
 import dit_workloads as W
 from oracle import joint_attention, rope_angles
 from oracle.fp8 import dequantize
-from tests.gpu_inputs import err_stats, from_device_bf16, sample_rows
+from tests.gpu_inputs import err_stats, from_device_bf16, sample_rows, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -99,14 +99,46 @@ def test_fp8_whole_ranges_and_key_range_pieces_in_one_launch():
         _assert_close(_run(w, qkv8, split=split), want, f"S={w.S} H={w.H} split={split}")
 
 
-@pytest.mark.parametrize("name,n_random", [("flux2048_fp8", 96), ("video_ulysses4", 32)])
-def test_fp8_sampled_parity_full_size(name, n_random):
-    w = W.get(name)
+def test_fp8_every_element_flux2048():
+    """The fp8 variant of the 2048 x 2048 FLUX shape (24 heads of 16896 tokens)
+    in the benchmark's launch configuration: every output against the oracle
+    on the dequantised inputs."""
+    w = W.get("flux2048_fp8")
     qkv8 = _quantized(w)
     got = _run(w, qkv8)
+    _assert_close(got, _oracle(w, qkv8), f"flux2048_fp8 every element ({got.size} outputs)")
+
+
+def test_fp8_every_query_tile_video_share():
+    """The video head share (10 heads of 76112 tokens) on the fp8 path: first,
+    last and two random rows of every 256-row query tile of every head."""
+    w = W.get("video_ulysses4")
+    (q8, sq), (k8, sk), (v8, sv) = qkv8 = _quantized(w)
+    got = _run(w, qkv8)
     assert np.all(np.isfinite(got))
-    rows = sample_rows(w.S, w.S_txt, n_random, seed=w.seed)
-    _assert_close(got[:, :, rows], _oracle(w, qkv8, rows=rows), f"{name} ({len(rows)} rows)")
+    ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
+    gots, wants = [], []
+    for h in range(w.H):
+        rows = tile_rows(w.S, seed=w.seed * 100 + 50 + h)
+        sl = slice(h, h + 1)
+        wants.append(joint_attention(dequantize(q8[:, sl], sq), dequantize(k8[:, sl], sk), dequantize(v8[:, sl], sv),
+                                     ang, rows=rows))
+        gots.append(got[:, sl][:, :, rows])
+    _assert_close(np.concatenate(gots, axis=2), np.concatenate(wants, axis=2),
+                  f"fp8 video_ulysses4 ({sum(x.shape[2] for x in gots)} rows over {w.H} heads)")
+
+
+@pytest.mark.parametrize("sign", [-1.0, 1.0])
+def test_fp8_scale_of_either_sign(sign):
+    """A negative softmax scale on the fp8 path: the Q re-quantisation step is
+    chosen from the magnitude of scale * log2(e), so Q'' keeps its codes in the
+    normal e4m3 range for either sign.  3 heads of 1000 tokens."""
+    w = W.Workload("edge8", B=1, H=3, D=128, S_txt=24, grid=(16, 61), axes_dim=(64, 64), theta=10000.0, seed=91)
+    qkv8 = _quantized(w)
+    scale = sign / math.sqrt(128)
+    want = _oracle(w, qkv8, scale=scale)
+    for split in (False, True):
+        _assert_close(_run(w, qkv8, split=split, scale=scale), want, f"fp8 scale {scale:+.4f} split={split}")
 
 
 @pytest.mark.parametrize("S_txt,grid,B,H", [(1, (0, 0), 1, 1), (0, (1, 31), 1, 1), (2, (1, 31), 1, 1),

@@ -12,7 +12,7 @@ import pytest
 
 import dit_workloads as W
 from oracle import joint_attention, rope_angles
-from tests.gpu_inputs import bf16_f64, err_stats, from_device_bf16, sample_rows, to_device_bf16
+from tests.gpu_inputs import bf16_f64, err_stats, from_device_bf16, sample_rows, tile_rows, to_device_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -105,17 +105,47 @@ def test_full_parity(name):
     _assert_close(got, want, name)
 
 
-@pytest.mark.parametrize("name,n_random", [("flux2048", 96), ("video_ulysses4", 48)])
-def test_sampled_parity_full_size(name, n_random):
-    """Full-size workloads in the launch configuration the benchmark times;
-    the oracle computes a sample of query rows (each against every key)."""
-    w = W.get(name)
+def test_every_element_flux2048():
+    """The 2048 x 2048 FLUX shape (24 heads of 16896 tokens) in the launch
+    configuration the benchmark times: every one of the B*H*S*D outputs is
+    compared with the oracle (about 3.5e12 flop of float64 on the host)."""
+    w = W.get("flux2048")
     qb, kb, vb = W.make_bf16_inputs(w)
     got = _run(w, qb, kb, vb)
-    assert np.all(np.isfinite(got)), name
-    rows = sample_rows(w.S, w.S_txt, n_random, seed=w.seed)
-    want = _oracle(w, qb, kb, vb, rows=rows)
-    _assert_close(got[:, :, rows], want, f"{name} ({len(rows)} rows x {w.H} heads)")
+    want = _oracle(w, qb, kb, vb)
+    _assert_close(got, want, f"flux2048 every element ({got.size} outputs)")
+
+
+def test_every_query_tile_video_share():
+    """The video head share (10 heads of 76112 tokens): the first, the last and
+    two random rows of every 256-row query tile of every head (so every
+    workgroup of the launch, whole-range and key-range pieces alike, is
+    compared), each row against all keys; random rows differ per head."""
+    w = W.get("video_ulysses4")
+    qb, kb, vb = W.make_bf16_inputs(w)
+    got = _run(w, qb, kb, vb)
+    assert np.all(np.isfinite(got))
+    ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
+    gots, wants = [], []
+    for h in range(w.H):
+        rows = tile_rows(w.S, seed=w.seed * 100 + h)
+        sl = slice(h, h + 1)
+        wants.append(joint_attention(bf16_f64(qb[:, sl]), bf16_f64(kb[:, sl]), bf16_f64(vb[:, sl]), ang, rows=rows))
+        gots.append(got[:, sl][:, :, rows])
+    _assert_close(np.concatenate(gots, axis=2), np.concatenate(wants, axis=2),
+                  f"video_ulysses4 ({sum(x.shape[2] for x in gots)} rows over {w.H} heads)")
+
+
+@pytest.mark.parametrize("sign", [-1.0, 1.0])
+def test_scale_of_either_sign(sign):
+    """The softmax scale is an argument of either sign (a negative one reverses
+    which keys dominate); 3 heads of 1000 tokens with a ragged last tile."""
+    w = _small(24, (16, 61), H=3)
+    qb, kb, vb = W.make_bf16_inputs(w)
+    scale = sign / math.sqrt(128)
+    for split in (False, True):
+        _assert_close(_run(w, qb, kb, vb, scale=scale, split=split), _oracle(w, qb, kb, vb, scale=scale),
+                      f"scale {scale:+.4f} split={split}")
 
 
 def test_longest_supported_sequence():
