@@ -21,7 +21,8 @@ __all__ = [
     "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_kv",
     "dit_attn_core", "dit_attn_workspace_bytes_fp8", "dit_attn_prepare_kv_fp8", "dit_attn_core_fp8",
     "dit_attn_forward_fp8", "dit_attn_core_lse", "dit_attn_merge_lse", "dit_mxfp4_quantize", "dit_mxfp4_gemm",
-    "dit_mxfp4_linear", "dit_dbcache_workspace_bytes", "dit_dbcache_residual_diff", "dit_clock_probe",
+    "dit_mxfp4_linear", "dit_dbcache_workspace_bytes", "dit_dbcache_residual_diff",
+    "dit_dbcache_residual_diff_noalloc", "dit_clock_probe",
     "dit_wall_clock_khz", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
     "DIT_ERR_NO_DEVICE", "DIT_ERR_OUT_OF_MEMORY", "DIT_ERR_LAUNCH", "DIT_DTYPE_BF16",
     "DIT_DTYPE_FP8_E4M3",
@@ -66,6 +67,7 @@ _SIGNATURES = {
     "dit_mxfp4_linear": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
     "dit_dbcache_workspace_bytes": (ctypes.c_size_t, []),
     "dit_dbcache_residual_diff": (_I, [_P, _P, ctypes.c_int64, ctypes.c_double, _P, ctypes.c_size_t, _P, _P, _P]),
+    "dit_dbcache_residual_diff_noalloc": (_I, [_P, _P, ctypes.c_int64, ctypes.c_double, _P, _P, _P]),
     "dit_clock_probe": (_I, [_P, ctypes.c_size_t, _I, _I, _P]),
     "dit_wall_clock_khz": (_I, [ctypes.POINTER(ctypes.c_int)]),
 }
@@ -413,6 +415,29 @@ def dit_dbcache_residual_diff(prev, cur, threshold: float, ws=None, diff=None, r
     _same_gpu(prev=prev, cur=cur, ws=ws, diff=diff, reuse=reuse)
     _check(lib().dit_dbcache_residual_diff(_ptr(prev), _ptr(cur), n, float(threshold), _ptr(ws), ws_bytes,
                                            _ptr(diff), _ptr(reuse), _stream(stream)))
+    return diff, reuse
+
+
+def dit_dbcache_residual_diff_noalloc(prev, cur, threshold: float, diff, reuse=None, stream=None):
+    """dit_dbcache_residual_diff with the library's static scratch instead of a
+    workspace: the library allocates nothing, so ``diff`` (float64, >= 1
+    element) must be given, and ``reuse`` (int32) may be.  Calls that overlap on
+    one GPU share the scratch and race."""
+    _tensor(prev, "prev", ["bfloat16"])
+    _tensor(cur, "cur", ["bfloat16"])
+    n = int(prev.numel())
+    if int(cur.numel()) != n:
+        raise ValueError("prev and cur must have the same number of elements")
+    _tensor(diff, "diff", ["float64"])
+    if diff.numel() < 1:
+        raise ValueError("diff must hold at least one element")
+    if reuse is not None:
+        _tensor(reuse, "reuse", ["int32"])
+        if reuse.numel() < 1:
+            raise ValueError("reuse must hold at least one element")
+    _same_gpu(prev=prev, cur=cur, diff=diff, reuse=reuse)
+    _check(lib().dit_dbcache_residual_diff_noalloc(_ptr(prev), _ptr(cur), n, float(threshold), _ptr(diff),
+                                                   _ptr(reuse), _stream(stream)))
     return diff, reuse
 
 

@@ -26,6 +26,8 @@ hipError_t launch_lse_merge(const void* o_a, const float* lse_a, const void* o_b
                             float* lse_out, int64_t rows, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const void* x, void* codes, void* scales, int64_t rows, int K, hipStream_t stream);
 size_t residual_diff_workspace_bytes();
+size_t residual_diff_scratch_bytes();
+hipError_t residual_diff_scratch(int dev, void** ptr);
 hipError_t launch_clock_probe(int blocks, int iters, void* out, hipStream_t stream);
 hipError_t launch_residual_diff(const void* prev, const void* cur, int64_t n, double threshold, void* ws,
                                 double* diff, int32_t* reuse, hipStream_t stream);
@@ -552,6 +554,36 @@ dit_status_t dit_dbcache_residual_diff(const void* prev, const void* cur, int64_
     if ((st = check_device()) != DIT_OK) return st;
     return launched(dit::launch_residual_diff(prev, cur, n, threshold, ws, diff, reuse, static_cast<hipStream_t>(stream)),
                     "residual_diff kernels");
+}
+
+dit_status_t dit_dbcache_residual_diff_noalloc(const void* prev, const void* cur, int64_t n, double threshold,
+                                               double* diff, int32_t* reuse, void* stream) {
+    if (n < 0) return fail(DIT_ERR_INVALID_ARG, "n must be >= 0 (got %lld)", (long long)n);
+    if (!diff || (n > 0 && (!prev || !cur)))
+        return fail(DIT_ERR_INVALID_ARG, "diff and (for n > 0) prev and cur must be non-NULL");
+    if (n > ((int64_t)1 << 40)) return fail(DIT_ERR_UNSUPPORTED, "n must be at most 2^40 (got %lld)", (long long)n);
+    const size_t need = dit::residual_diff_workspace_bytes();
+    if (need > dit::residual_diff_scratch_bytes())
+        return fail(DIT_ERR_UNSUPPORTED, "the partials need %zu bytes, the static scratch holds %zu", need,
+                    dit::residual_diff_scratch_bytes());
+    if (!aligned16(prev) || !aligned16(cur)) return fail(DIT_ERR_INVALID_ARG, "prev and cur must be 16-byte aligned");
+    if (!aligned(diff, 8) || (reuse && !aligned(reuse, 4)))
+        return fail(DIT_ERR_INVALID_ARG, "diff must be 8-byte and reuse 4-byte aligned");
+    const size_t nb = (size_t)n * 2;
+    if (overlaps(diff, 8, prev, nb) || overlaps(diff, 8, cur, nb) ||
+        (reuse && (overlaps(reuse, 4, prev, nb) || overlaps(reuse, 4, cur, nb) || overlaps(reuse, 4, diff, 8))))
+        return fail(DIT_ERR_INVALID_ARG, "diff or reuse overlaps an input or the other output");
+    dit_status_t st;
+    if ((st = check_device()) != DIT_OK) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(DIT_ERR_NO_DEVICE, "hipGetDevice failed");
+    void* scratch = nullptr;
+    const hipError_t e = dit::residual_diff_scratch(dev, &scratch);
+    if (e != hipSuccess)
+        return fail(DIT_ERR_LAUNCH, "address of the static scratch on device %d: %s", dev, hipGetErrorString(e));
+    return launched(dit::launch_residual_diff(prev, cur, n, threshold, scratch, diff, reuse,
+                                              static_cast<hipStream_t>(stream)),
+                    "residual_diff kernels (static scratch)");
 }
 
 // ---------------------------------------------------------------- clock probe

@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "gfx950.h"
 
@@ -137,6 +138,36 @@ int residual_diff_blocks(int64_t n) {
 }
 
 size_t residual_diff_workspace_bytes() { return (size_t)RD_MAX_BLOCKS * sizeof(double2); }
+
+// Scratch of the allocation-free entry point: room for the (num, den) pair of
+// every workgroup the partials launch can have (128 KiB).  Each GPU the
+// library runs on holds its own copy until the process ends; calls on one GPU
+// share it, so overlapping calls there race.  Nothing in it needs clearing:
+// the finish kernel reads only the pairs the partials kernel of the same call
+// wrote.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address comes from residual_diff_scratch().
+static __device__ __align__(256) double2 scratch[RD_MAX_BLOCKS];
+
+size_t residual_diff_scratch_bytes() { return sizeof(scratch); }
+
+// Device address of `scratch` on device `dev`, which must be the current
+// device: looked up once per device with hipGetSymbolAddress and kept.
+hipError_t residual_diff_scratch(int dev, void** ptr) {
+    constexpr int kDevices = 64;
+    static std::mutex mu;
+    static void* addr[kDevices];
+    if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_residual_diff(const void* prev, const void* cur, int64_t n, double threshold, void* ws,
                                 double* diff, int32_t* reuse, hipStream_t stream) {

@@ -283,6 +283,22 @@ dit_status_t dit_dbcache_residual_diff(const void* prev, const void* cur, int64_
                                        void* ws, size_t ws_bytes, double* diff, int32_t* reuse, void* stream);
 
 /*
+ * dit_dbcache_residual_diff_noalloc - dit_dbcache_residual_diff for callers
+ *   that cannot allocate device memory (code under HIP graph capture, tight
+ *   serving loops, harnesses that forbid hipMalloc): the same kernels and the
+ *   same result, bit for bit, but the per-workgroup partial sums go to a
+ *   static device array of the library (128 KiB per GPU, the most the
+ *   partials launch can use for any n, held until the process ends) instead
+ *   of a caller workspace.  Arguments and errors as in
+ *   dit_dbcache_residual_diff without ws / ws_bytes.  The call makes no
+ *   allocation of its own.  All calls on one GPU share that array: calls that
+ *   may overlap on one GPU (different streams, or different threads) race and
+ *   must be serialised by the caller; it needs no clearing between calls.
+ */
+dit_status_t dit_dbcache_residual_diff_noalloc(const void* prev, const void* cur, int64_t n, double threshold,
+                                               double* diff, int32_t* reuse, void* stream);
+
+/*
  * Clock probe (measurement aid, not part of the attention path).  The
  * published MI355X peaks assume a 2.4 GHz shader clock; under a sustained
  * matrix-core load the chip runs slower, and a roofline can also be priced at

@@ -286,6 +286,20 @@ def test_dbcache_entry_point_rejects_bad_arguments():
         assert f() == dj.DIT_ERR_NO_DEVICE
         assert f(n=0, r=None) == dj.DIT_ERR_NO_DEVICE                     # empty residuals are valid
         assert f(n=0, p=None, c=None) == dj.DIT_ERR_NO_DEVICE             # ... also as NULL pointers
+    # the allocation-free variant: the same checks, minus the workspace
+    na = lambda **kw: L.dit_dbcache_residual_diff_noalloc(kw.get("p", p), kw.get("c", c), kw.get("n", 1000), 0.12,
+                                                          kw.get("d", d), kw.get("r", r), None)
+    assert na(p=None) == dj.DIT_ERR_INVALID_ARG
+    assert na(d=None) == dj.DIT_ERR_INVALID_ARG
+    assert na(n=-1) == dj.DIT_ERR_INVALID_ARG
+    assert na(n=2 ** 40 + 1) == dj.DIT_ERR_UNSUPPORTED
+    assert na(c=c + 2) == dj.DIT_ERR_INVALID_ARG                          # misaligned input
+    assert na(d=d + 4) == dj.DIT_ERR_INVALID_ARG                          # misaligned diff
+    assert na(d=c + 16) == dj.DIT_ERR_INVALID_ARG                         # diff inside cur
+    assert na(r=d + 4) == dj.DIT_ERR_INVALID_ARG                          # reuse over diff
+    if _no_device():
+        assert na() == dj.DIT_ERR_NO_DEVICE
+        assert na(n=0, p=None, c=None, r=None) == dj.DIT_ERR_NO_DEVICE
 
 
 def test_clock_probe_rejects_bad_arguments():
