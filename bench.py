@@ -1,7 +1,7 @@
 """Benchmark: joint self-attention TFLOP/s on one MI355X.
 
 One step = one whole pass of the path over one batch of synthetic input:
-RoPE on K + tile preparation (dit_attn_prepare_kv) and the attention kernel
+RoPE on K + its tile layout (dit_attn_prepare_k) and the attention kernel
 with RoPE on Q fused into its prologue (dit_attn_core), i.e. the work of
 dit_attn_forward.  RoPE tables are built once per resolution (outside the
 step), as a DiT reuses them across all blocks and denoising steps.
@@ -132,10 +132,11 @@ def copy_calibration(args, torch):
 
 
 def ws_bytes_tiles(w, fp8):
-    """Bytes of prepared K'/V^T tiles the attention kernel streams: 64-key tiles of
-    35840 B (bf16) or 19456 B (fp8, plus its 256 B scale header) per (b, h)."""
+    """Bytes of prepared tiles the attention kernel streams: 64-key K' tiles of
+    17408 B (bf16; V is read as it is) or K'/V^T tiles of 19456 B (fp8, plus its
+    256 B scale header) per (b, h)."""
     tiles = w.B * w.H * ((w.S + 63) // 64)
-    return tiles * 19456 + 256 if fp8 else tiles * 35840
+    return tiles * 19456 + 256 if fp8 else tiles * 17408
 
 
 def bf16_dev(bits, torch):
@@ -241,9 +242,9 @@ def ring_bench(args, w, torch, dj):
     def step(ev):
         for b in range(P):
             ev.append(torch.cuda.Event(enable_timing=True)); ev[-1].record(stream)
-            dj.dit_attn_prepare_kv(kbk[b], vbk[b], tabs[b][0], tabs[b][1], ws[b], ws_bytes, stream=stream)
+            dj.dit_attn_prepare_k(kbk[b], tabs[b][0], tabs[b][1], ws[b], ws_bytes, stream=stream)
             ev.append(torch.cuda.Event(enable_timing=True)); ev[-1].record(stream)
-            dj.dit_attn_core_lse(qs, tabs[0][0], tabs[0][1], ws[b], outs[b], lses[b], scale=scale,
+            dj.dit_attn_core_lse(qs, vbk[b], tabs[0][0], tabs[0][1], ws[b], outs[b], lses[b], scale=scale,
                                  workspace_bytes=ws_bytes, stream=stream)
             ev.append(torch.cuda.Event(enable_timing=True)); ev[-1].record(stream)
             if b > 0:
@@ -497,9 +498,12 @@ def main():
     achieved = flops / (core_avg * 1e-3) / 1e12
     tensor_bytes = w.B * w.H * w.S * w.D * (1 if fp8 else 2)
     # read Q, the prepared tiles and the two tables; write the bf16 output
-    core_bytes = tensor_bytes + ws_bytes_tiles(w, fp8) + 2 * w.S * (w.D // 2) * 4 + w.B * w.H * w.S * w.D * 2
-    # read K, V, cos, sin; write the prepared tiles
-    prep_bytes = 2 * tensor_bytes + 2 * w.S * (w.D // 2) * 4 + ws_bytes_tiles(w, fp8)
+    tables = 2 * w.S * (w.D // 2) * 4
+    # core: read Q, the prepared tiles (bf16: K' only, plus V as it is) and the two tables; write the bf16 output
+    core_bytes = (tensor_bytes + ws_bytes_tiles(w, fp8) + (0 if fp8 else tensor_bytes) + tables
+                  + w.B * w.H * w.S * w.D * 2)
+    # preparation: read K (fp8: and V) and the tables; write the prepared tiles
+    prep_bytes = (2 if fp8 else 1) * tensor_bytes + tables + ws_bytes_tiles(w, fp8)
     rec = {
         "metric": METRIC,
         "value": flops / (step_ms * 1e-3) / 1e12,
@@ -584,8 +588,8 @@ class AttentionRun:
             self.out = out = torch.empty_like(q)
             ws_bytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
             ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-            self.prep = lambda: dj.dit_attn_prepare_kv(k, v, cos, sin, ws, ws_bytes, stream=stream)
-            self.core = lambda: dj.dit_attn_core(q, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes,
+            self.prep = lambda: dj.dit_attn_prepare_k(k, cos, sin, ws, ws_bytes, stream=stream)
+            self.core = lambda: dj.dit_attn_core(q, v, cos, sin, ws, out, scale=scale, workspace_bytes=ws_bytes,
                                                  stream=stream)
             self.forward = lambda: dj.dit_attn_forward(q, k, v, cos, sin, out=out, S_txt=w.S_txt, scale=scale)
             self.f64_head = lambda h: tuple(W.bf16_bits_to_f32(b[:, h:h + 1]).astype(np.float64) for b in (qb, kb, vb))

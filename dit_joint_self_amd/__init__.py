@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the path runs in the library's HIP
 kernels.  Functions keep the C names (``dit_attn_forward``, ``dit_rope_tables``,
-``dit_attn_workspace_bytes``, ``dit_attn_prepare_kv``, ``dit_attn_core``,
+``dit_attn_workspace_bytes``, ``dit_attn_prepare_k``, ``dit_attn_core``,
 ``dit_attn_core_lse``, ``dit_attn_merge_lse``, the ``_fp8`` entries, the
 MXFP4 linear-layer entries and the DBCache decision) and
 take torch tensors, whose device pointers are passed after the checks the
@@ -18,7 +18,7 @@ from typing import Optional, Sequence
 
 __all__ = [
     "LIB_PATH", "DitAttnError", "lib", "lib_loaded", "dit_last_error", "dit_abi_version",
-    "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_kv",
+    "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_k",
     "dit_attn_core", "dit_attn_workspace_bytes_fp8", "dit_attn_prepare_kv_fp8", "dit_attn_core_fp8",
     "dit_attn_forward_fp8", "dit_attn_core_lse", "dit_attn_merge_lse", "dit_mxfp4_quantize", "dit_mxfp4_gemm",
     "dit_mxfp4_linear", "dit_dbcache_workspace_bytes", "dit_dbcache_residual_diff",
@@ -54,13 +54,13 @@ _SIGNATURES = {
     "dit_rope_tables": (_I, [_P, _I, _I, ctypes.POINTER(ctypes.c_int32), _F, _P, _P, _P]),
     "dit_attn_forward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "dit_attn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
-    "dit_attn_prepare_kv": (_I, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P]),
-    "dit_attn_core": (_I, [_P, _P, _P, _P, ctypes.c_size_t, _P, _I, _I, _I, _I, _F, _P]),
+    "dit_attn_prepare_k": (_I, [_P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P]),
+    "dit_attn_core": (_I, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P, _I, _I, _I, _I, _F, _P]),
     "dit_attn_workspace_bytes_fp8": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "dit_attn_prepare_kv_fp8": (_I, [_P, _P, _F, _F, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P]),
     "dit_attn_core_fp8": (_I, [_P, _F, _P, _P, _P, ctypes.c_size_t, _P, _I, _I, _I, _I, _F, _P]),
     "dit_attn_forward_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
-    "dit_attn_core_lse": (_I, [_P, _P, _P, _P, ctypes.c_size_t, _P, _P, _I, _I, _I, _I, _F, _P]),
+    "dit_attn_core_lse": (_I, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _I, _I, _I, _I, _F, _P]),
     "dit_attn_merge_lse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dit_mxfp4_quantize": (_I, [_P, _P, _P, _I, _I, _P]),
     "dit_mxfp4_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
@@ -264,35 +264,38 @@ def dit_attn_workspace_bytes(B: int, H: int, S: int, D: int) -> int:
     return int(lib().dit_attn_workspace_bytes(B, H, S, D))
 
 
-def dit_attn_prepare_kv(k, v, rope_cos, rope_sin, workspace, workspace_bytes: Optional[int] = None, stream=None):
-    B, H, S, D = shp = _bhsd(k, "k", ["bfloat16"])
-    _tensor(v, "v", ["bfloat16"], shape=shp)
+def dit_attn_prepare_k(k, rope_cos, rope_sin, workspace, workspace_bytes: Optional[int] = None, stream=None):
+    """RoPE on K and its tile layout, into the caller's workspace (V is not prepared)."""
+    B, H, S, D = _bhsd(k, "k", ["bfloat16"])
     _tables(rope_cos, rope_sin, S, D)
     workspace_bytes = _workspace(workspace, workspace_bytes)
-    _same_gpu(k=k, v=v, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace)
-    _check(lib().dit_attn_prepare_kv(_ptr(k), _ptr(v), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace),
-                                     int(workspace_bytes), B, H, S, D, _stream(stream)))
+    _same_gpu(k=k, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace)
+    _check(lib().dit_attn_prepare_k(_ptr(k), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace),
+                                    int(workspace_bytes), B, H, S, D, _stream(stream)))
 
 
-def dit_attn_core(q, rope_cos, rope_sin, workspace, out, scale: Optional[float] = None,
+def dit_attn_core(q, v, rope_cos, rope_sin, workspace, out, scale: Optional[float] = None,
                   workspace_bytes: Optional[int] = None, stream=None):
+    """Attention of q against the keys prepared in `workspace` and the values v."""
     B, H, S, D = shp = _bhsd(q, "q", ["bfloat16"])
+    _tensor(v, "v", ["bfloat16"], shape=shp)
     _tables(rope_cos, rope_sin, S, D)
     _tensor(out, "out", ["bfloat16"], shape=shp)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     workspace_bytes = _workspace(workspace, workspace_bytes)
-    _same_gpu(q=q, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace, out=out)
-    _check(lib().dit_attn_core(_ptr(q), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace), int(workspace_bytes),
-                               _ptr(out), B, H, S, D, float(scale), _stream(stream)))
+    _same_gpu(q=q, v=v, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace, out=out)
+    _check(lib().dit_attn_core(_ptr(q), _ptr(v), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace),
+                               int(workspace_bytes), _ptr(out), B, H, S, D, float(scale), _stream(stream)))
     return out
 
 
-def dit_attn_core_lse(q, rope_cos, rope_sin, workspace, out, lse=None, scale: Optional[float] = None,
+def dit_attn_core_lse(q, v, rope_cos, rope_sin, workspace, out, lse=None, scale: Optional[float] = None,
                       workspace_bytes: Optional[int] = None, stream=None):
     """dit_attn_core plus the row log-sum-exp [B, H, S] fp32 (allocated when not given); returns (out, lse)."""
     import torch
     B, H, S, D = shp = _bhsd(q, "q", ["bfloat16"])
+    _tensor(v, "v", ["bfloat16"], shape=shp)
     _tables(rope_cos, rope_sin, S, D)
     _tensor(out, "out", ["bfloat16"], shape=shp)
     if scale is None:
@@ -301,9 +304,10 @@ def dit_attn_core_lse(q, rope_cos, rope_sin, workspace, out, lse=None, scale: Op
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     _tensor(lse, "lse", ["float32"], shape=(B, H, S))
-    _same_gpu(q=q, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace, out=out, lse=lse)
-    _check(lib().dit_attn_core_lse(_ptr(q), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace), int(workspace_bytes),
-                                   _ptr(out), _ptr(lse), B, H, S, D, float(scale), _stream(stream)))
+    _same_gpu(q=q, v=v, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace, out=out, lse=lse)
+    _check(lib().dit_attn_core_lse(_ptr(q), _ptr(v), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace),
+                                   int(workspace_bytes), _ptr(out), _ptr(lse), B, H, S, D, float(scale),
+                                   _stream(stream)))
     return out, lse
 
 

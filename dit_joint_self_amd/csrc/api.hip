@@ -20,8 +20,8 @@
 #include "tile_layout.h"
 
 namespace dit {
-hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, const float* sin_t,
-                             void* ws, int BH, int S, hipStream_t stream);
+hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_t, void* ws, int BH, int S,
+                            hipStream_t stream);
 hipError_t launch_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* out,
                             float* lse_out, int64_t rows, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const void* x, void* codes, void* scales, int64_t rows, int K, hipStream_t stream);
@@ -33,8 +33,8 @@ hipError_t launch_residual_diff(const void* prev, const void* cur, int64_t n, do
                                 double* diff, int32_t* reuse, hipStream_t stream);
 hipError_t launch_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
                              void* out, int M, int N, int K, hipStream_t stream);
-hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
-                            void* out, float* lse, int BH, int S, float qmul, hipStream_t stream);
+hipError_t launch_attn_core(const void* q, const void* v, const float* cos_t, const float* sin_t, const void* ws,
+                            void* part, void* out, float* lse, int BH, int S, float qmul, hipStream_t stream);
 size_t core_partial_bytes(int BH, int S);
 hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_t, const float* sin_t, void* ws,
                                  int BH, int S, float k_scale, float v_scale, hipStream_t stream);
@@ -47,7 +47,7 @@ hipError_t launch_rope_tables(const int32_t* pos, int S, int n_axes, const int32
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int kMaxDevices = 64;
 // Smallest query tile any kernel variant uses; bounds the workgroup count.
 constexpr int kMinBlockM = 128;
@@ -179,10 +179,10 @@ dit_status_t dit_rope_tables(const int32_t* pos, int S, int n_axes, const int32_
                     "rope_tables_kernel");
 }
 
-// Workspace: the K/V tile stream, then (256-byte aligned) the key-range
+// Workspace: the K' tile stream, then (256-byte aligned) the key-range
 // partials of the items that run split.
 static size_t tiles_bytes(int B, int H, int S) {
-    return ((size_t)B * H * (size_t)dit::num_kv_tiles(S) * dit::TILE_BYTES + 255) & ~(size_t)255;
+    return ((size_t)B * H * (size_t)dit::num_kv_tiles(S) * dit::K_PART_BYTES + 255) & ~(size_t)255;
 }
 
 size_t dit_attn_workspace_bytes(int B, int H, int S, int D) {
@@ -191,75 +191,75 @@ size_t dit_attn_workspace_bytes(int B, int H, int S, int D) {
     return tiles_bytes(B, H, S) + dit::core_partial_bytes(B * H, S);
 }
 
-dit_status_t dit_attn_prepare_kv(const void* k, const void* v, const float* rope_cos, const float* rope_sin,
-                                 void* workspace, size_t workspace_bytes, int B, int H, int S, int D,
-                                 void* stream) {
-    if (!k || !v || !workspace) return fail(DIT_ERR_INVALID_ARG, "k, v and workspace must be non-NULL");
+dit_status_t dit_attn_prepare_k(const void* k, const float* rope_cos, const float* rope_sin, void* workspace,
+                                size_t workspace_bytes, int B, int H, int S, int D, void* stream) {
+    if (!k || !workspace) return fail(DIT_ERR_INVALID_ARG, "k and workspace must be non-NULL");
     dit_status_t st = check_shape(B, H, S, D);
     if (st != DIT_OK) return st;
     if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
-    if (!aligned16(k) || !aligned16(v)) return fail(DIT_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    if (!aligned16(k)) return fail(DIT_ERR_INVALID_ARG, "k must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(DIT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     const size_t need = dit_attn_workspace_bytes(B, H, S, D);
     if (workspace_bytes < need)
         return fail(DIT_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
     const size_t tbytes = (size_t)B * H * S * D * 2;
-    if (overlaps(workspace, need, k, tbytes) || overlaps(workspace, need, v, tbytes))
-        return fail(DIT_ERR_INVALID_ARG, "workspace overlaps k or v");
+    if (overlaps(workspace, need, k, tbytes)) return fail(DIT_ERR_INVALID_ARG, "workspace overlaps k");
     if ((st = check_tables_apart(rope_cos, rope_sin, S, workspace, need, nullptr, 0)) != DIT_OK) return st;
     if ((st = check_device()) != DIT_OK) return st;
-    return launched(dit::launch_prepare_kv(k, v, rope_cos, rope_sin, workspace, B * H, S,
-                                           static_cast<hipStream_t>(stream)),
-                    "prepare_kv_kernel");
+    return launched(dit::launch_prepare_k(k, rope_cos, rope_sin, workspace, B * H, S,
+                                          static_cast<hipStream_t>(stream)),
+                    "prepare_k_kernel");
 }
 
-static dit_status_t core_impl(const void* q, const float* rope_cos, const float* rope_sin, void* workspace,
-                              size_t workspace_bytes, void* out, float* lse, int B, int H, int S, int D, float scale,
-                              void* stream) {
-    if (!q || !workspace || !out) return fail(DIT_ERR_INVALID_ARG, "q, workspace and out must be non-NULL");
+static dit_status_t core_impl(const void* q, const void* v, const float* rope_cos, const float* rope_sin,
+                              void* workspace, size_t workspace_bytes, void* out, float* lse, int B, int H, int S,
+                              int D, float scale, void* stream) {
+    if (!q || !v || !workspace || !out) return fail(DIT_ERR_INVALID_ARG, "q, v, workspace and out must be non-NULL");
     dit_status_t st = check_shape(B, H, S, D);
     if (st != DIT_OK) return st;
     if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
     if (!std::isfinite(scale)) return fail(DIT_ERR_INVALID_ARG, "scale must be finite");
-    if (!aligned16(q) || !aligned16(out)) return fail(DIT_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+    if (!aligned16(q) || !aligned16(v) || !aligned16(out))
+        return fail(DIT_ERR_INVALID_ARG, "q, v and out must be 16-byte aligned");
     const size_t need = dit_attn_workspace_bytes(B, H, S, D);
     if (workspace_bytes < need)
         return fail(DIT_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
     const size_t tbytes = (size_t)B * H * S * D * 2;
-    if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, workspace, need))
-        return fail(DIT_ERR_INVALID_ARG, "out overlaps q or the workspace");
+    if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, v, tbytes) || overlaps(out, tbytes, workspace, need))
+        return fail(DIT_ERR_INVALID_ARG, "out overlaps q, v or the workspace");
     // The call writes key-range partials into the workspace while other
-    // workgroups still read q and the tables.
-    if (overlaps(q, tbytes, workspace, need)) return fail(DIT_ERR_INVALID_ARG, "q overlaps the workspace");
+    // workgroups still read q, v and the tables.
+    if (overlaps(q, tbytes, workspace, need) || overlaps(v, tbytes, workspace, need))
+        return fail(DIT_ERR_INVALID_ARG, "q or v overlaps the workspace");
     if ((st = check_tables_apart(rope_cos, rope_sin, S, workspace, need, out, tbytes)) != DIT_OK) return st;
     if (lse) {
         const size_t lbytes = (size_t)B * H * S * 4;
         if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(DIT_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-        if (overlaps(lse, lbytes, out, tbytes) || overlaps(lse, lbytes, q, tbytes) ||
+        if (overlaps(lse, lbytes, out, tbytes) || overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, v, tbytes) ||
             overlaps(lse, lbytes, workspace, need))
-            return fail(DIT_ERR_INVALID_ARG, "lse overlaps q, out or the workspace");
+            return fail(DIT_ERR_INVALID_ARG, "lse overlaps q, v, out or the workspace");
         if ((st = check_tables_apart(rope_cos, rope_sin, S, lse, lbytes, nullptr, 0)) != DIT_OK) return st;
     }
     if ((st = check_device()) != DIT_OK) return st;
     const float qmul = (float)((double)scale * 1.4426950408889634073599);  // scale * log2(e)
     void* part = static_cast<char*>(workspace) + tiles_bytes(B, H, S);
-    return launched(dit::launch_attn_core(q, rope_cos, rope_sin, workspace, part, out, lse, B * H, S, qmul,
+    return launched(dit::launch_attn_core(q, v, rope_cos, rope_sin, workspace, part, out, lse, B * H, S, qmul,
                                           static_cast<hipStream_t>(stream)),
                     "attn_core_kernel");
 }
 
-dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin, void* workspace,
-                           size_t workspace_bytes, void* out, int B, int H, int S, int D, float scale,
+dit_status_t dit_attn_core(const void* q, const void* v, const float* rope_cos, const float* rope_sin,
+                           void* workspace, size_t workspace_bytes, void* out, int B, int H, int S, int D, float scale,
                            void* stream) {
-    return core_impl(q, rope_cos, rope_sin, workspace, workspace_bytes, out, nullptr, B, H, S, D, scale, stream);
+    return core_impl(q, v, rope_cos, rope_sin, workspace, workspace_bytes, out, nullptr, B, H, S, D, scale, stream);
 }
 
-dit_status_t dit_attn_core_lse(const void* q, const float* rope_cos, const float* rope_sin, void* workspace,
-                               size_t workspace_bytes, void* out, float* lse, int B, int H, int S, int D,
-                               float scale, void* stream) {
+dit_status_t dit_attn_core_lse(const void* q, const void* v, const float* rope_cos, const float* rope_sin,
+                               void* workspace, size_t workspace_bytes, void* out, float* lse, int B, int H, int S,
+                               int D, float scale, void* stream) {
     if (!lse) return fail(DIT_ERR_INVALID_ARG, "lse must be non-NULL");
-    return core_impl(q, rope_cos, rope_sin, workspace, workspace_bytes, out, lse, B, H, S, D, scale, stream);
+    return core_impl(q, v, rope_cos, rope_sin, workspace, workspace_bytes, out, lse, B, H, S, D, scale, stream);
 }
 
 // Two regions either coincide exactly (an allowed in-place fold) or are disjoint.
@@ -434,10 +434,10 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const
         (void)hipGetLastError();
         return fail(DIT_ERR_OUT_OF_MEMORY, "hipMallocAsync of %zu workspace bytes failed", need);
     }
-    hipError_t e = dit::launch_prepare_kv(k, v, rope_cos, rope_sin, ws, B * H, S, s);
+    hipError_t e = dit::launch_prepare_k(k, rope_cos, rope_sin, ws, B * H, S, s);
     if (e == hipSuccess) {
         const float qmul = (float)((double)scale * 1.4426950408889634073599);
-        e = dit::launch_attn_core(q, rope_cos, rope_sin, ws, static_cast<char*>(ws) + tiles_bytes(B, H, S), out,
+        e = dit::launch_attn_core(q, v, rope_cos, rope_sin, ws, static_cast<char*>(ws) + tiles_bytes(B, H, S), out,
                                   nullptr, B * H, S, qmul, s);
     }
     const hipError_t ef = hipFreeAsync(ws, s);

@@ -20,7 +20,8 @@ constexpr float LN2 = 0.693147180559945309f;
 // Longest sequence the kernels accept: keeps every byte offset inside one
 // (batch, head) slice of prepared tiles below 2^31.
 constexpr int MAX_SEQ = 1 << 21;
-static_assert((int64_t)((MAX_SEQ + KV_TILE - 1) / KV_TILE) * TILE_BYTES < (int64_t)1 << 31, "slice offsets fit");
+static_assert((int64_t)((MAX_SEQ + KV_TILE - 1) / KV_TILE) * K_PART_BYTES < (int64_t)1 << 31, "slice offsets fit");
+static_assert((int64_t)MAX_SEQ * V_ROW_BYTES < (int64_t)1 << 31, "V offsets of one head fit");
 
 // Partial results of one key-range workgroup: O (unnormalised, fp32, row-major
 // [BM][128]), then the offset m (base 2) and the weight sum l of each row.

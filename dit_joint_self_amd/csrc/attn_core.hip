@@ -13,11 +13,11 @@
 //   * Q prologue: each lane loads its query row's 8-dim chunks, applies RoPE
 //     and the factor scale*log2(e) in fp32 and keeps them as bf16 MFMA
 //     B operands for the whole kernel (Q-tile resident in VGPRs).
-//   * K/V stream: 64-key tiles already rotated and laid out by
-//     prepare_kv.hip, copied HBM -> LDS by buffer_load_dwordx4 ... lds into
-//     four K' and four V^T buffers (K' three tiles ahead, V^T two), one
-//     barrier per two tiles; the copies of a step are issued one at a time
-//     between its MFMAs.
+//   * K/V stream: 64-key tiles, K' already rotated and laid out by
+//     prepare_kv.hip, V straight from the caller's tensor; both copied
+//     HBM -> LDS by buffer_load_dwordx4 ... lds into four K' and four V
+//     buffers (K' three tiles ahead, V two), one barrier per two tiles; the
+//     copies of a step are issued one at a time between its MFMAs.
 //   * Software pipeline per wave: the QK^T MFMAs of tile j+1 run beside the
 //     exp2 / bf16 / row-sum work of tile j, then O += P V for tile j.
 //   * S^T = K' Q'^T on v_mfma_f32_32x32x16_bf16: lane (n, hh) of the
@@ -31,7 +31,8 @@
 //     weight_pair and settle_weights).  Weights stay <= 2^20, so fp32 and bf16 hold them with
 //     their usual relative precision, and the final O / l is unchanged.
 //   * O^T += V^T P^T on the same MFMA: P leaves the S accumulator already in
-//     B-operand layout (see tile_layout.h), V^T comes from LDS.
+//     B-operand layout (see tile_layout.h); the V^T A operand is read from
+//     the key-major V tile with the transposing LDS read ds_read_b64_tr_b16.
 //   * Epilogue: combine the two half-wave partial sums, scale by 1/l, round to
 //     bf16, store rows < S.
 //
@@ -73,13 +74,34 @@ constexpr float SUM_LIMIT = 1048576.0f;  // 2^20
 // MFMA operand ring: LDS reads run RING - 1 MFMA steps ahead of their use.
 constexpr int RING = 4;
 
-// K' operand of QK^T step i (dim step i >> 1, key block i & 1) and V^T operand
-// of PV step i (16-key step i >> 2, dim block i & 3), for lane (n, hh).
+// K' operand of QK^T step i (dim step i >> 1, key block i & 1), for lane (n, hh).
 __device__ __forceinline__ bf16x8 k_operand(const uint4* kt, int i, int n, int hh) {
     return as_bf16x8(kt[k_chunk((i & 1) * 32 + n, 2 * (i >> 1) + hh)]);
 }
-__device__ __forceinline__ bf16x8 v_operand(const uint4* vt, int i, int n, int hh) {
-    return as_bf16x8(vt[v_chunk((i & 3) * 32 + n, 2 * (i >> 2) + hh)]);
+
+// V^T operand of PV step i (16-key step u = i >> 2, dim block db = i & 3):
+// lane (n, hh) needs V[16u + 8hh + t][32 db + n], t = 0..7, as bf16x8.  Two
+// ds_read_b64_tr_b16 (t = 0..3, then 4..7): in each 16-lane group (lanes 16g
+// .. 16g + 15: n0 = 16 (g & 1), hh = g >> 1) the transposing read hands
+// result lane i the element i % 4 of source lanes i / 4 + 4 j, j = 0..3, so
+// source lane s = 4 j + a reads the four dims 32 db + n0 + 4a .. + 3 of key
+// 16u + 8hh + 4h + j.  `vlane` is the lane's byte offset for u = db = h = 0
+// (v_lane_offset); the rest is a compile-time offset.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ int v_lane_offset(int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    return v_lds_byte(8 * (g >> 1) + (s >> 2), 16 * (g & 1) + 4 * (s & 3));
+}
+__device__ __forceinline__ bf16x8 v_operand(const uint4* vt, int i, int vlane) {
+    const int u = i >> 2, db = i & 3;
+    const char* base = reinterpret_cast<const char*>(vt) + vlane + u * V_ROW_BYTES + 64 * db;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * V_PIECE_BYTES));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
 }
 
 // Two weights of score pair p (0..15) of the current tile: pair p of key
@@ -99,30 +121,40 @@ __device__ __forceinline__ void weight_pair(const f32x16 (&sc)[2], int p, uint32
     asm volatile("" : "+v"(w[p]), "+v"(sum));
 }
 
+// Piece p of a V tile: lane l moves 16 bytes of key p + 16 (l >> 4), chunk
+// l & 15, from V (tile byte offset vtoff) to the piece's l-th LDS chunk.
+// vgather is the lane's source offset inside the tile for p = 0
+// (v_gather_offset); rows past S read as zeros.
+__device__ __forceinline__ int v_gather_offset(int lane) { return (lane >> 4) * 16 * V_ROW_BYTES + (lane & 15) * 16; }
+__device__ __forceinline__ void v_piece(__amdgpu_buffer_rsrc_t vrsrc, int vtoff, int p, uint4* vdst, int vgather) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (__attribute__((address_space(3))) void*)(vdst + p * V_PIECE_CHUNKS),
+                                             16, vgather, vtoff + p * V_ROW_BYTES, 0, 0);
+}
+
 // The tile copies one pipelined step issues, spread over stage A: piece j of
-// the K' part three tiles ahead at step 2j + 1, piece j of the V^T part two
+// the K' part three tiles ahead at step 2j + 1, piece j of the V tile two
 // tiles ahead at step 2 (KJ + j) + 1.  Issued one at a time between MFMAs
 // instead of in a burst after the barrier, the copies do not hold up the
 // wave's first MFMAs.
 struct TileCopies {
     static constexpr int KJ = (K_PART_CHUNKS / 64 + NW - 1) / NW;  // K' pieces per wave (at most)
-    static constexpr int VJ = (V_PART_CHUNKS / 64 + NW - 1) / NW;  // V^T pieces per wave (at most)
-    __amdgpu_buffer_rsrc_t rsrc;
-    int ksoff, vsoff;  // byte offsets of the two parts in the slice
+    static constexpr int VJ = (V_PIECES + NW - 1) / NW;            // V pieces per wave (at most)
+    __amdgpu_buffer_rsrc_t krsrc, vrsrc;
+    int ksoff, vsoff;  // byte offsets of the K' tile in the workspace slice, of the V tile in the head's V
     uint4* kdst;
     uint4* vdst;
-    bool kon;          // the K' part exists (wave-uniform)
-    bool von;          // the V^T part exists (wave-uniform)
-    int wave, lane;
+    bool kon;          // the K' tile exists (wave-uniform)
+    bool von;          // the V tile exists (wave-uniform)
+    int wave, lane, vgather;
     __device__ __forceinline__ void at_step(int i) const {
         if ((i & 1) == 0) return;
         const int j = i >> 1;
         if (j < KJ) {
             const int p = j * NW + wave;
-            if (kon && p < K_PART_CHUNKS / 64) lds_piece(rsrc, ksoff + p * 1024, kdst + p * 64, lane);
+            if (kon && p < K_PART_CHUNKS / 64) lds_piece(krsrc, ksoff + p * 1024, kdst + p * 64, lane);
         } else if (j < KJ + VJ) {
             const int p = (j - KJ) * NW + wave;
-            if (von && p < V_PART_CHUNKS / 64) lds_piece(rsrc, vsoff + p * 1024, vdst + p * 64, lane);
+            if (von && p < V_PIECES) v_piece(vrsrc, vsoff, p, vdst, vgather);
         }
     }
 };
@@ -203,47 +235,47 @@ __device__ __forceinline__ void settle_weights(f32x16 (&sc)[2], f32x16 (&sn)[2],
     lsum += sum;
 }
 
-// Stage B: O^T += V^T P^T over the tile's 64 keys (V^T part vt): 16 MFMA steps;
+// Stage B: O^T += V^T P^T over the tile's 64 keys (V tile vt): 16 MFMA steps;
 // the weights of 16-key step u are w[4u .. 4u + 3], already in B-operand order.
-__device__ __forceinline__ void stage_b(const uint4* vt, const uint32_t (&w)[16], f32x16 (&o)[4], int n, int hh) {
+__device__ __forceinline__ void stage_b(const uint4* vt, const uint32_t (&w)[16], f32x16 (&o)[4], int vlane) {
     bf16x8 pf[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) pf[u] = as_bf16x8(make_uint4(w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]));
     bf16x8 ring[RING];
 #pragma unroll
-    for (int i0 = 0; i0 < RING - 1; ++i0) ring[i0] = v_operand(vt, i0, n, hh);
+    for (int i0 = 0; i0 < RING - 1; ++i0) ring[i0] = v_operand(vt, i0, vlane);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        if (i + RING - 1 < 16) ring[(i + RING - 1) % RING] = v_operand(vt, i + RING - 1, n, hh);
+        if (i + RING - 1 < 16) ring[(i + RING - 1) % RING] = v_operand(vt, i + RING - 1, vlane);
         __builtin_amdgcn_sched_barrier(0);
         o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % RING], pf[i >> 2], o[i & 3], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// A tile with a successor: scores sc (current), sn (next, written), K' part of
-// the next tile kn, V^T part of the current tile vt, copies cp.
+// A tile with a successor: scores sc (current), sn (next, written), K' tile of
+// the next tile kn, V tile of the current tile vt, copies cp.
 __device__ __forceinline__ void tile_step(const uint4* kn, const uint4* vt, f32x16 (&sc)[2], f32x16 (&sn)[2],
                                           const bf16x8 (&qf)[8], f32x16 (&o)[4], f32x16& negm, float& lsum, int n,
-                                          int hh, const TileCopies& cp) {
+                                          int hh, int vlane, const TileCopies& cp) {
     uint32_t w[16];
     float sum = 0.0f;
     stage_a<true, true>(kn, qf, negm, sn, sc, w, sum, n, hh, &cp);
     settle_weights<true>(sc, sn, w, sum, o, negm, lsum);
-    stage_b(vt, w, o, n, hh);
+    stage_b(vt, w, o, vlane);
 }
 
 // The range's last tile (index j), masked.
 __device__ __forceinline__ void tile_step_last(const uint4* vt, f32x16 (&sc)[2], int j, int S,
                                                const bf16x8 (&qf)[8], f32x16 (&o)[4], f32x16& negm, float& lsum,
-                                               int n, int hh) {
+                                               int n, int hh, int vlane) {
     mask_tail(sc, j, S, hh);
     uint32_t w[16];
     float sum = 0.0f;
     f32x16 none[2];
     stage_a<false, true>(nullptr, qf, negm, none, sc, w, sum, n, hh);
     settle_weights<false>(sc, none, w, sum, o, negm, lsum);
-    stage_b(vt, w, o, n, hh);
+    stage_b(vt, w, o, vlane);
 }
 
 // One workgroup = BM queries of one (batch, head) against the key tiles
@@ -251,22 +283,22 @@ __device__ __forceinline__ void tile_step_last(const uint4* vt, f32x16 (&sc)[2],
 // the `split` items).  Whole range: normalised bf16 output.  Key range:
 // unnormalised O, m and l of the range to `part`, merged afterwards.
 __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
-    const uint4* __restrict__ q, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
-    const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, int S,
-    int ntiles, int nqt, int full, int nsplit, float qmul, int has_rope) {
+    const uint4* __restrict__ q, const uint4* __restrict__ v, const float4* __restrict__ cos_t,
+    const float4* __restrict__ sin_t, const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part, int S, int ntiles, int nqt, int full, int nsplit, float qmul, int has_rope) {
     static_assert(QB == 1, "one 32-query block per wave");
-    // Tile t's K' part lives in kbuf[t % 4] and its V^T part in vbuf[t % 4]
-    // (140 KiB of LDS).  Distinct objects and a loop unrolled by four keep
+    // Tile t's K' part lives in kbuf[t % 4] and its V rows in vbuf[t % 4]
+    // (136 KiB of LDS).  Distinct objects and a loop unrolled by four keep
     // every buffer static, so the compiler does not make LDS reads wait for
     // the copies.
     __shared__ uint4 kb0[K_PART_CHUNKS];
     __shared__ uint4 kb1[K_PART_CHUNKS];
     __shared__ uint4 kb2[K_PART_CHUNKS];
     __shared__ uint4 kb3[K_PART_CHUNKS];
-    __shared__ uint4 vb0[V_PART_CHUNKS];
-    __shared__ uint4 vb1[V_PART_CHUNKS];
-    __shared__ uint4 vb2[V_PART_CHUNKS];
-    __shared__ uint4 vb3[V_PART_CHUNKS];
+    __shared__ uint4 vb0[V_LDS_CHUNKS];
+    __shared__ uint4 vb1[V_LDS_CHUNKS];
+    __shared__ uint4 vb2[V_LDS_CHUNKS];
+    __shared__ uint4 vb3[V_LDS_CHUNKS];
     uint4* const kbuf[4] = {kb0, kb1, kb2, kb3};
     uint4* const vbuf[4] = {vb0, vb1, vb2, vb3};
 
@@ -282,30 +314,45 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const int n = lane & 31;
     const int hh = lane >> 5;
 
-    // The (batch, head) slice of prepared tiles as a buffer resource; tile
-    // tb + i starts at byte tile0 + i * TILE_BYTES (< 2^31 for S <= MAX_SEQ).
-    const __amdgpu_buffer_rsrc_t rsrc =
-        raw_rsrc(ws + bh * (int64_t)ntiles * TILE_CHUNKS, (uint32_t)ntiles * TILE_BYTES);
+    // The (batch, head) slice of prepared K' tiles and the head's V rows as
+    // buffer resources; K' tile tb + i starts at byte ktile0 + i * K_PART_BYTES
+    // and V tile tb + i at vtile0 + i * KV_TILE * V_ROW_BYTES (both < 2^31 for
+    // S <= MAX_SEQ).  V rows at or past S read as zeros.
+    const __amdgpu_buffer_rsrc_t krsrc =
+        raw_rsrc(ws + bh * (int64_t)ntiles * K_PART_CHUNKS, (uint32_t)ntiles * K_PART_BYTES);
+    const __amdgpu_buffer_rsrc_t vrsrc = raw_rsrc(v + bh * (int64_t)S * (V_ROW_BYTES / 16), (uint32_t)S * V_ROW_BYTES);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int tile0 = tb * TILE_BYTES;
+    const int ktile0 = tb * K_PART_BYTES;
+    const int vtile0 = tb * KV_TILE * V_ROW_BYTES;
+    const int vgather = v_gather_offset(lane);
+    const int vlane = v_lane_offset(lane);
     auto copies = [&](int ki, uint4* kd, bool kon, int vi, uint4* vd, bool von = true) {
         TileCopies c;
-        c.rsrc = rsrc;
-        c.ksoff = tile0 + ki * TILE_BYTES;
-        c.vsoff = tile0 + vi * TILE_BYTES + K_PART_BYTES;
+        c.krsrc = krsrc;
+        c.vrsrc = vrsrc;
+        c.ksoff = ktile0 + ki * K_PART_BYTES;
+        c.vsoff = vtile0 + vi * KV_TILE * V_ROW_BYTES;
         c.kdst = kd;
         c.vdst = vd;
         c.kon = kon;
         c.von = von;
         c.wave = wv;
         c.lane = lane;
+        c.vgather = vgather;
         return c;
     };
-    copy_to_lds<NW, K_PART_CHUNKS>(rsrc, tile0, kb0, wv, lane);
-    copy_to_lds<NW, V_PART_CHUNKS>(rsrc, tile0 + K_PART_BYTES, vb0, wv, lane);
-    if (nt > 1) copy_to_lds<NW, K_PART_CHUNKS>(rsrc, tile0 + TILE_BYTES, kb1, wv, lane);
-    if (nt > 1) copy_to_lds<NW, V_PART_CHUNKS>(rsrc, tile0 + TILE_BYTES + K_PART_BYTES, vb1, wv, lane);
-    if (nt > 2) copy_to_lds<NW, K_PART_CHUNKS>(rsrc, tile0 + 2 * TILE_BYTES, kb2, wv, lane);
+    auto copy_v = [&](int vi, uint4* vd) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TileCopies::VJ; ++i) {
+            const int p = i * NW + wv;
+            if (p < V_PIECES) v_piece(vrsrc, vtile0 + vi * KV_TILE * V_ROW_BYTES, p, vd, vgather);
+        }
+    };
+    copy_to_lds<NW, K_PART_CHUNKS>(krsrc, ktile0, kb0, wv, lane);
+    copy_v(0, vb0);
+    if (nt > 1) copy_to_lds<NW, K_PART_CHUNKS>(krsrc, ktile0 + K_PART_BYTES, kb1, wv, lane);
+    if (nt > 1) copy_v(1, vb1);
+    if (nt > 2) copy_to_lds<NW, K_PART_CHUNKS>(krsrc, ktile0 + 2 * K_PART_BYTES, kb2, wv, lane);
 
     // ---- Q prologue: RoPE, fold scale*log2(e), round to bf16, keep resident.
     bf16x8 qf[8];
@@ -377,7 +424,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
-        tile_step(kbuf[(R + 1) % 4], vbuf[R], s[R % 2], s[(R + 1) % 2], qf, o, negm, lsum, n, hh,
+        tile_step(kbuf[(R + 1) % 4], vbuf[R], s[R % 2], s[(R + 1) % 2], qf, o, negm, lsum, n, hh, vlane,
                   copies(k + 3, kbuf[(R + 3) % 4], k + 3 <= L, k + 2, vbuf[(R + 2) % 4], k + 2 <= L));
     };
     for (int k = 0;;) {
@@ -394,13 +441,13 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
-    // No copy is in flight any more, so the last V^T part may be picked at
-    // run time; only the score registers need a static choice.
+    // No copy is in flight any more, so the last V tile may be picked at run
+    // time; only the score registers need a static choice.
     const uint4* vlast = (L & 2) ? ((L & 1) ? vb3 : vb2) : ((L & 1) ? vb1 : vb0);
     if (L & 1)
-        tile_step_last(vlast, s[1], te - 1, S, qf, o, negm, lsum, n, hh);
+        tile_step_last(vlast, s[1], te - 1, S, qf, o, negm, lsum, n, hh, vlane);
     else
-        tile_step_last(vlast, s[0], te - 1, S, qf, o, negm, lsum, n, hh);
+        tile_step_last(vlast, s[0], te - 1, S, qf, o, negm, lsum, n, hh, vlane);
 #pragma unroll
     for (int db = 0; db < 4; ++db) settle(o[db]);
 
@@ -479,17 +526,18 @@ hipError_t launch_merge(const float* part, void* out, float* lse, int S, int nqt
 
 size_t core_partial_bytes(int BH, int S) { return core_partial_bytes_for(core_plan(BH, S)); }
 
-hipError_t launch_attn_core(const void* q, const float* cos_t, const float* sin_t, const void* ws, void* part,
-                            void* out, float* lse, int BH, int S, float qmul, hipStream_t stream) {
+hipError_t launch_attn_core(const void* q, const void* v, const float* cos_t, const float* sin_t, const void* ws,
+                            void* part, void* out, float* lse, int BH, int S, float qmul, hipStream_t stream) {
     const CorePlan p = core_plan(BH, S);
     const uint4* wsv = static_cast<const uint4*>(ws);
     const uint4* qv = static_cast<const uint4*>(q);
+    const uint4* vv = static_cast<const uint4*>(v);
     const float4* cv = reinterpret_cast<const float4*>(cos_t);
     const float4* sv = reinterpret_cast<const float4*>(sin_t);
     const int rope = cos_t != nullptr;
     float* pt = static_cast<float*>(part);
-    attn_core_kernel<<<core_grid(p), NW * 64, 0, stream>>>(qv, cv, sv, wsv, static_cast<uint2*>(out), lse, pt, S,
-                                                          p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
+    attn_core_kernel<<<core_grid(p), NW * 64, 0, stream>>>(qv, vv, cv, sv, wsv, static_cast<uint2*>(out), lse, pt,
+                                                          S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && p.split > 0) e = launch_merge(pt, out, lse, S, p.nqt, p.full, p.nsplit, p.split, stream);
     return e;

@@ -1,18 +1,19 @@
-// prepare_kv.hip - RoPE on K and re-layout of K and V into streamed tiles.
+// prepare_kv.hip - RoPE on K and its re-layout into streamed K' tiles (bf16
+// path); RoPE on K and the K'/V^T tiles of the fp8 path.
 //
-// One workgroup of 256 threads per (batch*head, 64-key tile).  It reads the
-// tile's 64 rows of K and V once from HBM ([B, H, S, 128] bf16), rotates K per
-// interleaved pair in fp32 (RoPE as read from the DiT pages: the xDiT paper's
-// abstract and the AMD RDNA 4 xDiT blog describe attention over RoPE'd text +
-// latent tokens; pair j = dims (2j, 2j+1) times exp(i phi[s][j])), rounds to
-// bf16 (RNE), and writes the tile in the LDS image described in tile_layout.h.
-// V is transposed through LDS so the attention kernel can read it as the A
-// operand of O^T = V^T P^T.  Keys at or past S are written as zeros so the
-// PV product never multiplies a masked probability by garbage.
+// bf16: one workgroup of 256 threads per (batch*head, 64-key tile).  It reads
+// the tile's 64 rows of K once from HBM ([B, H, S, 128] bf16), rotates them
+// per interleaved pair in fp32 (RoPE as read from the DiT pages: the xDiT
+// paper's abstract and the AMD RDNA 4 xDiT blog describe attention over
+// RoPE'd text + latent tokens; pair j = dims (2j, 2j+1) times
+// exp(i phi[s][j])), rounds to bf16 (RNE), and writes the K' tile image of
+// tile_layout.h with coalesced stores (consecutive threads write consecutive
+// 16-byte chunks).  Keys at or past S are written as zeros.  V needs no
+// preparation: the attention kernel copies its rows as they are.
 //
-// Roofline: HBM bound.  Algorithmic bytes per tile and head: read 2 x 16 KiB
-// (K, V) + 2 x 16 KiB (cos, sin rows when RoPE is on; shared by all heads),
-// write TILE_BYTES = 35 KiB (the two parts with their row padding).
+// Roofline: HBM bound.  Algorithmic bytes per tile and head: read 16 KiB of K
+// + 16 KiB of cos/sin rows (shared by all heads, L2/MALL resident), write
+// K_PART_BYTES = 17 KiB (the rows with their padding chunk).
 
 #include <hip/hip_runtime.h>
 
@@ -22,42 +23,22 @@
 
 namespace dit {
 
-// Every global store of a workgroup is coalesced: consecutive threads write
-// consecutive 16-byte chunks of the tile image (K' part, then V^T part), so
-// each wave store covers one contiguous 1 KiB run.  For the V^T part that
-// means consecutive lanes take consecutive (d, c) chunks; to keep their LDS
-// gathers apart, V is kept in LDS with its 16-byte chunks XOR-swizzled by
-// the key's 8-key group (chunk ch of key r sits at ch ^ (r >> 3)).
-__device__ __forceinline__ int vswz(int key, int ch) { return key * 16 + (ch ^ ((key >> 3) & 15)); }
-
-__global__ __launch_bounds__(256) void prepare_kv_kernel(
-    const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
+__global__ __launch_bounds__(256) void prepare_k_kernel(
+    const uint4* __restrict__ k, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
     uint4* __restrict__ ws, int S, int ntiles, int has_rope) {
-    __shared__ uint4 vtile[KV_TILE * 16];  // 64 keys x 128 dims, chunks swizzled (vswz)
-
     const int tile = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int key0 = tile * KV_TILE;
-    uint4* dst = ws + (bh * ntiles + tile) * (int64_t)TILE_CHUNKS;
+    uint4* dst = ws + (bh * ntiles + tile) * (int64_t)K_PART_CHUNKS;
     const uint4* ksrc = k + bh * (int64_t)S * 16;
-    const uint4* vsrc = v + bh * (int64_t)S * 16;
 
-    // Every load of the thread is issued before any is used (V rows, K chunks
-    // and their cos/sin rows), so the HBM latency is paid about once per
-    // workgroup rather than once per chunk.
-    constexpr int KI = (K_PART_CHUNKS + 255) / 256;  // K chunks per thread (the last partly)
-    uint4 vw[4], kw[KI];
+    // Output chunk x = (row rho, chunk c); chunk 16 of a row is padding.  Every
+    // load of the thread is issued before any is used, so the HBM latency is
+    // paid about once per workgroup rather than once per chunk.
+    constexpr int KI = (K_PART_CHUNKS + 255) / 256;  // chunks per thread (the last partly)
+    uint4 kw[KI];
     float4 cw[KI], sw[KI];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int x = tid + i * 256;
-        const int key = key0 + (x >> 4);
-        vw[i] = make_uint4(0, 0, 0, 0);
-        if (key < S) vw[i] = vsrc[(int64_t)key * 16 + (x & 15)];
-    }
-    // K part: output chunk x = (row rho, chunk c); chunk 16 of a row is padding.
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
         const int x = tid + i * 256;
@@ -74,11 +55,6 @@ __global__ __launch_bounds__(256) void prepare_kv_kernel(
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int x = tid + i * 256;
-        vtile[vswz(x >> 4, x & 15)] = vw[i];
-    }
-#pragma unroll
     for (int i = 0; i < KI; ++i) {
         const int x = tid + i * 256;
         if (x >= K_PART_CHUNKS) break;
@@ -93,35 +69,6 @@ __global__ __launch_bounds__(256) void prepare_kv_kernel(
             w = pack8(f);
         }
         dst[x] = w;
-    }
-
-    __syncthreads();
-
-    // V^T part: chunk q = (d, c) = keys 8c..8c+7 of head dim d (c = 8 is
-    // padding), q = d * 9 + c running over consecutive threads.
-    const unsigned short* vt16 = reinterpret_cast<const unsigned short*>(vtile);
-    uint4* vdst = dst + K_PART_CHUNKS;
-    constexpr int VI = (V_PART_CHUNKS + 255) / 256;
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-        const int q = tid + i * 256;
-        if (q >= V_PART_CHUNKS) break;
-        const int d = q / V_ROW_CHUNKS;
-        const int c = q - d * V_ROW_CHUNKS;
-        uint4 out = make_uint4(0, 0, 0, 0);
-        if (c < 8) {
-            // keys 8c + j share the swizzle c, so dim d sits in chunk (d >> 3) ^ c of each row
-            const int col = (((d >> 3) ^ c) << 3) | (d & 7);
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = vt16[(c * 8 + 2 * e) * 128 + col];
-                const uint32_t hi = vt16[(c * 8 + 2 * e + 1) * 128 + col];
-                w[e] = lo | (hi << 16);
-            }
-            out = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        vdst[q] = out;
     }
 }
 
@@ -252,14 +199,13 @@ hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_
     return hipGetLastError();
 }
 
-hipError_t launch_prepare_kv(const void* k, const void* v, const float* cos_t, const float* sin_t,
-                             void* ws, int BH, int S, hipStream_t stream) {
+hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_t, void* ws, int BH, int S,
+                            hipStream_t stream) {
     const int ntiles = (int)num_kv_tiles(S);
     dim3 grid(ntiles, BH);
-    prepare_kv_kernel<<<grid, 256, 0, stream>>>(
-        static_cast<const uint4*>(k), static_cast<const uint4*>(v),
-        reinterpret_cast<const float4*>(cos_t), reinterpret_cast<const float4*>(sin_t),
-        static_cast<uint4*>(ws), S, ntiles, cos_t != nullptr);
+    prepare_k_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(k), reinterpret_cast<const float4*>(cos_t),
+                                               reinterpret_cast<const float4*>(sin_t), static_cast<uint4*>(ws), S,
+                                               ntiles, cos_t != nullptr);
     return hipGetLastError();
 }
 

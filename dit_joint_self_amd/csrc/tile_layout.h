@@ -1,16 +1,20 @@
-// tile_layout.h - the workspace tile format shared by the K/V preparation
-// kernel (writer) and the attention kernels (readers), gfx950 only.
+// tile_layout.h - the K' tile format shared by the K preparation kernel
+// (writer) and the bf16 attention kernel (reader), and the LDS layout of the
+// V tiles that kernel copies straight from V, gfx950 only.
 //
-// The attention kernels stream K and V in tiles of KV_TILE = 64 keys.  Each
-// tile is stored in the workspace exactly as it will sit in LDS, so the
-// kernels copy it with linear 16-byte direct-to-LDS loads:
+// The attention kernel streams K and V in tiles of KV_TILE = 64 keys.
 //
-//   K' part (K_PART_BYTES = 17408): 64 rows of 272 bytes.  Row rho holds the
-//        rotated key kperm(rho) of the tile: 16-byte chunk c (c < 16) holds
-//        dims 8c..8c+7, chunk 16 is zero padding.
-//   V^T part (V_PART_BYTES = 18432): 128 rows of 144 bytes, one per head dim
-//        d: chunk c (c < 8) holds keys 8c..8c+7 of the tile, chunk 8 is zero
-//        padding.
+//   K' tile (K_PART_BYTES = 17408, prepared): 64 rows of 272 bytes, stored in
+//        the workspace exactly as it sits in LDS, so the kernel copies it with
+//        linear 16-byte direct-to-LDS loads.  Row rho holds the rotated key
+//        kperm(rho) of the tile: 16-byte chunk c (c < 16) holds dims
+//        8c..8c+7, chunk 16 is zero padding.  Keys at or past S are zeros.
+//   V tile (V_LDS_BYTES = 17408, not prepared): the 64 key rows of V ([B, H,
+//        S, 128] bf16, 256 bytes per key) in 16 pieces of 4 rows.  Piece p
+//        holds keys p, p + 16, p + 32, p + 48 of the tile (row r = key >> 4)
+//        and sits V_PIECE_BYTES = 1088 bytes (1024 + 64 of padding) after
+//        piece p - 1.  One direct-to-LDS load fills one piece, each lane
+//        gathering 16 bytes of a key row (rows past S read as zeros).
 //
 // Why: the QK^T product is computed transposed (S^T = K' Q'^T) on
 // v_mfma_f32_32x32x16_bf16 so each lane owns one query column.  In that
@@ -18,10 +22,15 @@
 // every 16-row group; storing key kperm(rho) in row rho makes those rows the
 // 8 consecutive keys 8hh..8hh+7, which is exactly the B-operand layout the PV
 // product needs, so P goes from accumulator to MFMA operand without any lane
-// exchange.  The padded row strides (17 and 9 chunks, both odd) put the rows
-// read by consecutive lanes in distinct LDS banks, and keep every operand
-// address of a lane equal to one base plus a compile-time offset.  Keys at or
-// past S in the last tile are stored as zeros.
+// exchange.  The PV A operand (V^T: one head dim per row, 8 consecutive keys
+// per lane) is read from the key-major V tile with ds_read_b64_tr_b16, whose
+// 16-lane groups each return a transposed 4 (keys) x 16 (dims) block; the
+// four keys of such a block (16u + 8hh + 4h + j, j = 0..3) sit in four
+// consecutive pieces, and the 64-byte piece padding moves consecutive pieces
+// 16 banks apart, so a group reads 16 distinct bank pairs.  The K' row stride
+// (17 chunks, odd) puts the rows read by consecutive lanes in distinct LDS
+// banks and keeps every K' operand address one base plus a compile-time
+// offset.
 #pragma once
 
 #include <stdint.h>
@@ -31,25 +40,28 @@ namespace dit {
 constexpr int HEAD_DIM = 128;
 constexpr int KV_TILE = 64;                              // keys per streamed tile
 constexpr int K_ROW_CHUNKS = 17;                         // 16 data chunks + 1 pad
-constexpr int V_ROW_CHUNKS = 9;                          // 8 data chunks + 1 pad
 constexpr int K_PART_CHUNKS = KV_TILE * K_ROW_CHUNKS;    // 1088
-constexpr int V_PART_CHUNKS = HEAD_DIM * V_ROW_CHUNKS;   // 1152
-constexpr int K_PART_BYTES = K_PART_CHUNKS * 16;         // 17408
-constexpr int V_PART_BYTES = V_PART_CHUNKS * 16;         // 18432
-constexpr int TILE_CHUNKS = K_PART_CHUNKS + V_PART_CHUNKS;  // 2240 = 35 x 64
-constexpr int TILE_BYTES = TILE_CHUNKS * 16;             // 35840
+constexpr int K_PART_BYTES = K_PART_CHUNKS * 16;         // 17408: one prepared K' tile
+constexpr int V_PIECES = KV_TILE / 4;                    // 16 pieces of 4 key rows
+constexpr int V_PIECE_CHUNKS = 68;                       // 64 data chunks + 4 pad
+constexpr int V_PIECE_BYTES = V_PIECE_CHUNKS * 16;       // 1088
+constexpr int V_LDS_CHUNKS = V_PIECES * V_PIECE_CHUNKS;  // 1088
+constexpr int V_LDS_BYTES = V_LDS_CHUNKS * 16;           // 17408
+constexpr int V_ROW_BYTES = HEAD_DIM * 2;                // 256: one key row of V
 
-static_assert(K_PART_CHUNKS % 64 == 0 && V_PART_CHUNKS % 64 == 0, "parts are whole wave copies");
+static_assert(K_PART_CHUNKS % 64 == 0, "the K' tile is whole wave copies");
 
 __host__ __device__ constexpr inline int kperm(int rho) {
     return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
 }
 
-// Chunk index (16 B units, inside the K part) holding dims 8c..8c+7 of row rho.
+// Chunk index (16 B units, inside a K' tile) holding dims 8c..8c+7 of row rho.
 __host__ __device__ constexpr inline int k_chunk(int rho, int c) { return rho * K_ROW_CHUNKS + c; }
 
-// Chunk index (inside the V part) holding keys 8c..8c+7 of head dim d.
-__host__ __device__ constexpr inline int v_chunk(int d, int c) { return d * V_ROW_CHUNKS + c; }
+// Byte offset, inside an LDS V tile, of dim d of tile key `key`.
+__host__ __device__ constexpr inline int v_lds_byte(int key, int d) {
+    return (key & 15) * V_PIECE_BYTES + (key >> 4) * V_ROW_BYTES + 2 * d;
+}
 
 __host__ __device__ constexpr inline int64_t num_kv_tiles(int S) {
     return (S + KV_TILE - 1) / KV_TILE;

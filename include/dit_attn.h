@@ -115,34 +115,35 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v,
 
 /*
  * The two stages of dit_attn_forward, for callers that own the workspace
- * (for example, to reuse one workspace across layers, or to time the stages).
- * dit_attn_forward(...) == prepare_kv then core, on one workspace.
+ * (for example, to reuse one workspace across layers, to capture the calls in
+ * a HIP graph, or to time the stages).
+ * dit_attn_forward(...) == prepare_k then core, on one workspace.
  *
  * dit_attn_workspace_bytes  bytes needed for B, H, S, D (0 on invalid sizes).
  *
- * dit_attn_prepare_kv  rotates K (bf16 RNE) and re-lays K and V out into the
- *   workspace in the tile order the attention kernel streams.  The workspace
- *   layout is private to this library and may change between versions.
- *   workspace: device, 256-byte aligned, >= dit_attn_workspace_bytes(B,H,S,D).
+ * dit_attn_prepare_k  rotates K (bf16 RNE) and lays it out in the workspace
+ *   in the tile order the attention kernel streams.  V needs no preparation.
+ *   The workspace layout is private to this library and may change between
+ *   versions.  workspace: device, 256-byte aligned, >= dit_attn_workspace_bytes(B,H,S,D).
  *
  * dit_attn_core  attention of q (rotated and scaled in its prologue) against
- *   the prepared workspace; rope tables must be the ones given to prepare_kv.
+ *   the prepared K and the caller's v (bf16 [B, H, S, D], read as it is); the
+ *   rope tables must be the ones given to prepare_k.
  *   The call also WRITES the workspace: past the prepared tiles it keeps the
  *   partial results of the query tiles whose keys it splits into ranges
  *   (shapes whose work does not fill whole rounds of the GPU's compute
- *   units; 24 heads of 16896 tokens is one).  Core calls that may run
- *   at the same time (on different streams) must therefore not share a
- *   workspace, even when they read the same prepared keys.  q, out and the
- *   rope tables must not overlap the workspace.
+ *   units; 24 heads of 16896 tokens is one).  Core calls that may run at the
+ *   same time (on different streams) must therefore not share a workspace,
+ *   even when they read the same prepared keys.  q, v, out and the rope
+ *   tables must not overlap the workspace, and out must not overlap q or v.
  */
 size_t dit_attn_workspace_bytes(int B, int H, int S, int D);
 
-dit_status_t dit_attn_prepare_kv(const void* k, const void* v,
-                                 const float* rope_cos, const float* rope_sin,
-                                 void* workspace, size_t workspace_bytes,
-                                 int B, int H, int S, int D, void* stream);
+dit_status_t dit_attn_prepare_k(const void* k, const float* rope_cos, const float* rope_sin,
+                                void* workspace, size_t workspace_bytes,
+                                int B, int H, int S, int D, void* stream);
 
-dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* rope_sin,
+dit_status_t dit_attn_core(const void* q, const void* v, const float* rope_cos, const float* rope_sin,
                            void* workspace, size_t workspace_bytes, void* out,
                            int B, int H, int S, int D, float scale, void* stream);
 
@@ -157,13 +158,13 @@ dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* ro
  *   aligned, written with the natural-log log-sum-exp of each query row's
  *   scaled scores, L = log(sum_j exp(scale * q'.k'_j)) over the keys of the
  *   workspace (computed from the same rounded Q'' and K' and the same bf16
- *   weights as out).  For a ring step, prepare the key/value block with the
- *   block's own RoPE tables (dit_attn_prepare_kv) and pass the query shard's
- *   tables here: RoPE of a row depends only on its own position.  The shard
- *   and the block have the same length S.  lse must not overlap q, out, the
- *   rope tables or the workspace.  Like dit_attn_core it writes key-range
- *   partials into the workspace, so ring steps that run concurrently need
- *   one workspace each.
+ *   weights as out).  For a ring step, prepare the block's keys with the
+ *   block's own RoPE tables (dit_attn_prepare_k), pass the block's v, and pass
+ *   the query shard's tables here: RoPE of a row depends only on its own
+ *   position.  The shard and the block have the same length S.  lse must not
+ *   overlap q, v, out, the rope tables or the workspace.  Like dit_attn_core
+ *   it writes key-range partials into the workspace, so ring steps that run
+ *   concurrently need one workspace each.
  *
  * dit_attn_merge_lse  folds two partial results over disjoint key blocks:
  *   out = w_a o_a + w_b o_b with w_x = exp(lse_x - lse_out) and
@@ -174,7 +175,7 @@ dit_status_t dit_attn_core(const void* q, const float* rope_cos, const float* ro
  *   any other overlap is DIT_ERR_INVALID_ARG.  A row whose two LSEs are both
  *   -inf (no keys on either side) yields NaN.
  */
-dit_status_t dit_attn_core_lse(const void* q, const float* rope_cos, const float* rope_sin,
+dit_status_t dit_attn_core_lse(const void* q, const void* v, const float* rope_cos, const float* rope_sin,
                                void* workspace, size_t workspace_bytes, void* out, float* lse,
                                int B, int H, int S, int D, float scale, void* stream);
 

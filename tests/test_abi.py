@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     lib = dj.lib()
     for name in dj.EXPORTED_SYMBOLS:
         assert getattr(lib, name) is not None
-    assert dj.dit_abi_version() == 4
+    assert dj.dit_abi_version() == 5
 
 
 def _expected_workspace(B, H, S):
@@ -51,7 +51,7 @@ def _expected_workspace(B, H, S):
     f on ties, when f >= 2; each range keeps 256 x 128 + 2 x 256 fp32 values."""
     from fractions import Fraction
     ntiles = -(-S // 64)
-    tiles = (B * H * ntiles * 35840 + 255) // 256 * 256
+    tiles = (B * H * ntiles * 17408 + 255) // 256 * 256
     items = B * H * -(-S // 256)
     r = items % 256
     f = 1
@@ -63,10 +63,10 @@ def _expected_workspace(B, H, S):
 
 
 def test_workspace_bytes():
-    assert dj.dit_attn_workspace_bytes(1, 24, 16896, 128) == 24 * 264 * 35840 + 48 * 5 * 33280 * 4
-    assert dj.dit_attn_workspace_bytes(1, 1, 1, 128) == 35840
+    assert dj.dit_attn_workspace_bytes(1, 24, 16896, 128) == 24 * 264 * 17408 + 48 * 5 * 33280 * 4
+    assert dj.dit_attn_workspace_bytes(1, 1, 1, 128) == 17408
     # The video share: 2980 items leave 164 after 11 rounds, split over 3 key ranges.
-    assert dj.dit_attn_workspace_bytes(1, 10, 76112, 128) == 10 * 1190 * 35840 + 164 * 3 * 33280 * 4
+    assert dj.dit_attn_workspace_bytes(1, 10, 76112, 128) == 10 * 1190 * 17408 + 164 * 3 * 33280 * 4
     for B, H, S in [(1, 24, 16896), (2, 3, 65), (1, 1, 1), (1, 24, 3584), (1, 10, 76112), (1, 2, 320), (3, 7, 999),
                     (1, 1, 130000), (4, 13, 4000), (1, 200, 256)]:
         assert dj.dit_attn_workspace_bytes(B, H, S, 128) == _expected_workspace(B, H, S), (B, H, S)
@@ -121,24 +121,30 @@ def test_split_entry_points_reject_bad_arguments():
     L = dj.lib()
     need = dj.dit_attn_workspace_bytes(1, 2, 8, 128)
     ws = 0x10000000
-    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, None, None, ws, need - 1, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
-    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, None, None, ws + 16, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
-    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, None, None, FAKE, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
-    assert L.dit_attn_prepare_kv(FAKE, None, None, None, ws, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
-    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, None, None, ws, need, 1, 2, 8, 96, None) == dj.DIT_ERR_UNSUPPORTED
-    assert L.dit_attn_core(FAKE, None, None, ws, need, ws, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
-    assert L.dit_attn_core(FAKE, FAKE * 2, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
-    assert L.dit_attn_core(FAKE, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, float("nan"), None) == dj.DIT_ERR_INVALID_ARG
-    assert L.dit_attn_core(FAKE, None, None, ws, need - 1, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
-    # core writes key-range partials into its workspace: q and the tables must lie outside it
-    assert L.dit_attn_core(ws + 256, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
-    assert "q overlaps" in dj.dit_last_error()
-    assert L.dit_attn_core(FAKE, ws + 512, FAKE * 5, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
-    assert L.dit_attn_core(FAKE, FAKE * 5, FAKE * 3 + 64, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
-    assert L.dit_attn_prepare_kv(FAKE, FAKE * 2, ws + 512, FAKE * 5, ws, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    V = FAKE * 7
+    assert L.dit_attn_prepare_k(FAKE, None, None, ws, need - 1, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_k(FAKE, None, None, ws + 16, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_k(FAKE, None, None, FAKE, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_k(None, None, None, ws, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_k(FAKE, None, None, ws, need, 1, 2, 8, 96, None) == dj.DIT_ERR_UNSUPPORTED
+    assert L.dit_attn_core(FAKE, V, None, None, ws, need, ws, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, V, FAKE * 2, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, V, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, float("nan"), None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, V, None, None, ws, need - 1, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, None, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, V + 8, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, FAKE * 3 + 64, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    # core writes key-range partials into its workspace: q, v and the tables must lie outside it
+    assert L.dit_attn_core(ws + 256, V, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert "overlaps the workspace" in dj.dit_last_error()
+    assert L.dit_attn_core(FAKE, ws + 256, None, None, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, V, ws + 512, FAKE * 5, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_core(FAKE, V, FAKE * 5, FAKE * 3 + 64, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_INVALID_ARG
+    assert L.dit_attn_prepare_k(FAKE, ws + 512, FAKE * 5, ws, need, 1, 2, 8, 128, None) == dj.DIT_ERR_INVALID_ARG
     assert _fwd(cos=FAKE * 4 + 256, sin=FAKE * 6) == dj.DIT_ERR_INVALID_ARG      # a table inside out
     if _no_device():                                                             # tables apart: valid
-        assert L.dit_attn_core(FAKE, FAKE * 5, FAKE * 6, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_NO_DEVICE
+        assert L.dit_attn_core(FAKE, V, FAKE * 5, FAKE * 6, ws, need, FAKE * 3, 1, 2, 8, 128, 0.1, None) == dj.DIT_ERR_NO_DEVICE
+        assert L.dit_attn_prepare_k(FAKE, FAKE * 5, FAKE * 6, ws, need, 1, 2, 8, 128, None) == dj.DIT_ERR_NO_DEVICE
 
 
 def test_rope_tables_reject_bad_arguments():
@@ -203,7 +209,7 @@ def test_lse_entry_points_reject_bad_arguments():
     need = dj.dit_attn_workspace_bytes(1, 2, 8, 128)
     ws = 0x10000000
     lse = 0x20000000
-    core = lambda **kw: L.dit_attn_core_lse(kw.get("q", FAKE), None, None, ws, need, kw.get("out", FAKE * 3),
+    core = lambda **kw: L.dit_attn_core_lse(kw.get("q", FAKE), FAKE * 7, None, None, ws, need, kw.get("out", FAKE * 3),
                                             kw.get("lse", lse), 1, 2, 8, 128, 0.1, None)
     assert core(lse=None) == dj.DIT_ERR_INVALID_ARG
     assert core(lse=lse + 2) == dj.DIT_ERR_INVALID_ARG                 # misaligned

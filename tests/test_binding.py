@@ -69,17 +69,19 @@ def test_split_entry_points_reject_bad_arguments():
     q, k, v = _qkv()
     ws = torch.zeros(dj.dit_attn_workspace_bytes(1, 2, 8, 128), dtype=torch.uint8)
     with pytest.raises(ValueError, match="shape"):
-        dj.dit_attn_prepare_kv(k, torch.zeros((1, 2, 16, 128), dtype=BF), None, None, ws)
+        dj.dit_attn_prepare_k(k, torch.zeros((7, 64)), torch.zeros((7, 64)), ws)
     with pytest.raises(ValueError, match="exceeds"):
-        dj.dit_attn_prepare_kv(k, v, None, None, ws, workspace_bytes=ws.numel() + 1)
+        dj.dit_attn_prepare_k(k, None, None, ws, workspace_bytes=ws.numel() + 1)
     with pytest.raises(TypeError):
-        dj.dit_attn_prepare_kv(k, v, None, None, 0x1000)
+        dj.dit_attn_prepare_k(k, None, None, 0x1000)
     with pytest.raises(ValueError, match="shape"):
-        dj.dit_attn_core(q, None, None, ws, torch.zeros((1, 2, 8, 64), dtype=BF))
+        dj.dit_attn_core(q, v, None, None, ws, torch.zeros((1, 2, 8, 64), dtype=BF))
     with pytest.raises(ValueError, match="shape"):
-        dj.dit_attn_core_lse(q, None, None, ws, torch.empty_like(q), lse=torch.zeros((1, 2, 7)))
+        dj.dit_attn_core(q, torch.zeros((1, 2, 16, 128), dtype=BF), None, None, ws, torch.empty_like(q))
+    with pytest.raises(ValueError, match="shape"):
+        dj.dit_attn_core_lse(q, v, None, None, ws, torch.empty_like(q), lse=torch.zeros((1, 2, 7)))
     with pytest.raises(ValueError, match="GPU"):
-        dj.dit_attn_core(q, None, None, ws, torch.empty_like(q))
+        dj.dit_attn_core(q, v, None, None, ws, torch.empty_like(q))
 
 
 def test_merge_lse_rejects_bad_arguments():

@@ -65,9 +65,9 @@ def test_bf16_prepare_core_lse_graph_replays():
     lse = torch.empty((w0.B, w0.H, w0.S), dtype=torch.float32, device="cuda")
 
     def call():
-        dj.dit_attn_prepare_kv(k, v, cos, sin, ws)
-        dj.dit_attn_core(q, cos, sin, ws, out)
-        dj.dit_attn_core_lse(q, cos, sin, ws, out2, lse)
+        dj.dit_attn_prepare_k(k, cos, sin, ws)
+        dj.dit_attn_core(q, v, cos, sin, ws, out)
+        dj.dit_attn_core_lse(q, v, cos, sin, ws, out2, lse)
 
     call()                                   # eager once before capture (device checks cached)
     torch.cuda.synchronize()
@@ -79,9 +79,9 @@ def test_bf16_prepare_core_lse_graph_replays():
         want = torch.empty_like(qe)
         want2 = torch.empty_like(qe)
         want_lse = torch.empty_like(lse)
-        dj.dit_attn_prepare_kv(ke, ve, cos, sin, ws_e)
-        dj.dit_attn_core(qe, cos, sin, ws_e, want)
-        dj.dit_attn_core_lse(qe, cos, sin, ws_e, want2, want_lse)
+        dj.dit_attn_prepare_k(ke, cos, sin, ws_e)
+        dj.dit_attn_core(qe, ve, cos, sin, ws_e, want)
+        dj.dit_attn_core_lse(qe, ve, cos, sin, ws_e, want2, want_lse)
         torch.cuda.synchronize()
         q.copy_(qe)
         k.copy_(ke)

@@ -49,8 +49,8 @@ def _run(w, qb, kb, vb, rope=True, scale=None, split=False):
         nbytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         out = torch.empty_like(q)
-        dj.dit_attn_prepare_kv(k, v, cos, sin, ws)
-        dj.dit_attn_core(q, cos, sin, ws, out, scale=scale)
+        dj.dit_attn_prepare_k(k, cos, sin, ws)
+        dj.dit_attn_core(q, v, cos, sin, ws, out, scale=scale)
     else:
         out = dj.dit_attn_forward(q, k, v, cos, sin, S_txt=w.S_txt, scale=scale)
     torch.cuda.synchronize()
@@ -243,11 +243,11 @@ def test_rotated_keys_round_like_plain_fp32():
     cos_d, sin_d = torch.from_numpy(cos32).cuda(), torch.from_numpy(sin32).cuda()
     nbytes = dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    dj.dit_attn_prepare_kv(k, v, cos_d, sin_d, ws)
+    dj.dit_attn_prepare_k(k, cos_d, sin_d, ws)
     torch.cuda.synchronize()
     ntiles = -(-w.S // 64)
-    img = ws.cpu().numpy()[: w.B * w.H * ntiles * 35840].view(np.uint16).reshape(w.B, w.H, ntiles, 17920)
-    rows = img[..., :8704].reshape(w.B, w.H, ntiles, 64, 136)[..., :128]
+    img = ws.cpu().numpy()[: w.B * w.H * ntiles * 17408].view(np.uint16).reshape(w.B, w.H, ntiles, 8704)
+    rows = img.reshape(w.B, w.H, ntiles, 64, 136)[..., :128]
     rho = np.arange(64)
     key_of_row = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1)
     got = np.zeros((w.B, w.H, ntiles * 64, 128), np.uint16)

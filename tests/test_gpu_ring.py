@@ -65,9 +65,9 @@ def _block_result(w, q, k, v, qrows, krows):
     kk = k[:, :, krows[0]:krows[-1] + 1].contiguous()
     vv = v[:, :, krows[0]:krows[-1] + 1].contiguous()
     qq = q[:, :, qrows[0]:qrows[-1] + 1].contiguous()
-    dj.dit_attn_prepare_kv(kk, vv, ck, sk, ws)
+    dj.dit_attn_prepare_k(kk, ck, sk, ws)
     out = torch.empty_like(qq)
-    return dj.dit_attn_core_lse(qq, cq, sq, ws, out)
+    return dj.dit_attn_core_lse(qq, vv, cq, sq, ws, out)
 
 
 def _lse_close(got, want, tag):
@@ -105,8 +105,8 @@ def test_core_lse_matches_oracle(name, S_txt, grid, B, H):
     out_plain = torch.empty_like(out)
     cos, sin = _tables(w, rows)
     ws = torch.empty(dj.dit_attn_workspace_bytes(w.B, w.H, w.S, w.D), dtype=torch.uint8, device="cuda")
-    dj.dit_attn_prepare_kv(k, v, cos, sin, ws)
-    dj.dit_attn_core(q, cos, sin, ws, out_plain)
+    dj.dit_attn_prepare_k(k, cos, sin, ws)
+    dj.dit_attn_core(q, v, cos, sin, ws, out_plain)
     torch.cuda.synchronize()
     # the LSE variant writes the same O as the plain call
     assert torch.equal(out.view(torch.int16), out_plain.view(torch.int16))
