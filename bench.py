@@ -99,6 +99,8 @@ def parse():
                     choices=list(W.WORKLOADS) + list(W.LINEAR_WORKLOADS) + list(W.RESIDUAL_WORKLOADS),
                     help="an attention workload, or an MXFP4 linear-layer shape (quantise + A4W4 GEMM)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
+    ap.add_argument("--prewarm-s", type=float, default=0.5,
+                    help="seconds of untimed back-to-back steps before the warmup steps (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single-config", action="store_true",
                     help="time only --workload (by default an attention run also times every other attention "
@@ -252,6 +254,7 @@ def ring_bench(args, w, torch, dj):
                                       stream=stream)
             ev.append(torch.cuda.Event(enable_timing=True)); ev[-1].record(stream)
 
+    prewarm(torch, lambda: step([]), args.prewarm_s)
     for _ in range(args.warmup):
         step([])
     torch.cuda.synchronize()
@@ -326,6 +329,7 @@ def gemm_bench(args, lw, torch, dj):
         torch.cuda.synchronize()
         return [e0.elapsed_time(e1) for e0, e1 in ev]
 
+    prewarm(torch, lambda: (step(), gemm(), quant()), args.prewarm_s)
     for _ in range(args.warmup):
         step(); gemm(); quant()
     torch.cuda.synchronize()
@@ -402,6 +406,7 @@ def residual_bench(args, rw, torch, dj):
     diff = torch.empty(1, dtype=torch.float64, device="cuda")
     reuse = torch.empty(1, dtype=torch.int32, device="cuda")
     step = lambda: dj.dit_dbcache_residual_diff(prev, cur, 0.12, ws=ws, diff=diff, reuse=reuse, stream=stream)
+    prewarm(torch, step, args.prewarm_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -488,7 +493,7 @@ def main():
         return
     print(f"[bench] workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype}", file=sys.stderr, flush=True)
     run = AttentionRun(w, torch, dj)
-    timing = run.time_steps(args.steps, args.warmup)
+    timing = run.time_steps(args.steps, args.warmup, args.prewarm_s)
     fwd_ms = run.time_forward(args.steps)
     fp8, flops, peak = run.fp8, w.flops, run.peak
     step_ms, core_avg, prep_avg = timing["step_ms"], timing["core_ms"], timing["prep_ms"]
@@ -536,6 +541,9 @@ def main():
                       "prepare_kv_algorithmic_bytes": prep_bytes},
         "forward_ms": fwd_ms,
         "wall_s": timing["wall_s"],
+        "prewarm": {"seconds": args.prewarm_s, "steps": run.prewarm_steps,
+                    "why": "untimed steps before the warmup steps: the shader clock ramps up over the first tens of "
+                           "ms of sustained load after an idle spell (first calls up to 20% slower)"},
         "clock": clock_record(torch, dj, achieved, flops / (step_ms * 1e-3) / 1e12, 8192 if fp8 else 4096),
     }
     out_host = run.out.cpu()
@@ -552,6 +560,21 @@ def main():
 
         rec["cpu_baseline"] = cpu_baseline(w, f64_head, args.cpu_seconds, gpu_rows)
     print(json.dumps(rec), flush=True)
+
+
+def prewarm(torch, step, seconds):
+    """Run `step` back to back until `seconds` of wall time have passed
+    (synchronising every few steps so the queue stays short); returns the
+    number of steps run.  Brings the GPU from its idle clock to the clock it
+    holds under sustained load before anything is timed."""
+    n = 0
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            step()
+        n += 4
+        torch.cuda.synchronize()
+    return n
 
 
 class AttentionRun:
@@ -595,10 +618,13 @@ class AttentionRun:
             self.f64_head = lambda h: tuple(W.bf16_bits_to_f32(b[:, h:h + 1]).astype(np.float64) for b in (qb, kb, vb))
             self.peak = BF16_PEAK_TFLOPS
 
-    def time_steps(self, K, warmup):
-        """`warmup` untimed steps, then K steps; each stage bracketed by HIP
-        events on the launch stream."""
+    def time_steps(self, K, warmup, prewarm_s=0.0):
+        """Steps back to back for `prewarm_s` seconds (untimed: the shader clock
+        ramps up over the first tens of milliseconds of sustained load after an
+        idle spell), then `warmup` untimed steps, then K steps; each stage
+        bracketed by HIP events on the launch stream."""
         torch, stream = self.torch, self.stream
+        self.prewarm_steps = prewarm(torch, lambda: (self.prep(), self.core()), prewarm_s)
         for _ in range(warmup):
             self.prep()
             self.core()
@@ -651,7 +677,7 @@ def other_configs(headline, args, torch, dj):
         print(f"[bench] also timing {name}", file=sys.stderr, flush=True)
         run = AttentionRun(w, torch, dj)
         K = max(10, args.steps // 5) if w.S > 50000 else args.steps
-        t = run.time_steps(K, args.warmup)
+        t = run.time_steps(K, args.warmup, args.prewarm_s)
         run.release()
         res[name] = {"B": w.B, "H": w.H, "S": w.S, "dtype": w.dtype, "steps": K,
                      "step_ms": t["step_ms"], "step_median_ms": t["step_median_ms"], "prepare_kv_ms": t["prep_ms"],

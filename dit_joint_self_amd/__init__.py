@@ -29,6 +29,8 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
+# Debug build whose attention kernels fill LDS with NaN before their first tile copy.
+DEBUG_LDS_NAN_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn_ldsnan.so")
 
 DIT_DTYPE_BF16 = 0
 DIT_DTYPE_FP8_E4M3 = 1
@@ -102,6 +104,20 @@ def lib() -> ctypes.CDLL:
 
 def lib_loaded() -> bool:
     return _lib is not None
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """A separate handle on another build of the library (for example the
+    LDS-NaN debug build), with the same signatures; the wrappers above keep
+    using the main library."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built")
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
 
 
 def _ptr(x) -> Optional[int]:

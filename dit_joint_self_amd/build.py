@@ -46,21 +46,36 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libditattn.so; returns its path."""
+# Debug variant: every attention kernel fills its LDS buffers with NaN bytes
+# before its first tile copy (DIT_DEBUG_LDS_NAN), so a read of LDS that no copy
+# wrote poisons the output; the GPU tests compare it with the normal build.
+DEBUG_LDS_NAN_LIB = os.path.join(PKG, "libditattn_ldsnan.so")
+DEBUG_LDS_NAN_SOURCES = ["attn_core.hip", "attn_core_fp8.hip"]
+
+
+def _build(lib_path: str, build_dir: str, extra: list, verbose: bool) -> str:
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build(verbose: bool = False, debug_lds_nan: bool = True) -> str:
+    """Compile every HIP source for gfx950 and link libditattn.so (and, by
+    default, the LDS-NaN debug variant); returns the main library's path."""
+    _build(LIB, BUILD_DIR, [], verbose)
+    if debug_lds_nan:
+        _build(DEBUG_LDS_NAN_LIB, os.path.join(BUILD_DIR, "ldsnan"), ["-DDIT_DEBUG_LDS_NAN=1"], verbose)
     return LIB
 
 

@@ -406,7 +406,7 @@ dit_status_t dit_attn_forward_fp8(const void* q8, const void* k8, const void* v8
 
 dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const float* rope_cos,
                               const float* rope_sin, void* out, int B, int H, int S_txt, int S_img, int D,
-                              float scale, dit_dtype_t dtype, void* stream) {
+                              float scale, int dtype, void* stream) {
     if (!q || !k || !v || !out) return fail(DIT_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
     if (S_txt < 0 || S_img < 0)
         return fail(DIT_ERR_INVALID_ARG, "S_txt and S_img must be >= 0 (got %d, %d)", S_txt, S_img);
@@ -417,7 +417,7 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const
     if ((st = check_rope(rope_cos, rope_sin)) != DIT_OK) return st;
     if (dtype == DIT_DTYPE_FP8_E4M3)
         return fail(DIT_ERR_UNSUPPORTED, "fp8 inputs go through dit_attn_forward_fp8 (it takes their scales)");
-    if (dtype != DIT_DTYPE_BF16) return fail(DIT_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (dtype != DIT_DTYPE_BF16) return fail(DIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (!std::isfinite(scale)) return fail(DIT_ERR_INVALID_ARG, "scale must be finite");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(DIT_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");

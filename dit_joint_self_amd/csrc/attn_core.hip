@@ -302,6 +302,14 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     uint4* const kbuf[4] = {kb0, kb1, kb2, kb3};
     uint4* const vbuf[4] = {vb0, vb1, vb2, vb3};
 
+    if (DIT_DEBUG_LDS_NAN) {
+        for (int b = 0; b < 4; ++b) {
+            debug_fill_lds<NW * 64>(kbuf[b], K_PART_CHUNKS);
+            debug_fill_lds<NW * 64>(vbuf[b], V_LDS_CHUNKS);
+        }
+        __syncthreads();
+    }
+
     const CoreWork cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
     const int64_t bh = cw.item / nqt;
     const int qt = cw.item - (int)bh * nqt;

@@ -164,6 +164,10 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     __shared__ uint4 lds1[F8_TILE_CHUNKS];
     __shared__ uint4 lds2[F8_TILE_CHUNKS];
     uint4* const buf[3] = {lds0, lds1, lds2};
+    if (DIT_DEBUG_LDS_NAN) {
+        for (int b = 0; b < 3; ++b) debug_fill_lds<NW * 64>(buf[b], F8_TILE_CHUNKS);
+        __syncthreads();
+    }
 
     const CoreWork cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
     const int64_t bh = cw.item / nqt;

@@ -74,4 +74,18 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, int sof
     }
 }
 
+// Debug builds (DIT_DEBUG_LDS_NAN=1) fill a kernel's LDS buffers with all-ones
+// bytes before its first copy: a NaN in bf16 (0xFFFF) and in e4m3 (0xFF), so
+// any operand read from LDS that the tile copies did not write poisons the
+// output.  The fill ends with a barrier; normal builds compile it away.
+#ifndef DIT_DEBUG_LDS_NAN
+#define DIT_DEBUG_LDS_NAN 0
+#endif
+template <int THREADS>
+__device__ __forceinline__ void debug_fill_lds(uint4* buf, int chunks) {
+    if (DIT_DEBUG_LDS_NAN) {
+        for (int i = threadIdx.x; i < chunks; i += THREADS) buf[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    }
+}
+
 }  // namespace dit

@@ -23,21 +23,24 @@
 
 namespace dit {
 
+// G heads per workgroup: the tile's cos/sin chunks are loaded once and reused
+// for every head of the group, and each head's K loads are issued before the
+// previous head's rotations and stores.
+template <int G>
 __global__ __launch_bounds__(256) void prepare_k_kernel(
     const uint4* __restrict__ k, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
-    uint4* __restrict__ ws, int S, int ntiles, int has_rope) {
+    uint4* __restrict__ ws, int S, int ntiles, int BH, int has_rope) {
     const int tile = blockIdx.x;
-    const int64_t bh = blockIdx.y;
+    const int64_t bh0 = (int64_t)blockIdx.y * G;
+    const int ng = (int)min((int64_t)G, (int64_t)BH - bh0);  // heads of this group (workgroup-uniform)
     const int tid = threadIdx.x;
     const int key0 = tile * KV_TILE;
-    uint4* dst = ws + (bh * ntiles + tile) * (int64_t)K_PART_CHUNKS;
-    const uint4* ksrc = k + bh * (int64_t)S * 16;
 
     // Output chunk x = (row rho, chunk c); chunk 16 of a row is padding.  Every
     // load of the thread is issued before any is used, so the HBM latency is
     // paid about once per workgroup rather than once per chunk.
     constexpr int KI = (K_PART_CHUNKS + 255) / 256;  // chunks per thread (the last partly)
-    uint4 kw[KI];
+    int koff[KI];  // element offset (16-byte units) of the chunk in a head's K; -1: a zero chunk
     float4 cw[KI], sw[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
@@ -45,30 +48,38 @@ __global__ __launch_bounds__(256) void prepare_k_kernel(
         const int rho = x / K_ROW_CHUNKS;
         const int c = x - rho * K_ROW_CHUNKS;
         const int key = key0 + kperm(rho);
-        kw[i] = make_uint4(0, 0, 0, 0);
-        if (x < K_PART_CHUNKS && c < 16 && key < S) {
-            kw[i] = ksrc[(int64_t)key * 16 + c];
-            if (has_rope) {
-                cw[i] = cos_t[(int64_t)key * 16 + c];
-                sw[i] = sin_t[(int64_t)key * 16 + c];
-            }
+        const bool live = x < K_PART_CHUNKS && c < 16 && key < S;
+        koff[i] = live ? key * 16 + c : -1;
+        if (live && has_rope) {
+            cw[i] = cos_t[(int64_t)key * 16 + c];
+            sw[i] = sin_t[(int64_t)key * 16 + c];
         }
     }
+    uint4 kw[2][KI];
+    auto load = [&](int64_t bh, uint4 (&w)[KI]) __attribute__((always_inline)) {
+        const uint4* ksrc = k + bh * (int64_t)S * 16;
 #pragma unroll
-    for (int i = 0; i < KI; ++i) {
-        const int x = tid + i * 256;
-        if (x >= K_PART_CHUNKS) break;
-        const int rho = x / K_ROW_CHUNKS;
-        const int c = x - rho * K_ROW_CHUNKS;
-        const int key = key0 + kperm(rho);
-        uint4 w = kw[i];
-        if (has_rope && c < 16 && key < S) {
-            float f[8];
-            unpack8(w, f);
-            rotate4(f, cw[i], sw[i]);
-            w = pack8(f);
+        for (int i = 0; i < KI; ++i) w[i] = koff[i] >= 0 ? ksrc[koff[i]] : make_uint4(0, 0, 0, 0);
+    };
+    load(bh0, kw[0]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (g >= ng) break;
+        if (g + 1 < ng) load(bh0 + g + 1, kw[(g + 1) & 1]);
+        uint4* dst = ws + ((bh0 + g) * ntiles + tile) * (int64_t)K_PART_CHUNKS;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+            const int x = tid + i * 256;
+            if (x >= K_PART_CHUNKS) break;
+            uint4 w = kw[g & 1][i];
+            if (has_rope && koff[i] >= 0) {
+                float f[8];
+                unpack8(w, f);
+                rotate4(f, cw[i], sw[i]);
+                w = pack8(f);
+            }
+            dst[x] = w;
         }
-        dst[x] = w;
     }
 }
 
@@ -202,10 +213,22 @@ hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_
 hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_t, void* ws, int BH, int S,
                             hipStream_t stream) {
     const int ntiles = (int)num_kv_tiles(S);
-    dim3 grid(ntiles, BH);
-    prepare_k_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(k), reinterpret_cast<const float4*>(cos_t),
-                                               reinterpret_cast<const float4*>(sin_t), static_cast<uint4*>(ws), S,
-                                               ntiles, cos_t != nullptr);
+    const uint4* kk = static_cast<const uint4*>(k);
+    const float4* cc = reinterpret_cast<const float4*>(cos_t);
+    const float4* ss = reinterpret_cast<const float4*>(sin_t);
+    uint4* w = static_cast<uint4*>(ws);
+    const int rope = cos_t != nullptr;
+    // While the two tables (S x 64 x 8 bytes) stay cache resident across the
+    // heads, one head per workgroup is fastest (16896 tokens: 32 us against 35
+    // with two heads); beyond that the per-head table re-reads go to HBM and
+    // four heads per workgroup pay (76112 tokens, 39 MB of tables: 110 -> 80 us).
+    if (rope && (int64_t)S * HEAD_DIM * 4 > ((int64_t)16 << 20) && BH > 1) {
+        dim3 grid(ntiles, (BH + 3) / 4);
+        prepare_k_kernel<4><<<grid, 256, 0, stream>>>(kk, cc, ss, w, S, ntiles, BH, rope);
+    } else {
+        dim3 grid(ntiles, BH);
+        prepare_k_kernel<1><<<grid, 256, 0, stream>>>(kk, cc, ss, w, S, ntiles, BH, rope);
+    }
     return hipGetLastError();
 }
 

@@ -96,8 +96,10 @@ dit_status_t dit_rope_tables(const int32_t* pos, int S, int n_axes, const int32_
  *              means no RoPE; exactly one NULL is DIT_ERR_INVALID_ARG.
  *   out        device bf16 [B, H, S, D], written in full.
  *   scale      softmax scale (normally 1/sqrt(D)); finite.
- *   dtype      must be DIT_DTYPE_BF16; DIT_DTYPE_FP8_E4M3 returns DIT_ERR_UNSUPPORTED
- *              (fp8 inputs need their scales: dit_attn_forward_fp8).
+ *   dtype      a dit_dtype_t value, passed as int (any other value is
+ *              DIT_ERR_INVALID_ARG); must be DIT_DTYPE_BF16: DIT_DTYPE_FP8_E4M3
+ *              returns DIT_ERR_UNSUPPORTED (fp8 inputs need their scales:
+ *              dit_attn_forward_fp8).
  *
  * Rounding: rotated K is rounded to bf16 (RNE); rotated Q is multiplied by
  * scale*log2(e) in fp32 and rounded to bf16; QK^T and PV accumulate in fp32
@@ -111,7 +113,7 @@ dit_status_t dit_rope_tables(const int32_t* pos, int S, int n_axes, const int32_
 dit_status_t dit_attn_forward(const void* q, const void* k, const void* v,
                               const float* rope_cos, const float* rope_sin, void* out,
                               int B, int H, int S_txt, int S_img, int D,
-                              float scale, dit_dtype_t dtype, void* stream);
+                              float scale, int dtype, void* stream);
 
 /*
  * The two stages of dit_attn_forward, for callers that own the workspace
