@@ -38,16 +38,16 @@ FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/
 KERNEL_SOURCES = BF16_SOURCES
 MEASURED_TRAFFIC = {
     # dit_attn_core (attn_core_kernel + attn_merge_kernel), hash over BF16_SOURCES
-    ("c3d9694f14615563", "flux2048"): {"read_bytes": 1082.3e6, "write_bytes": 135.8e6,
+    ("34e594639ee63538", "flux2048"): {"read_bytes": 1040.2e6, "write_bytes": 135.8e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
     # dit_attn_core_fp8 (attn_core_fp8_kernel + attn_merge_kernel), hash over FP8_SOURCES
-    ("589431f18f58cffb", "flux2048_fp8"): {"read_bytes": 693.5e6, "write_bytes": 135.8e6,
+    ("59c598ed5c21e8ed", "flux2048_fp8"): {"read_bytes": 693.5e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
-    ("97d06d7abed0bc27", "flux2048_qkv"): {"read_bytes": 435.8e6, "write_bytes": 331.1e6,
+    ("68292c3f8fd19d45", "flux2048_qkv"): {"read_bytes": 435.7e6, "write_bytes": 331.1e6,
                                            "profile": "profiles/mxfp4_gemm_flux2048_qkv.md"},
     # residual_diff_partials + residual_diff_finish (hash over RESIDUAL_SOURCES)
-    ("c9372c4bfe52bcf7", "flux2048_residual"): {"read_bytes": 207.80e6, "write_bytes": 0.26e6,
+    ("ab5d6a5aa3060f98", "flux2048_residual"): {"read_bytes": 207.80e6, "write_bytes": 0.26e6,
                                                 "profile": "profiles/dbcache_residual_diff_flux2048.md"},
 }
 
