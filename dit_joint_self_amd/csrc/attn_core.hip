@@ -10,9 +10,10 @@
 // Work decomposition
 //   * One workgroup = NW waves; wave w owns QB blocks of 32 queries, so a
 //     workgroup covers BM = NW * 32 * QB consecutive queries of one head.
-//   * Q prologue: each lane loads its query row's 8-dim chunks, applies RoPE
-//     and the factor scale*log2(e) in fp32 and keeps them as bf16 MFMA
-//     B operands for the whole kernel (Q-tile resident in VGPRs).
+//   * Q prologue: coalesced loads of the Q rows and their cos/sin rows (each
+//     load covers whole cache lines), RoPE and the factor scale*log2(e) in
+//     fp32, then through LDS into the MFMA B-operand layout, where the bf16
+//     Q' tile stays for the whole kernel (Q-tile resident in VGPRs).
 //   * K/V stream: 64-key tiles, K' already rotated and laid out by
 //     prepare_kv.hip, V straight from the caller's tensor; both copied
 //     HBM -> LDS by buffer_load_dwordx4 ... lds into four K' and four V
@@ -34,7 +35,7 @@
 //     B-operand layout (see tile_layout.h); the V^T A operand is read from
 //     the key-major V tile with the transposing LDS read ds_read_b64_tr_b16.
 //   * Epilogue: combine the two half-wave partial sums, scale by 1/l, round to
-//     bf16, store rows < S.
+//     bf16, and store rows < S through LDS, so the stores are coalesced.
 //
 // Roofline: MFMA bound.  Algorithmic work per (query block of BM rows, head):
 // 4 * BM * S * 128 flop; per call 4 * B * H * S^2 * 128 flop.
@@ -200,12 +201,13 @@ __device__ __forceinline__ float tile_max(const f32x16 (&sc)[2]) {
 // Lane half hh, register r of key block kb holds key 32 kb + 16 (r >> 3) +
 // 8 hh + (r & 7) of the tile.
 __device__ __forceinline__ void mask_tail(f32x16 (&sc)[2], int j, int S, int hh) {
-    const int base = j * KV_TILE + 8 * hh;
+    if ((j + 1) * KV_TILE <= S) return;          // a whole tile (wave-uniform)
+    const int lim = S - (j * KV_TILE + 8 * hh);  // the lane's key offsets >= lim are past S
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            if (base + 32 * kb + 16 * (r >> 3) + (r & 7) >= S) sc[kb][r] = -INFINITY;
+            if (32 * kb + 16 * (r >> 3) + (r & 7) >= lim) sc[kb][r] = -INFINITY;
 }
 
 // Between the stages: move m if this tile's weights overflow, then add the
@@ -363,36 +365,57 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     if (nt > 2) copy_to_lds<NW, K_PART_CHUNKS>(krsrc, ktile0 + 2 * K_PART_BYTES, kb2, wv, lane);
 
     // ---- Q prologue: RoPE, fold scale*log2(e), round to bf16, keep resident.
+    // The loads are coalesced: load i of lane l reads 16-byte chunk
+    // 8 (i / 4) + l % 8 of row 8 (i % 4) + l / 8 of the wave's 32 rows, so one
+    // load covers the same half of 8 consecutive rows, 8 whole cache lines (a
+    // row per lane would touch 32 lines per load).  Chunk c of a Q row holds
+    // the RoPE pairs 4c..4c+3, as chunk c of a cos/sin row does, so the
+    // rotation runs in that layout.  The rotated chunks reach the MFMA layout
+    // (lane (n, hh), register t: chunk 2t + hh of row n) through a 4 KiB area
+    // per wave in kb3 / vb2, which no copy touches before the first loop
+    // step, in two passes (chunks 0-7 of every row, then chunks 8-15).  Row
+    // rho keeps chunk c' of a pass in slot c' ^ ((rho / 2) % 8), so the
+    // writes (two rows per 16 lanes) and the reads (16 rows per 16 lanes)
+    // both spread over all LDS banks.  Rows past S read row S - 1 and are zeroed.
     bf16x8 qf[8];
     const int rloc = wave * 32 + n;
     const int row = qt * BM + rloc;
     {
-        // Every load of the lane is issued before any is used (rows past S
-        // read row S - 1 and are zeroed afterwards), so the prologue waits for
-        // one memory latency instead of one per chunk.
-        const bool ok = row < S;
-        const int64_t rr = ok ? row : S - 1;
-        const uint4* qrow = q + (bh * S + rr) * 16;
+        const int row0 = qt * BM + wave * 32;  // the wave's first row
         uint4 qw[8];
         float4 cosw[8], sinw[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qw[t] = qrow[2 * t + hh];
-        if (has_rope) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                cosw[t] = cos_t[rr * 16 + 2 * t + hh];
-                sinw[t] = sin_t[rr * 16 + 2 * t + hh];
+        for (int i = 0; i < 8; ++i) {
+            const int r = row0 + 8 * (i & 3) + (lane >> 3);
+            const int c = 8 * (i >> 2) + (lane & 7);
+            const int64_t rr = r < S ? r : S - 1;
+            qw[i] = q[(bh * S + rr) * 16 + c];
+            if (has_rope) {
+                cosw[i] = cos_t[rr * 16 + c];
+                sinw[i] = sin_t[rr * 16 + c];
             }
         }
+        char* const stage =
+            (wave < 4 ? reinterpret_cast<char*>(kb3) : reinterpret_cast<char*>(vb2)) + (wave & 3) * 4096;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            float fv[8];
-            unpack8(qw[t], fv);
-            if (has_rope) rotate4(fv, cosw[t], sinw[t]);
+        for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) fv[e] *= qmul;
-            const uint4 pk = pack8(fv);
-            qf[t] = as_bf16x8(ok ? pk : make_uint4(0, 0, 0, 0));
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int i = 4 * pass + i4;
+                float fv[8];
+                unpack8(qw[i], fv);
+                if (has_rope) rotate4(fv, cosw[i], sinw[i]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fv[e] *= qmul;
+                const int rho = 8 * i4 + (lane >> 3);
+                const uint4 pk = row0 + rho < S ? pack8(fv) : make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4*>(stage + rho * 128 + (((lane & 7) ^ ((rho >> 1) & 7)) << 4)) = pk;
+            }
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) {
+                const int slot = (2 * t4 + hh) ^ ((n >> 1) & 7);
+                qf[4 * pass + t4] = as_bf16x8(*reinterpret_cast<const uint4*>(stage + n * 128 + (slot << 4)));
+            }
         }
     }
 
@@ -460,34 +483,65 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     for (int db = 0; db < 4; ++db) settle(o[db]);
 
     // ---- epilogue: lane (n, hh), register r of dim block db holds dim
-    // 32 db + 8 (r >> 2) + 4 hh + (r & 3) of query n.
+    // 32 db + 8 (r >> 2) + 4 hh + (r & 3) of query n.  The rows go out
+    // through LDS (the tile buffers are free once every wave is past its last
+    // tile), so the global stores are coalesced like the Q loads: one store
+    // covers 1 KiB of consecutive rows instead of touching 32 cache lines.
     const float l = swap_halves_sum(lsum);
+    __syncthreads();
+    const int row0 = qt * BM + wave * 32;  // the wave's first row
     if (cw.partial) {
-        float* pw = part + (int64_t)cw.piece * PART_FLOATS;
-        float4* prow = reinterpret_cast<float4*>(pw + (int64_t)rloc * HEAD_DIM);
+        // fp32 rows of 512 bytes, 16 KiB per wave in buffer `wave`: row n
+        // keeps 16-byte piece p (dims 4p..4p+3) in slot p ^ (n % 16).
+        uint4* const sb = wave < 4 ? (wave < 2 ? (wave == 0 ? kb0 : kb1) : (wave == 2 ? kb2 : kb3))
+                                   : (wave < 6 ? (wave == 4 ? vb0 : vb1) : (wave == 6 ? vb2 : vb3));
+        char* const st = reinterpret_cast<char*>(sb);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                prow[db * 8 + g * 2 + hh] = make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2],
-                                                        o[db][4 * g + 3]);
+            for (int g = 0; g < 4; ++g) {
+                const int piece = db * 8 + g * 2 + hh;
+                *reinterpret_cast<float4*>(st + n * 512 + ((piece ^ (n & 15)) << 4)) =
+                    make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+            }
+        float* pw = part + (int64_t)cw.piece * PART_FLOATS;
+        float4* pwave = reinterpret_cast<float4*>(pw + (int64_t)wave * 32 * HEAD_DIM);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rho = 2 * i + (lane >> 5), c = lane & 31;
+            pwave[rho * 32 + c] = *reinterpret_cast<const float4*>(st + rho * 512 + ((c ^ (rho & 15)) << 4));
+        }
         if (hh == 0) {
             pw[BM * HEAD_DIM + rloc] = -negm[0];
             pw[BM * HEAD_DIM + BM + rloc] = l;
         }
-    } else if (row < S) {
+    } else {
         // Row log-sum-exp of the scaled scores (natural log): the kernel's
         // base-2 scores are scale * log2(e) * q'.k', offset by m, so
         // sum_j exp(scale q'.k_j) = 2^m * l.
-        if (lse != nullptr && hh == 0) lse[bh * S + row] = LN2 * (-negm[0] + __builtin_amdgcn_logf(l));
+        if (lse != nullptr && hh == 0 && row < S) lse[bh * S + row] = LN2 * (-negm[0] + __builtin_amdgcn_logf(l));
+        // bf16 rows of 256 bytes, 8 KiB per wave: row n keeps 8-byte piece p
+        // (dims 4p..4p+3) in slot p ^ n, so 16-byte chunk c sits in slot
+        // c ^ (n / 2), its halves swapped when n is odd.
+        uint4* const sb = wave < 4 ? (wave < 2 ? kb0 : kb1) : (wave < 6 ? kb2 : kb3);
+        char* const st = reinterpret_cast<char*>(sb) + (wave & 1) * 8192;
         const float inv = 1.0f / l;
-        uint2* orow = out + (bh * S + row) * 32;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                orow[db * 8 + g * 2 + hh] = make_uint2(pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                                                       pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+            for (int g = 0; g < 4; ++g) {
+                const int piece = db * 8 + g * 2 + hh;
+                *reinterpret_cast<uint2*>(st + n * 256 + ((piece ^ n) << 3)) =
+                    make_uint2(pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                               pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+            }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int rho = 4 * i + (lane >> 4), c = lane & 15;
+            uint4 w = *reinterpret_cast<const uint4*>(st + rho * 256 + ((c ^ (rho >> 1)) << 4));
+            if (rho & 1) w = make_uint4(w.z, w.w, w.x, w.y);
+            if (row0 + rho < S) reinterpret_cast<uint4*>(out)[(bh * S + row0 + rho) * 16 + c] = w;
+        }
     }
 }
 
