@@ -20,8 +20,8 @@
 #include "tile_layout.h"
 
 namespace dit {
-hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_t, void* ws, int BH, int S,
-                            hipStream_t stream);
+hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_t, void* ws, int* ctl, int BH,
+                            int S, hipStream_t stream);
 hipError_t launch_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* out,
                             float* lse_out, int64_t rows, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const void* x, void* codes, void* scales, int64_t rows, int K, hipStream_t stream);
@@ -34,7 +34,8 @@ hipError_t launch_residual_diff(const void* prev, const void* cur, int64_t n, do
 hipError_t launch_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
                              void* out, int M, int N, int K, hipStream_t stream);
 hipError_t launch_attn_core(const void* q, const void* v, const float* cos_t, const float* sin_t, const void* ws,
-                            void* part, void* out, float* lse, int BH, int S, float qmul, hipStream_t stream);
+                            void* part, int* ctl, void* out, float* lse, int BH, int S, float qmul,
+                            hipStream_t stream);
 size_t core_partial_bytes(int BH, int S);
 hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_t, const float* sin_t, void* ws,
                                  int BH, int S, float k_scale, float v_scale, hipStream_t stream);
@@ -180,15 +181,19 @@ dit_status_t dit_rope_tables(const int32_t* pos, int S, int n_axes, const int32_
 }
 
 // Workspace: the K' tile stream, then (256-byte aligned) the key-range
-// partials of the items that run split.
+// partials of the items that run split, then the attention launch's piece
+// counters (CORE_CTL_BYTES).
 static size_t tiles_bytes(int B, int H, int S) {
     return ((size_t)B * H * (size_t)dit::num_kv_tiles(S) * dit::K_PART_BYTES + 255) & ~(size_t)255;
+}
+static int* ctl_of(void* ws, int B, int H, int S) {
+    return reinterpret_cast<int*>(static_cast<char*>(ws) + tiles_bytes(B, H, S) + dit::core_partial_bytes(B * H, S));
 }
 
 size_t dit_attn_workspace_bytes(int B, int H, int S, int D) {
     if (B < 1 || H < 1 || S < 1 || D != dit::HEAD_DIM) return 0;
     if (check_shape(B, H, S, D) != DIT_OK) return 0;
-    return tiles_bytes(B, H, S) + dit::core_partial_bytes(B * H, S);
+    return tiles_bytes(B, H, S) + dit::core_partial_bytes(B * H, S) + dit::CORE_CTL_BYTES;
 }
 
 dit_status_t dit_attn_prepare_k(const void* k, const float* rope_cos, const float* rope_sin, void* workspace,
@@ -207,7 +212,7 @@ dit_status_t dit_attn_prepare_k(const void* k, const float* rope_cos, const floa
     if (overlaps(workspace, need, k, tbytes)) return fail(DIT_ERR_INVALID_ARG, "workspace overlaps k");
     if ((st = check_tables_apart(rope_cos, rope_sin, S, workspace, need, nullptr, 0)) != DIT_OK) return st;
     if ((st = check_device()) != DIT_OK) return st;
-    return launched(dit::launch_prepare_k(k, rope_cos, rope_sin, workspace, B * H, S,
+    return launched(dit::launch_prepare_k(k, rope_cos, rope_sin, workspace, ctl_of(workspace, B, H, S), B * H, S,
                                           static_cast<hipStream_t>(stream)),
                     "prepare_k_kernel");
 }
@@ -244,8 +249,8 @@ static dit_status_t core_impl(const void* q, const void* v, const float* rope_co
     if ((st = check_device()) != DIT_OK) return st;
     const float qmul = (float)((double)scale * 1.4426950408889634073599);  // scale * log2(e)
     void* part = static_cast<char*>(workspace) + tiles_bytes(B, H, S);
-    return launched(dit::launch_attn_core(q, v, rope_cos, rope_sin, workspace, part, out, lse, B * H, S, qmul,
-                                          static_cast<hipStream_t>(stream)),
+    return launched(dit::launch_attn_core(q, v, rope_cos, rope_sin, workspace, part, ctl_of(workspace, B, H, S), out,
+                                          lse, B * H, S, qmul, static_cast<hipStream_t>(stream)),
                     "attn_core_kernel");
 }
 
@@ -434,11 +439,11 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v, const
         (void)hipGetLastError();
         return fail(DIT_ERR_OUT_OF_MEMORY, "hipMallocAsync of %zu workspace bytes failed", need);
     }
-    hipError_t e = dit::launch_prepare_k(k, rope_cos, rope_sin, ws, B * H, S, s);
+    hipError_t e = dit::launch_prepare_k(k, rope_cos, rope_sin, ws, ctl_of(ws, B, H, S), B * H, S, s);
     if (e == hipSuccess) {
         const float qmul = (float)((double)scale * 1.4426950408889634073599);
-        e = dit::launch_attn_core(q, v, rope_cos, rope_sin, ws, static_cast<char*>(ws) + tiles_bytes(B, H, S), out,
-                                  nullptr, B * H, S, qmul, s);
+        e = dit::launch_attn_core(q, v, rope_cos, rope_sin, ws, static_cast<char*>(ws) + tiles_bytes(B, H, S),
+                                  ctl_of(ws, B, H, S), out, nullptr, B * H, S, qmul, s);
     }
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return launched(e, "dit_attn_forward kernels");

@@ -108,6 +108,58 @@ __device__ __forceinline__ CoreWork core_work(int x, int grid, int full, int nsp
 
 inline int core_grid(const CorePlan& p) { return p.full + p.split * p.nsplit; }
 
+// ---------------------------------------------------------------------------
+// Run-time piece hand-out (bf16 launch).  The whole-range workgroups keep the
+// static XCD-aware order above; the key-range pieces go to workgroups in the
+// order they start: the launch has 2 P piece workgroups for P pieces, each
+// takes the next piece from a counter, and those that find none left end at
+// once.  Workgroups are dispatched round-robin over the XCDs and each XCD
+// starts its share as its CUs free up, so an XCD that finishes its whole
+// items early takes more pieces instead of idling while a slower XCD works
+// through its share.  The counters sit in a CORE_CTL_BYTES block at the end
+// of the workspace: ctl[0] is the next piece, ctl[CTL_STRIDE] the number of
+// piece workgroups that have finished; the last one to finish clears both,
+// so every call leaves them at zero (dit_attn_prepare_k zeroes them first).
+// ---------------------------------------------------------------------------
+constexpr int CORE_CTL_BYTES = 256;
+constexpr int CTL_STRIDE = 16;  // ints between the two counters (64 bytes)
+
+inline int core_pieces(const CorePlan& p) { return p.split * p.nsplit; }
+inline int core_piece_wgs(const CorePlan& p) { return 2 * core_pieces(p); }
+inline int core_grid_dynamic(const CorePlan& p) { return p.full + core_piece_wgs(p); }
+
+__device__ __forceinline__ CoreWork piece_work(int p, int full, int nsplit) {
+    CoreWork w;
+    w.item = full + p / nsplit;
+    w.f = p - (p / nsplit) * nsplit;
+    w.nsplit = nsplit;
+    w.piece = p;
+    w.partial = true;
+    return w;
+}
+
+// The piece of this workgroup, or -1 if none is left (every thread gets the
+// same value; contains a barrier).
+__device__ __forceinline__ int take_piece(int* ctl, int npieces) {
+    __shared__ int taken;
+    if (threadIdx.x == 0)
+        taken = __hip_atomic_fetch_add(ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int p = __builtin_amdgcn_readfirstlane(taken);
+    return p < npieces ? p : -1;
+}
+
+// Called once by every piece workgroup after its last access to ctl[0].
+__device__ __forceinline__ void finish_piece_wg(int* ctl, int nwg) {
+    if (threadIdx.x == 0) {
+        const int done = __hip_atomic_fetch_add(ctl + CTL_STRIDE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == nwg - 1) {
+            __hip_atomic_store(ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ctl + CTL_STRIDE, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 inline size_t core_partial_bytes_for(const CorePlan& p) {
     return (size_t)p.split * p.nsplit * PART_FLOATS * sizeof(float);
 }

@@ -287,7 +287,8 @@ __device__ __forceinline__ void tile_step_last(const uint4* vt, f32x16 (&sc)[2],
 __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ v, const float4* __restrict__ cos_t,
     const float4* __restrict__ sin_t, const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part, int S, int ntiles, int nqt, int full, int nsplit, float qmul, int has_rope) {
+    float* __restrict__ part, int* __restrict__ ctl, int S, int ntiles, int nqt, int full, int nsplit, float qmul,
+    int has_rope) {
     static_assert(QB == 1, "one 32-query block per wave");
     // Tile t's K' part lives in kbuf[t % 4] and its V rows in vbuf[t % 4]
     // (136 KiB of LDS).  Distinct objects and a loop unrolled by four keep
@@ -312,7 +313,18 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
         __syncthreads();
     }
 
-    const CoreWork cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
+    CoreWork cw;
+    if ((int)blockIdx.x < full) {
+        cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
+    } else {
+        const int npieces = ((int)gridDim.x - full) / 2;
+        const int p = take_piece(ctl, npieces);
+        if (p < 0) {
+            finish_piece_wg(ctl, (int)gridDim.x - full);
+            return;
+        }
+        cw = piece_work(p, full, nsplit);
+    }
     const int64_t bh = cw.item / nqt;
     const int qt = cw.item - (int)bh * nqt;
     const int tb = (int)((int64_t)cw.f * ntiles / cw.nsplit);
@@ -515,6 +527,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
             pw[BM * HEAD_DIM + rloc] = -negm[0];
             pw[BM * HEAD_DIM + BM + rloc] = l;
         }
+        finish_piece_wg(ctl, (int)gridDim.x - full);
     } else {
         // Row log-sum-exp of the scaled scores (natural log): the kernel's
         // base-2 scores are scale * log2(e) * q'.k', offset by m, so
@@ -589,7 +602,8 @@ hipError_t launch_merge(const float* part, void* out, float* lse, int S, int nqt
 size_t core_partial_bytes(int BH, int S) { return core_partial_bytes_for(core_plan(BH, S)); }
 
 hipError_t launch_attn_core(const void* q, const void* v, const float* cos_t, const float* sin_t, const void* ws,
-                            void* part, void* out, float* lse, int BH, int S, float qmul, hipStream_t stream) {
+                            void* part, int* ctl, void* out, float* lse, int BH, int S, float qmul,
+                            hipStream_t stream) {
     const CorePlan p = core_plan(BH, S);
     const uint4* wsv = static_cast<const uint4*>(ws);
     const uint4* qv = static_cast<const uint4*>(q);
@@ -598,8 +612,9 @@ hipError_t launch_attn_core(const void* q, const void* v, const float* cos_t, co
     const float4* sv = reinterpret_cast<const float4*>(sin_t);
     const int rope = cos_t != nullptr;
     float* pt = static_cast<float*>(part);
-    attn_core_kernel<<<core_grid(p), NW * 64, 0, stream>>>(qv, vv, cv, sv, wsv, static_cast<uint2*>(out), lse, pt,
-                                                          S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
+    attn_core_kernel<<<core_grid_dynamic(p), NW * 64, 0, stream>>>(qv, vv, cv, sv, wsv, static_cast<uint2*>(out), lse,
+                                                                  pt, ctl, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul,
+                                                                  rope);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && p.split > 0) e = launch_merge(pt, out, lse, S, p.nqt, p.full, p.nsplit, p.split, stream);
     return e;

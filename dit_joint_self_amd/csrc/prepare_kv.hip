@@ -17,6 +17,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "attn_common.h"
 #include "bf16_util.h"
 #include "fp8_util.h"
 #include "tile_layout.h"
@@ -29,8 +30,11 @@ namespace dit {
 template <int G>
 __global__ __launch_bounds__(256) void prepare_k_kernel(
     const uint4* __restrict__ k, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
-    uint4* __restrict__ ws, int S, int ntiles, int BH, int has_rope) {
+    uint4* __restrict__ ws, int* __restrict__ ctl, int S, int ntiles, int BH, int has_rope) {
     const int tile = blockIdx.x;
+    // The attention launch's piece counters start from zero.
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2)
+        __hip_atomic_store(ctl + threadIdx.x * CTL_STRIDE, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int64_t bh0 = (int64_t)blockIdx.y * G;
     const int ng = (int)min((int64_t)G, (int64_t)BH - bh0);  // heads of this group (workgroup-uniform)
     const int tid = threadIdx.x;
@@ -210,8 +214,8 @@ hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_
     return hipGetLastError();
 }
 
-hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_t, void* ws, int BH, int S,
-                            hipStream_t stream) {
+hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_t, void* ws, int* ctl, int BH,
+                            int S, hipStream_t stream) {
     const int ntiles = (int)num_kv_tiles(S);
     const uint4* kk = static_cast<const uint4*>(k);
     const float4* cc = reinterpret_cast<const float4*>(cos_t);
@@ -224,10 +228,10 @@ hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_
     // four heads per workgroup pay (76112 tokens, 39 MB of tables: 110 -> 80 us).
     if (rope && (int64_t)S * HEAD_DIM * 4 > ((int64_t)16 << 20) && BH > 1) {
         dim3 grid(ntiles, (BH + 3) / 4);
-        prepare_k_kernel<4><<<grid, 256, 0, stream>>>(kk, cc, ss, w, S, ntiles, BH, rope);
+        prepare_k_kernel<4><<<grid, 256, 0, stream>>>(kk, cc, ss, w, ctl, S, ntiles, BH, rope);
     } else {
         dim3 grid(ntiles, BH);
-        prepare_k_kernel<1><<<grid, 256, 0, stream>>>(kk, cc, ss, w, S, ntiles, BH, rope);
+        prepare_k_kernel<1><<<grid, 256, 0, stream>>>(kk, cc, ss, w, ctl, S, ntiles, BH, rope);
     }
     return hipGetLastError();
 }

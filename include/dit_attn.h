@@ -134,10 +134,14 @@ dit_status_t dit_attn_forward(const void* q, const void* k, const void* v,
  *   The call also WRITES the workspace: past the prepared tiles it keeps the
  *   partial results of the query tiles whose keys it splits into ranges
  *   (shapes whose work does not fill whole rounds of the GPU's compute
- *   units; 24 heads of 16896 tokens is one).  Core calls that may run at the
- *   same time (on different streams) must therefore not share a workspace,
- *   even when they read the same prepared keys.  q, v, out and the rope
- *   tables must not overlap the workspace, and out must not overlap q or v.
+ *   units; 24 heads of 16896 tokens is one), and two counters with which its
+ *   workgroups share out those ranges at run time.  dit_attn_prepare_k clears
+ *   the counters and every core call leaves them cleared, so a workspace must
+ *   have been prepared (for the same B, H, S) before its first core call, and
+ *   core calls that may run at the same time (on different streams) must not
+ *   share a workspace, even when they read the same prepared keys.  q, v, out
+ *   and the rope tables must not overlap the workspace, and out must not
+ *   overlap q or v.
  */
 size_t dit_attn_workspace_bytes(int B, int H, int S, int D);
 

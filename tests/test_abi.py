@@ -43,12 +43,13 @@ def test_library_exports_every_declared_symbol():
 
 
 def _expected_workspace(B, H, S):
-    """Tile stream (35 KiB per 64-key tile per (batch, head), rounded up to 256 B)
+    """Tile stream (17 KiB of K' per 64-key tile per (batch, head), rounded up to 256 B)
     plus the key-range partials: items = B*H*ceil(S/256) query tiles; the r = items
     mod 256 items past the last full round of 256 CUs run split into the f key
     ranges (1 <= f <= min(8, ntiles)) that minimise ceil(r f / 256) * (1/f + 1/32)
     (rounds of pieces, each piece 1/f of an item plus a fixed 1/32), the smallest
-    f on ties, when f >= 2; each range keeps 256 x 128 + 2 x 256 fp32 values."""
+    f on ties, when f >= 2; each range keeps 256 x 128 + 2 x 256 fp32 values; then
+    256 bytes for the launch's piece counters."""
     from fractions import Fraction
     ntiles = -(-S // 64)
     tiles = (B * H * ntiles * 17408 + 255) // 256 * 256
@@ -59,14 +60,14 @@ def _expected_workspace(B, H, S):
         cost = lambda g: -(-r * g // 256) * (Fraction(1, g) + Fraction(1, 32))
         f = min(range(1, min(8, ntiles) + 1), key=lambda g: (cost(g), g))
     part = r * f * (256 * 128 + 512) * 4 if (r and f >= 2) else 0
-    return tiles + part
+    return tiles + part + 256
 
 
 def test_workspace_bytes():
-    assert dj.dit_attn_workspace_bytes(1, 24, 16896, 128) == 24 * 264 * 17408 + 48 * 5 * 33280 * 4
-    assert dj.dit_attn_workspace_bytes(1, 1, 1, 128) == 17408
+    assert dj.dit_attn_workspace_bytes(1, 24, 16896, 128) == 24 * 264 * 17408 + 48 * 5 * 33280 * 4 + 256
+    assert dj.dit_attn_workspace_bytes(1, 1, 1, 128) == 17408 + 256
     # The video share: 2980 items leave 164 after 11 rounds, split over 3 key ranges.
-    assert dj.dit_attn_workspace_bytes(1, 10, 76112, 128) == 10 * 1190 * 17408 + 164 * 3 * 33280 * 4
+    assert dj.dit_attn_workspace_bytes(1, 10, 76112, 128) == 10 * 1190 * 17408 + 164 * 3 * 33280 * 4 + 256
     for B, H, S in [(1, 24, 16896), (2, 3, 65), (1, 1, 1), (1, 24, 3584), (1, 10, 76112), (1, 2, 320), (3, 7, 999),
                     (1, 1, 130000), (4, 13, 4000), (1, 200, 256)]:
         assert dj.dit_attn_workspace_bytes(B, H, S, 128) == _expected_workspace(B, H, S), (B, H, S)
