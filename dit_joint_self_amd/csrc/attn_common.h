@@ -109,24 +109,39 @@ __device__ __forceinline__ CoreWork core_work(int x, int grid, int full, int nsp
 inline int core_grid(const CorePlan& p) { return p.full + p.split * p.nsplit; }
 
 // ---------------------------------------------------------------------------
-// Run-time piece hand-out (bf16 launch).  The whole-range workgroups keep the
-// static XCD-aware order above; the key-range pieces go to workgroups in the
-// order they start: the launch has 2 P piece workgroups for P pieces, each
-// takes the next piece from a counter, and those that find none left end at
-// once.  Workgroups are dispatched round-robin over the XCDs and each XCD
-// starts its share as its CUs free up, so an XCD that finishes its whole
-// items early takes more pieces instead of idling while a slower XCD works
-// through its share.  The counters sit in a CORE_CTL_BYTES block at the end
-// of the workspace: ctl[0] is the next piece, ctl[CTL_STRIDE] the number of
-// piece workgroups that have finished; the last one to finish clears both,
-// so every call leaves them at zero (dit_attn_prepare_k zeroes them first).
+// Run-time hand-out (bf16 launch).  The whole-range workgroups of all but the
+// last round keep the static XCD-aware order above.  The rest form a pool:
+// the last round of whole items (when there are at least three rounds; with
+// fewer, every whole item stays static so that each XCD streams its own
+// heads' K and V) and then the key-range pieces.  The launch has two pool
+// workgroups per pool unit; each takes the next unit from a counter, and
+// those that find none left end at once.  Workgroups are dispatched
+// round-robin over the XCDs and each XCD starts its share as its CUs free
+// up, so an XCD that runs ahead takes more of the pool instead of idling
+// while a slower XCD works through its share.  The counters sit in a
+// CORE_CTL_BYTES block at the end of the workspace: ctl[0] is the next pool
+// unit, ctl[CTL_STRIDE] the number of pool workgroups that have finished; the
+// last one to finish clears both, so every call leaves them at zero
+// (dit_attn_prepare_k zeroes them first).
 // ---------------------------------------------------------------------------
 constexpr int CORE_CTL_BYTES = 256;
 constexpr int CTL_STRIDE = 16;  // ints between the two counters (64 bytes)
 
 inline int core_pieces(const CorePlan& p) { return p.split * p.nsplit; }
-inline int core_piece_wgs(const CorePlan& p) { return 2 * core_pieces(p); }
-inline int core_grid_dynamic(const CorePlan& p) { return p.full + core_piece_wgs(p); }
+// Whole items in the pool (the last round when there are three or more).
+inline int core_pool_whole(const CorePlan& p) { return p.full >= 3 * MI355X_CUS ? MI355X_CUS : 0; }
+inline int core_pool_units(const CorePlan& p) { return core_pool_whole(p) + core_pieces(p); }
+inline int core_grid_dynamic(const CorePlan& p) { return p.full - core_pool_whole(p) + 2 * core_pool_units(p); }
+
+__device__ __forceinline__ CoreWork whole_work(int item) {
+    CoreWork w;
+    w.item = item;
+    w.f = 0;
+    w.nsplit = 1;
+    w.piece = 0;
+    w.partial = false;
+    return w;
+}
 
 __device__ __forceinline__ CoreWork piece_work(int p, int full, int nsplit) {
     CoreWork w;
@@ -138,19 +153,19 @@ __device__ __forceinline__ CoreWork piece_work(int p, int full, int nsplit) {
     return w;
 }
 
-// The piece of this workgroup, or -1 if none is left (every thread gets the
-// same value; contains a barrier).
-__device__ __forceinline__ int take_piece(int* ctl, int npieces) {
+// The pool unit of this workgroup, or -1 if none is left (every thread gets
+// the same value; contains a barrier).
+__device__ __forceinline__ int take_unit(int* ctl, int nunits) {
     __shared__ int taken;
     if (threadIdx.x == 0)
         taken = __hip_atomic_fetch_add(ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int p = __builtin_amdgcn_readfirstlane(taken);
-    return p < npieces ? p : -1;
+    const int u = __builtin_amdgcn_readfirstlane(taken);
+    return u < nunits ? u : -1;
 }
 
-// Called once by every piece workgroup after its last access to ctl[0].
-__device__ __forceinline__ void finish_piece_wg(int* ctl, int nwg) {
+// Called once by every pool workgroup after its last access to ctl[0].
+__device__ __forceinline__ void finish_pool_wg(int* ctl, int nwg) {
     if (threadIdx.x == 0) {
         const int done = __hip_atomic_fetch_add(ctl + CTL_STRIDE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (done == nwg - 1) {

@@ -287,8 +287,8 @@ __device__ __forceinline__ void tile_step_last(const uint4* vt, f32x16 (&sc)[2],
 __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ v, const float4* __restrict__ cos_t,
     const float4* __restrict__ sin_t, const uint4* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part, int* __restrict__ ctl, int S, int ntiles, int nqt, int full, int nsplit, float qmul,
-    int has_rope) {
+    float* __restrict__ part, int* __restrict__ ctl, int S, int ntiles, int nqt, int full, int nsplit,
+    int pool_whole, float qmul, int has_rope) {
     static_assert(QB == 1, "one 32-query block per wave");
     // Tile t's K' part lives in kbuf[t % 4] and its V rows in vbuf[t % 4]
     // (136 KiB of LDS).  Distinct objects and a loop unrolled by four keep
@@ -313,17 +313,19 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
         __syncthreads();
     }
 
+    // Static whole items first, then the pool (see attn_common.h).
+    const int nstatic = full - pool_whole;
+    const int pool_wgs = (int)gridDim.x - nstatic;
     CoreWork cw;
-    if ((int)blockIdx.x < full) {
-        cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
+    if ((int)blockIdx.x < nstatic) {
+        cw = core_work(blockIdx.x, nstatic, nstatic, nsplit);
     } else {
-        const int npieces = ((int)gridDim.x - full) / 2;
-        const int p = take_piece(ctl, npieces);
-        if (p < 0) {
-            finish_piece_wg(ctl, (int)gridDim.x - full);
+        const int u = take_unit(ctl, pool_wgs / 2);
+        if (u < 0) {
+            finish_pool_wg(ctl, pool_wgs);
             return;
         }
-        cw = piece_work(p, full, nsplit);
+        cw = u < pool_whole ? whole_work(nstatic + u) : piece_work(u - pool_whole, full, nsplit);
     }
     const int64_t bh = cw.item / nqt;
     const int qt = cw.item - (int)bh * nqt;
@@ -527,7 +529,6 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
             pw[BM * HEAD_DIM + rloc] = -negm[0];
             pw[BM * HEAD_DIM + BM + rloc] = l;
         }
-        finish_piece_wg(ctl, (int)gridDim.x - full);
     } else {
         // Row log-sum-exp of the scaled scores (natural log): the kernel's
         // base-2 scores are scale * log2(e) * q'.k', offset by m, so
@@ -556,6 +557,7 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
             if (row0 + rho < S) reinterpret_cast<uint4*>(out)[(bh * S + row0 + rho) * 16 + c] = w;
         }
     }
+    if ((int)blockIdx.x >= nstatic) finish_pool_wg(ctl, pool_wgs);
 }
 
 // Combine the nsplit key-range partials of each split item (the same streaming
@@ -613,8 +615,8 @@ hipError_t launch_attn_core(const void* q, const void* v, const float* cos_t, co
     const int rope = cos_t != nullptr;
     float* pt = static_cast<float*>(part);
     attn_core_kernel<<<core_grid_dynamic(p), NW * 64, 0, stream>>>(qv, vv, cv, sv, wsv, static_cast<uint2*>(out), lse,
-                                                                  pt, ctl, S, p.ntiles, p.nqt, p.full, p.nsplit, qmul,
-                                                                  rope);
+                                                                  pt, ctl, S, p.ntiles, p.nqt, p.full, p.nsplit,
+                                                                  core_pool_whole(p), qmul, rope);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && p.split > 0) e = launch_merge(pt, out, lse, S, p.nqt, p.full, p.nsplit, p.split, stream);
     return e;
