@@ -38,9 +38,9 @@ hipError_t launch_attn_core(const void* q, const void* v, const float* cos_t, co
                             hipStream_t stream);
 size_t core_partial_bytes(int BH, int S);
 hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_t, const float* sin_t, void* ws,
-                                 int BH, int S, float k_scale, float v_scale, hipStream_t stream);
+                                 int* ctl, int BH, int S, float k_scale, float v_scale, hipStream_t stream);
 hipError_t launch_attn_core_fp8(const void* q, float q_scale, const float* cos_t, const float* sin_t, const void* ws,
-                                void* part, void* out, int BH, int S, float qmul, hipStream_t stream);
+                                void* part, int* ctl, void* out, int BH, int S, float qmul, hipStream_t stream);
 size_t core_fp8_partial_bytes(int BH, int S);
 hipError_t launch_rope_tables(const int32_t* pos, int S, int n_axes, const int32_t* axes_dim,
                               double theta, float* cos_t, float* sin_t, hipStream_t stream);
@@ -300,9 +300,14 @@ dit_status_t dit_attn_merge_lse(const void* o_a, const float* lse_a, const void*
 
 // ---------------------------------------------------------------- fp8
 
+// fp8 workspace: header and tiles, the key-range partials, the pool counters.
 static size_t fp8_tiles_bytes(int B, int H, int S) {
     return (dit::F8_HEADER_BYTES + (size_t)B * H * (size_t)dit::num_kv_tiles(S) * dit::F8_TILE_BYTES + 255) &
            ~(size_t)255;
+}
+static int* fp8_ctl_of(void* ws, int B, int H, int S) {
+    return reinterpret_cast<int*>(static_cast<char*>(ws) + fp8_tiles_bytes(B, H, S) +
+                                  dit::core_fp8_partial_bytes(B * H, S));
 }
 
 static dit_status_t check_scale(float s, const char* name) {
@@ -313,7 +318,7 @@ static dit_status_t check_scale(float s, const char* name) {
 size_t dit_attn_workspace_bytes_fp8(int B, int H, int S, int D) {
     if (B < 1 || H < 1 || S < 1 || D != dit::HEAD_DIM) return 0;
     if (check_shape(B, H, S, D) != DIT_OK) return 0;
-    return fp8_tiles_bytes(B, H, S) + dit::core_fp8_partial_bytes(B * H, S);
+    return fp8_tiles_bytes(B, H, S) + dit::core_fp8_partial_bytes(B * H, S) + dit::CORE_CTL_BYTES;
 }
 
 dit_status_t dit_attn_prepare_kv_fp8(const void* k8, const void* v8, float k_scale, float v_scale,
@@ -336,7 +341,8 @@ dit_status_t dit_attn_prepare_kv_fp8(const void* k8, const void* v8, float k_sca
         return fail(DIT_ERR_INVALID_ARG, "workspace overlaps k8 or v8");
     if ((st = check_tables_apart(rope_cos, rope_sin, S, workspace, need, nullptr, 0)) != DIT_OK) return st;
     if ((st = check_device()) != DIT_OK) return st;
-    return launched(dit::launch_prepare_kv_fp8(k8, v8, rope_cos, rope_sin, workspace, B * H, S, k_scale, v_scale,
+    return launched(dit::launch_prepare_kv_fp8(k8, v8, rope_cos, rope_sin, workspace, fp8_ctl_of(workspace, B, H, S),
+                                               B * H, S, k_scale, v_scale,
                                                static_cast<hipStream_t>(stream)),
                     "prepare_kv_fp8_kernel");
 }
@@ -363,7 +369,8 @@ dit_status_t dit_attn_core_fp8(const void* q8, float q_scale, const float* rope_
     if ((st = check_device()) != DIT_OK) return st;
     const float qmul = (float)((double)scale * 1.4426950408889634073599);
     void* part = static_cast<char*>(workspace) + fp8_tiles_bytes(B, H, S);
-    return launched(dit::launch_attn_core_fp8(q8, q_scale, rope_cos, rope_sin, workspace, part, out, B * H, S, qmul,
+    return launched(dit::launch_attn_core_fp8(q8, q_scale, rope_cos, rope_sin, workspace, part,
+                                              fp8_ctl_of(workspace, B, H, S), out, B * H, S, qmul,
                                               static_cast<hipStream_t>(stream)),
                     "attn_core_fp8_kernel");
 }
@@ -398,11 +405,12 @@ dit_status_t dit_attn_forward_fp8(const void* q8, const void* k8, const void* v8
         (void)hipGetLastError();
         return fail(DIT_ERR_OUT_OF_MEMORY, "hipMallocAsync of %zu workspace bytes failed", need);
     }
-    hipError_t e = dit::launch_prepare_kv_fp8(k8, v8, rope_cos, rope_sin, ws, B * H, S, k_scale, v_scale, s);
+    hipError_t e =
+        dit::launch_prepare_kv_fp8(k8, v8, rope_cos, rope_sin, ws, fp8_ctl_of(ws, B, H, S), B * H, S, k_scale, v_scale, s);
     if (e == hipSuccess) {
         const float qmul = (float)((double)scale * 1.4426950408889634073599);
         e = dit::launch_attn_core_fp8(q8, q_scale, rope_cos, rope_sin, ws, static_cast<char*>(ws) + fp8_tiles_bytes(B, H, S),
-                                      out, B * H, S, qmul, s);
+                                      fp8_ctl_of(ws, B, H, S), out, B * H, S, qmul, s);
     }
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return launched(e, "dit_attn_forward_fp8 kernels");

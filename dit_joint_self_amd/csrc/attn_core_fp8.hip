@@ -157,19 +157,35 @@ __device__ __forceinline__ void f8_pv(const uint4* vt, const i32x8& pf, f32x16 (
 
 __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     const uint4* __restrict__ q, float q_scale, const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
-    const uint8_t* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ part, int S, int ntiles, int nqt,
-    int full, int nsplit, float qmul, int has_rope) {
-    // Tile k of the range lives in buf[k % 3] (see the two wave groups below).
+    const uint8_t* __restrict__ ws, uint2* __restrict__ out, float* __restrict__ part, int* __restrict__ ctl, int S,
+    int ntiles, int nqt, int full, int nsplit, int pool_whole, float qmul, int has_rope) {
+    // Tile k of the range lives in buf[k % 3] (see the two wave groups below);
+    // stage: 8 KiB per wave for the Q prologue and the epilogue.
     __shared__ uint4 lds0[F8_TILE_CHUNKS];
     __shared__ uint4 lds1[F8_TILE_CHUNKS];
     __shared__ uint4 lds2[F8_TILE_CHUNKS];
+    __shared__ uint4 stage_all[NW * 512];
     uint4* const buf[3] = {lds0, lds1, lds2};
     if (DIT_DEBUG_LDS_NAN) {
         for (int b = 0; b < 3; ++b) debug_fill_lds<NW * 64>(buf[b], F8_TILE_CHUNKS);
+        debug_fill_lds<NW * 64>(stage_all, NW * 512);
         __syncthreads();
     }
 
-    const CoreWork cw = core_work(blockIdx.x, gridDim.x, full, nsplit);
+    // Static whole items first, then the pool (as in the bf16 kernel; attn_common.h).
+    const int nstatic = full - pool_whole;
+    const int pool_wgs = (int)gridDim.x - nstatic;
+    CoreWork cw;
+    if ((int)blockIdx.x < nstatic) {
+        cw = core_work(blockIdx.x, nstatic, nstatic, nsplit);
+    } else {
+        const int u = take_unit(ctl, pool_wgs / 2);
+        if (u < 0) {
+            finish_pool_wg(ctl, pool_wgs);
+            return;
+        }
+        cw = u < pool_whole ? whole_work(nstatic + u) : piece_work(u - pool_whole, full, nsplit);
+    }
     const int64_t bh = cw.item / nqt;
     const int qt = cw.item - (int)bh * nqt;
     const int tb = (int)((int64_t)cw.f * ntiles / cw.nsplit);
@@ -196,53 +212,70 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
     const int e = qbound > 0.0f ? min(max((int)ceilf(log2f(qbound / E4M3_MAX)), -126), 126) : 0;
     const float qfac = qmul * sk * ldexpf(1.0f, -e);
     const int qscale = E8M0_ONE + e;
+    // The loads are coalesced as in the bf16 kernel: load i of lane l covers
+    // 16-byte chunk l % 8 (16 codes, RoPE pairs 8c..8c+7) of row 8 i + l / 8
+    // of the wave's 32 rows of 128 codes (8 whole cache lines per load), with
+    // cos/sin chunks 2c and 2c + 1 of the same row.  Dequantise, rotate and
+    // requantise run in that layout; the codes reach the MFMA layout (lane
+    // (n, hh): chunks 4 kk + 2 hh + h of row n) through the wave's part of
+    // `stage`, where row rho keeps chunk c in slot c ^ ((rho / 2) % 8) (both
+    // directions spread over all LDS banks).  Rows past S read row S - 1 and
+    // are zeroed.
+    char* const stage = reinterpret_cast<char*>(stage_all) + wave * 8192;
     i32x8 qf[2];
     {
-        // Every load of the lane is issued before any is used (rows past S
-        // read row S - 1 and are zeroed afterwards).
-        const int row = qt * BM + wave * 32 + n;
-        const bool ok = row < S;
-        const int64_t rr = ok ? row : S - 1;
-        const uint4* qrow = q + (bh * S + rr) * 8;
+        const int row0 = qt * BM + wave * 32;  // the wave's first row
+        const int c = lane & 7;
         uint4 qw[4];
-        float4 cosw[8], sinw[8];
+        float4 cosw[4][2], sinw[4][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qw[i] = qrow[(i >> 1) * 4 + hh * 2 + (i & 1)];
-        if (has_rope) {
+        for (int i = 0; i < 4; ++i) {
+            const int r = row0 + 8 * i + (lane >> 3);
+            const int64_t rr = r < S ? r : S - 1;
+            qw[i] = q[(bh * S + rr) * 8 + c];
+            if (has_rope) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c = ((i >> 2) * 4 + hh * 2 + ((i >> 1) & 1));
-                cosw[i] = cos_t[rr * 16 + 2 * c + (i & 1)];
-                sinw[i] = sin_t[rr * 16 + 2 * c + (i & 1)];
+                for (int u = 0; u < 2; ++u) {
+                    cosw[i][u] = cos_t[rr * 16 + 2 * c + u];
+                    sinw[i][u] = sin_t[rr * 16 + 2 * c + u];
+                }
             }
         }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int i = 0; i < 4; ++i) {
+            const uint4 w = qw[i];
+            float fv[16];
+            fp8x4_to_f32(w.x, fv);
+            fp8x4_to_f32(w.y, fv + 4);
+            fp8x4_to_f32(w.z, fv + 8);
+            fp8x4_to_f32(w.w, fv + 12);
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                float t[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) t[x] = fv[8 * g + x] * q_scale;
+                if (has_rope) rotate4(t, cosw[i][g], sinw[i][g]);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) fv[8 * g + x] = clamp_e4m3(t[x] * qfac);
+            }
+            uint32_t code[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) code[x] = f32x4_to_fp8(fv[4 * x], fv[4 * x + 1], fv[4 * x + 2], fv[4 * x + 3]);
+            const int rho = 8 * i + (lane >> 3);
+            const uint4 pk = row0 + rho < S ? make_uint4(code[0], code[1], code[2], code[3]) : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(stage + rho * 128 + ((c ^ ((rho >> 1) & 7)) << 4)) = pk;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                // dims 64 kk + 32 hh + 16 h .. +15: chunk kk * 4 + hh * 2 + h of the row
-                const uint4 w = qw[2 * kk + h];
-                float fv[16];
-                fp8x4_to_f32(w.x, fv);
-                fp8x4_to_f32(w.y, fv + 4);
-                fp8x4_to_f32(w.z, fv + 8);
-                fp8x4_to_f32(w.w, fv + 12);
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    float t[8];
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) t[x] = fv[8 * g + x] * q_scale;
-                    if (has_rope) rotate4(t, cosw[4 * kk + 2 * h + g], sinw[4 * kk + 2 * h + g]);
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) fv[8 * g + x] = clamp_e4m3(t[x] * qfac);
-                }
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int code = (int)f32x4_to_fp8(fv[4 * x], fv[4 * x + 1], fv[4 * x + 2], fv[4 * x + 3]);
-                    qf[kk][4 * h + x] = ok ? code : 0;
-                }
+                const int slot = (4 * kk + 2 * hh + h) ^ ((n >> 1) & 7);
+                const uint4 w = *reinterpret_cast<const uint4*>(stage + n * 128 + (slot << 4));
+                qf[kk][4 * h + 0] = (int)w.x;
+                qf[kk][4 * h + 1] = (int)w.y;
+                qf[kk][4 * h + 2] = (int)w.z;
+                qf[kk][4 * h + 3] = (int)w.w;
             }
-        }
     }
 
     f32x16 o[4], negm = f32x16{};
@@ -333,39 +366,68 @@ __global__ __launch_bounds__(NW * 64) void attn_core_fp8_kernel(
 #pragma unroll
     for (int db = 0; db < 4; ++db) settle(o[db]);
 
-    // ---- epilogue (as in the bf16 kernel), O scaled by the V step.
+    // ---- epilogue (as in the bf16 kernel), O scaled by the V step, through
+    // the wave's part of `stage` so the global stores are coalesced.  The
+    // prologue's reads of it were done before the first barrier.
     const float l = swap_halves_sum(lsum);
     const int rloc = wave * 32 + n;
-    const int row = qt * BM + rloc;
+    const int row0 = qt * BM + wave * 32;
     if (cw.partial) {
+        // fp32 rows in two passes of 64 dims (256 bytes per row): row n keeps
+        // 16-byte piece p of the pass in slot p ^ (n % 16).
         float* pw = part + (int64_t)cw.piece * PART_FLOATS;
-        float4* prow = reinterpret_cast<float4*>(pw + (int64_t)rloc * HEAD_DIM);
+        float4* pwave = reinterpret_cast<float4*>(pw + (int64_t)wave * 32 * HEAD_DIM);
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                prow[db * 8 + g * 2 + hh] = make_float4(o[db][4 * g] * sv, o[db][4 * g + 1] * sv,
-                                                        o[db][4 * g + 2] * sv, o[db][4 * g + 3] * sv);
+            for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int db = 2 * pass + d2, piece = d2 * 8 + g * 2 + hh;
+                    *reinterpret_cast<float4*>(stage + n * 256 + ((piece ^ (n & 15)) << 4)) =
+                        make_float4(o[db][4 * g] * sv, o[db][4 * g + 1] * sv, o[db][4 * g + 2] * sv,
+                                    o[db][4 * g + 3] * sv);
+                }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int rho = 4 * i + (lane >> 4), cc = lane & 15;
+                pwave[rho * 32 + 16 * pass + cc] =
+                    *reinterpret_cast<const float4*>(stage + rho * 256 + ((cc ^ (rho & 15)) << 4));
+            }
+        }
         if (hh == 0) {
             pw[BM * HEAD_DIM + rloc] = -negm[0];
             pw[BM * HEAD_DIM + BM + rloc] = l;
         }
-    } else if (row < S) {
+    } else {
+        // bf16 rows of 256 bytes: row n keeps 8-byte piece p (dims 4p..4p+3)
+        // in slot p ^ n, so 16-byte chunk c sits in slot c ^ (n / 2), its
+        // halves swapped when n is odd.
         const float inv = sv / l;
-        uint2* orow = out + (bh * S + row) * 32;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                orow[db * 8 + g * 2 + hh] = make_uint2(pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                                                       pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+            for (int g = 0; g < 4; ++g) {
+                const int piece = db * 8 + g * 2 + hh;
+                *reinterpret_cast<uint2*>(stage + n * 256 + ((piece ^ n) << 3)) =
+                    make_uint2(pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                               pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+            }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int rho = 4 * i + (lane >> 4), cc = lane & 15;
+            uint4 w = *reinterpret_cast<const uint4*>(stage + rho * 256 + ((cc ^ (rho >> 1)) << 4));
+            if (rho & 1) w = make_uint4(w.z, w.w, w.x, w.y);
+            if (row0 + rho < S) reinterpret_cast<uint4*>(out)[(bh * S + row0 + rho) * 16 + cc] = w;
+        }
     }
+    if ((int)blockIdx.x >= nstatic) finish_pool_wg(ctl, pool_wgs);
 }
 
 size_t core_fp8_partial_bytes(int BH, int S) { return core_partial_bytes_for(core_plan(BH, S)); }
 
 hipError_t launch_attn_core_fp8(const void* q, float q_scale, const float* cos_t, const float* sin_t, const void* ws,
-                                void* part, void* out, int BH, int S, float qmul, hipStream_t stream) {
+                                void* part, int* ctl, void* out, int BH, int S, float qmul, hipStream_t stream) {
     const CorePlan p = core_plan(BH, S);
     const uint4* qv = static_cast<const uint4*>(q);
     const uint8_t* wsv = static_cast<const uint8_t*>(ws);
@@ -373,8 +435,10 @@ hipError_t launch_attn_core_fp8(const void* q, float q_scale, const float* cos_t
     const float4* sv = reinterpret_cast<const float4*>(sin_t);
     const int rope = cos_t != nullptr;
     float* pt = static_cast<float*>(part);
-    attn_core_fp8_kernel<<<core_grid(p), NW * 64, 0, stream>>>(qv, q_scale, cv, sv, wsv, static_cast<uint2*>(out), pt,
-                                                              S, p.ntiles, p.nqt, p.full, p.nsplit, qmul, rope);
+    attn_core_fp8_kernel<<<core_grid_dynamic(p), NW * 64, 0, stream>>>(qv, q_scale, cv, sv, wsv,
+                                                                      static_cast<uint2*>(out), pt, ctl, S, p.ntiles,
+                                                                      p.nqt, p.full, p.nsplit, core_pool_whole(p), qmul,
+                                                                      rope);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && p.split > 0) e = launch_merge(pt, out, nullptr, S, p.nqt, p.full, p.nsplit, p.split, stream);
     return e;

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void prepare_k_kernel(
 __global__ __launch_bounds__(256) void prepare_kv_fp8_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v,
     const float4* __restrict__ cos_t, const float4* __restrict__ sin_t,
-    uint8_t* __restrict__ ws, int S, int ntiles, int has_rope, float k_scale, float v_scale) {
+    uint8_t* __restrict__ ws, int* __restrict__ ctl, int S, int ntiles, int has_rope, float k_scale, float v_scale) {
     __shared__ uint4 vtile[KV_TILE * 8];  // 64 keys x 128 e4m3 codes, key-major
 
     const int tile = blockIdx.x;
@@ -109,6 +109,9 @@ __global__ __launch_bounds__(256) void prepare_kv_fp8_kernel(
         reinterpret_cast<float*>(ws)[0] = sk;
         reinterpret_cast<float*>(ws)[1] = v_scale;
     }
+    // The attention launch's pool counters start from zero.
+    if (tile == 0 && bh == 0 && tid < 2)
+        __hip_atomic_store(ctl + tid * CTL_STRIDE, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint4* dst = reinterpret_cast<uint4*>(ws + F8_HEADER_BYTES) + (bh * ntiles + tile) * (int64_t)F8_TILE_CHUNKS;
     const uint4* ksrc = k + bh * (int64_t)S * 8;
     const uint4* vsrc = v + bh * (int64_t)S * 8;
@@ -204,12 +207,12 @@ __global__ __launch_bounds__(256) void prepare_kv_fp8_kernel(
 }
 
 hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_t, const float* sin_t, void* ws,
-                                 int BH, int S, float k_scale, float v_scale, hipStream_t stream) {
+                                 int* ctl, int BH, int S, float k_scale, float v_scale, hipStream_t stream) {
     const int ntiles = (int)num_kv_tiles(S);
     dim3 grid(ntiles, BH);
     prepare_kv_fp8_kernel<<<grid, 256, 0, stream>>>(
         static_cast<const uint4*>(k), static_cast<const uint4*>(v), reinterpret_cast<const float4*>(cos_t),
-        reinterpret_cast<const float4*>(sin_t), static_cast<uint8_t*>(ws), S, ntiles, cos_t != nullptr, k_scale,
+        reinterpret_cast<const float4*>(sin_t), static_cast<uint8_t*>(ws), ctl, S, ntiles, cos_t != nullptr, k_scale,
         v_scale);
     return hipGetLastError();
 }

@@ -177,8 +177,9 @@ def test_binding_raises_on_error_status():
 
 def test_fp8_entry_points_reject_bad_arguments():
     L = dj.lib()
-    # fp8 workspace: 256-byte header + 19 KiB tiles, plus the same split partials as bf16.
-    assert dj.dit_attn_workspace_bytes_fp8(1, 1, 1, 128) == 256 + 19456
+    # fp8 workspace: 256-byte header + 19 KiB tiles, the same split partials as bf16, the pool counters.
+    # header, one 64-key tile, the launch's pool counters
+    assert dj.dit_attn_workspace_bytes_fp8(1, 1, 1, 128) == 256 + 19456 + 256
     assert dj.dit_attn_workspace_bytes_fp8(1, 1, 64, 64) == 0
     F = L.dit_attn_forward_fp8
     ok = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, sq=0.1, sk=0.1, sv=0.1, out=FAKE * 4)
