@@ -73,7 +73,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast
 constexpr float SUM_LIMIT = 1048576.0f;  // 2^20
 
 // MFMA operand ring: LDS reads run RING - 1 MFMA steps ahead of their use.
-constexpr int RING = 4;
+constexpr int RING = 6;
 
 // K' operand of QK^T step i (dim step i >> 1, key block i & 1), for lane (n, hh).
 __device__ __forceinline__ bf16x8 k_operand(const uint4* kt, int i, int n, int hh) {
