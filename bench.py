@@ -38,10 +38,10 @@ FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/
 KERNEL_SOURCES = BF16_SOURCES
 MEASURED_TRAFFIC = {
     # dit_attn_core (attn_core_kernel + attn_merge_kernel), hash over BF16_SOURCES
-    ("34e594639ee63538", "flux2048"): {"read_bytes": 1040.2e6, "write_bytes": 135.8e6,
+    ("f26581d5c5880a72", "flux2048"): {"read_bytes": 1045.3e6, "write_bytes": 135.8e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
     # dit_attn_core_fp8 (attn_core_fp8_kernel + attn_merge_kernel), hash over FP8_SOURCES
-    ("59c598ed5c21e8ed", "flux2048_fp8"): {"read_bytes": 693.5e6, "write_bytes": 135.8e6,
+    ("5b720b2b819d28e1", "flux2048_fp8"): {"read_bytes": 711.7e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
     ("68292c3f8fd19d45", "flux2048_qkv"): {"read_bytes": 435.7e6, "write_bytes": 331.1e6,
