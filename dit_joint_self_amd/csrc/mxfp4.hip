@@ -314,22 +314,31 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
 
     // acc[nb][mb]: lane (n_lane, hh), register r holds C[m][n .. n+3] with
     // m = m0 + 64 wm + 32 mb + n_lane, n = n0 + 128 wn + 32 nb + 8 (r >> 2) + 4 hh + (r & 3).
+    // The wave's 64 x 128 block leaves through LDS (16 KiB per wave in the
+    // stages, free once every wave is past its last step), so each 8-byte
+    // store instruction covers two whole 256-byte row segments instead of
+    // 32 rows: row rho keeps 8-byte piece p (columns 4p..4p+3) in slot p ^ (rho % 32),
+    // which spreads both the writes (32 rows per lane group) and the reads
+    // (32 pieces of one row) over all LDS banks.
+    __syncthreads();
+    char* const blk = reinterpret_cast<char*>(wave < 4 ? &st0 : &st1) + (wave & 3) * 16384;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int m = m0 + 64 * wm + 32 * mb + n_lane;
-        if (m >= M) continue;
-        uint2* orow = out + (int64_t)m * (N / 4);
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const int n = n0 + 128 * wn + 32 * nb + 8 * gq + 4 * hh;
-                if (n < N) {
-                    const f32x16& c = acc[nb][mb];
-                    orow[n / 4] = make_uint2(pack_bf16x2(c[4 * gq], c[4 * gq + 1]),
-                                             pack_bf16x2(c[4 * gq + 2], c[4 * gq + 3]));
-                }
+                const int rho = 32 * mb + n_lane, piece = 8 * nb + 2 * gq + hh;
+                const f32x16& c = acc[nb][mb];
+                *reinterpret_cast<uint2*>(blk + rho * 256 + ((piece ^ (rho & 31)) << 3)) =
+                    make_uint2(pack_bf16x2(c[4 * gq], c[4 * gq + 1]), pack_bf16x2(c[4 * gq + 2], c[4 * gq + 3]));
             }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int rho = 2 * i + (lane >> 5), piece = lane & 31;
+        const int m = m0 + 64 * wm + rho, n = n0 + 128 * wn + 4 * piece;
+        const uint2 v = *reinterpret_cast<const uint2*>(blk + rho * 256 + ((piece ^ (rho & 31)) << 3));
+        if (m < M && n < N) out[(int64_t)m * (N / 4) + n / 4] = v;
     }
 }
 
