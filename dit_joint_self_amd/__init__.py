@@ -20,8 +20,9 @@ __all__ = [
     "LIB_PATH", "DitAttnError", "lib", "lib_loaded", "dit_last_error", "dit_abi_version",
     "dit_rope_tables", "dit_attn_forward", "dit_attn_workspace_bytes", "dit_attn_prepare_k",
     "dit_attn_core", "dit_attn_workspace_bytes_fp8", "dit_attn_prepare_kv_fp8", "dit_attn_core_fp8",
-    "dit_attn_forward_fp8", "dit_attn_core_lse", "dit_attn_merge_lse", "dit_mxfp4_quantize", "dit_mxfp4_gemm",
-    "dit_mxfp4_linear", "dit_dbcache_workspace_bytes", "dit_dbcache_residual_diff",
+    "dit_attn_forward_fp8", "dit_attn_core_lse", "dit_attn_merge_lse", "dit_mxfp4_scale_bytes",
+    "dit_mxfp4_quantize", "dit_mxfp4_gemm", "dit_mxfp4_linear", "mxfp4_scale_shape", "mxfp4_scales_to_tiles",
+    "mxfp4_scales_from_tiles", "dit_dbcache_workspace_bytes", "dit_dbcache_residual_diff",
     "dit_dbcache_residual_diff_noalloc", "dit_clock_probe",
     "dit_wall_clock_khz", "EXPORTED_SYMBOLS", "DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED",
     "DIT_ERR_NO_DEVICE", "DIT_ERR_OUT_OF_MEMORY", "DIT_ERR_LAUNCH", "DIT_DTYPE_BF16",
@@ -64,6 +65,7 @@ _SIGNATURES = {
     "dit_attn_forward_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "dit_attn_core_lse": (_I, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _I, _I, _I, _I, _F, _P]),
     "dit_attn_merge_lse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "dit_mxfp4_scale_bytes": (ctypes.c_size_t, [_I, _I]),
     "dit_mxfp4_quantize": (_I, [_P, _P, _P, _I, _I, _P]),
     "dit_mxfp4_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dit_mxfp4_linear": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
@@ -348,8 +350,40 @@ def dit_attn_merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=No
 
 # ---------------------------------------------------------------- MXFP4 linear layers
 
+def mxfp4_scale_shape(rows: int, K: int):
+    """Shape of the tiled E8M0 scale array the library uses for an MXFP4 [rows, K]
+    operand: (ceil(rows / 32), ceil(K / 256), 256) bytes, tile (i, g) holding the
+    scales of blocks 8g..8g+7 of rows 32i..32i+31, 8 bytes per row (see
+    include/dit_attn.h)."""
+    return (-(-rows // 32), -(-K // 256), 256)
+
+
+def dit_mxfp4_scale_bytes(rows: int, K: int) -> int:
+    return int(lib().dit_mxfp4_scale_bytes(int(rows), int(K)))
+
+
+def mxfp4_scales_to_tiles(scales):
+    """numpy uint8 [rows, K/32] (row-major scales) -> the tiled array of
+    mxfp4_scale_shape (unused bytes zero).  A layout permutation only."""
+    import numpy as np
+    rows, nb = scales.shape
+    nt, g, _ = mxfp4_scale_shape(rows, nb * 32)
+    pad = np.zeros((nt * 32, g * 8), dtype=np.uint8)
+    pad[:rows, :nb] = scales
+    return np.ascontiguousarray(pad.reshape(nt, 32, g, 8).transpose(0, 2, 1, 3)).reshape(nt, g, 256)
+
+
+def mxfp4_scales_from_tiles(tiles, rows: int, K: int):
+    """The inverse of mxfp4_scales_to_tiles: tiled uint8 -> row-major [rows, K/32]."""
+    import numpy as np
+    nt, g, _ = mxfp4_scale_shape(rows, K)
+    t = np.asarray(tiles).reshape(nt, g, 32, 8).transpose(0, 2, 1, 3).reshape(nt * 32, g * 8)
+    return np.ascontiguousarray(t[:rows, :K // 32])
+
+
 def dit_mxfp4_quantize(x, codes=None, scales=None, stream=None):
-    """bf16 [rows, K] -> (codes uint8 [rows, K/2], scales uint8 [rows, K/32]) on the device."""
+    """bf16 [rows, K] -> (codes uint8 [rows, K/2], scales uint8 in the tiled shape
+    mxfp4_scale_shape(rows, K)) on the device."""
     import torch
     _tensor(x, "x", ["bfloat16"], ndim=2)
     rows, K = (int(s) for s in x.shape)
@@ -358,16 +392,17 @@ def dit_mxfp4_quantize(x, codes=None, scales=None, stream=None):
     if codes is None:
         codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(mxfp4_scale_shape(rows, K), dtype=torch.uint8, device=x.device)
     _tensor(codes, "codes", ["uint8"], shape=(rows, K // 2))
-    _tensor(scales, "scales", ["uint8"], shape=(rows, K // 32))
+    _tensor(scales, "scales", ["uint8"], shape=mxfp4_scale_shape(rows, K))
     _same_gpu(x=x, codes=codes, scales=scales)
     _check(lib().dit_mxfp4_quantize(_ptr(x), _ptr(codes), _ptr(scales), rows, K, _stream(stream)))
     return codes, scales
 
 
 def dit_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out=None, stream=None):
-    """out [M, N] bf16 = deq(A) deq(W)^T from MXFP4 codes/scales ([M, K/2], [M, K/32], [N, K/2], [N, K/32])."""
+    """out [M, N] bf16 = deq(A) deq(W)^T from MXFP4 codes [M, K/2], [N, K/2] and
+    tiled scales (mxfp4_scale_shape(M, K), mxfp4_scale_shape(N, K))."""
     import torch
     _tensor(a_codes, "a_codes", ["uint8"], ndim=2)
     _tensor(w_codes, "w_codes", ["uint8"], ndim=2)
@@ -375,8 +410,8 @@ def dit_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out=None, stream=None):
     if K % 32:
         raise ValueError(f"K = {K} must be a multiple of 32")
     _tensor(w_codes, "w_codes", ["uint8"], shape=(N, K // 2))
-    _tensor(a_scales, "a_scales", ["uint8"], shape=(M, K // 32))
-    _tensor(w_scales, "w_scales", ["uint8"], shape=(N, K // 32))
+    _tensor(a_scales, "a_scales", ["uint8"], shape=mxfp4_scale_shape(M, K))
+    _tensor(w_scales, "w_scales", ["uint8"], shape=mxfp4_scale_shape(N, K))
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
     _tensor(out, "out", ["bfloat16"], shape=(M, N))
@@ -387,7 +422,8 @@ def dit_mxfp4_gemm(a_codes, a_scales, w_codes, w_scales, out=None, stream=None):
 
 
 def dit_mxfp4_linear(x, w_codes, w_scales, out=None, stream=None):
-    """x bf16 [M, K] times the MXFP4 weight [N, K]^T: dynamic per-1x32 quantisation + A4W4 GEMM."""
+    """x bf16 [M, K] times the MXFP4 weight [N, K]^T (codes [N, K/2], tiled scales
+    mxfp4_scale_shape(N, K)): dynamic per-1x32 quantisation + A4W4 GEMM."""
     import torch
     _tensor(x, "x", ["bfloat16"], ndim=2)
     M, K = (int(s) for s in x.shape)
@@ -396,7 +432,7 @@ def dit_mxfp4_linear(x, w_codes, w_scales, out=None, stream=None):
     _tensor(w_codes, "w_codes", ["uint8"], ndim=2)
     N = int(w_codes.shape[0])
     _tensor(w_codes, "w_codes", ["uint8"], shape=(N, K // 2))
-    _tensor(w_scales, "w_scales", ["uint8"], shape=(N, K // 32))
+    _tensor(w_scales, "w_scales", ["uint8"], shape=mxfp4_scale_shape(N, K))
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _tensor(out, "out", ["bfloat16"], shape=(M, N))

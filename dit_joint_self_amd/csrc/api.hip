@@ -25,6 +25,7 @@ hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_
 hipError_t launch_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* out,
                             float* lse_out, int64_t rows, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const void* x, void* codes, void* scales, int64_t rows, int K, hipStream_t stream);
+size_t mx_scale_bytes(int64_t rows, int K);
 size_t residual_diff_workspace_bytes();
 size_t residual_diff_scratch_bytes();
 hipError_t residual_diff_scratch(int dev, void** ptr);
@@ -48,7 +49,7 @@ hipError_t launch_rope_tables(const int32_t* pos, int S, int n_axes, const int32
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int kMaxDevices = 64;
 // Smallest query tile any kernel variant uses; bounds the workgroup count.
 constexpr int kMinBlockM = 128;
@@ -471,13 +472,18 @@ static dit_status_t check_mx_rows(int rows, int K, const char* what) {
 
 static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+size_t dit_mxfp4_scale_bytes(int rows, int K) {
+    if (rows < 1 || K < 32 || K % 32) return 0;
+    return dit::mx_scale_bytes(rows, K);
+}
+
 dit_status_t dit_mxfp4_quantize(const void* x, void* codes, void* scales, int rows, int K, void* stream) {
     if (!x || !codes || !scales) return fail(DIT_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
     dit_status_t st = check_mx_rows(rows, K, "dit_mxfp4_quantize");
     if (st != DIT_OK) return st;
     if (K % 32) return fail(DIT_ERR_INVALID_ARG, "K must be a multiple of 32 (got %d)", K);
     if (!aligned16(x) || !aligned(codes, 4)) return fail(DIT_ERR_INVALID_ARG, "x must be 16-byte and codes 4-byte aligned");
-    const size_t xb = (size_t)rows * K * 2, cb = (size_t)rows * K / 2, sb = (size_t)rows * K / 32;
+    const size_t xb = (size_t)rows * K * 2, cb = (size_t)rows * K / 2, sb = dit::mx_scale_bytes(rows, K);
     if (overlaps(codes, cb, x, xb) || overlaps(scales, sb, x, xb) || overlaps(codes, cb, scales, sb))
         return fail(DIT_ERR_INVALID_ARG, "x, codes and scales must not overlap");
     if ((st = check_device()) != DIT_OK) return st;
@@ -498,8 +504,8 @@ static dit_status_t check_gemm(const void* a_codes, const void* a_scales, const 
     if (!aligned(out, 8)) return fail(DIT_ERR_INVALID_ARG, "out must be 8-byte aligned");
     const size_t ob = (size_t)M * N * 2;
     if ((a_codes && overlaps(out, ob, a_codes, (size_t)M * K / 2)) ||
-        (a_scales && overlaps(out, ob, a_scales, (size_t)M * K / 32)) || overlaps(out, ob, w_codes, (size_t)N * K / 2) ||
-        overlaps(out, ob, w_scales, (size_t)N * K / 32))
+        (a_scales && overlaps(out, ob, a_scales, dit::mx_scale_bytes(M, K))) ||
+        overlaps(out, ob, w_codes, (size_t)N * K / 2) || overlaps(out, ob, w_scales, dit::mx_scale_bytes(N, K)))
         return fail(DIT_ERR_INVALID_ARG, "out overlaps an input");
     return DIT_OK;
 }
@@ -525,7 +531,7 @@ dit_status_t dit_mxfp4_linear(const void* x, const void* w_codes, const void* w_
     if (overlaps(out, (size_t)M * N * 2, x, (size_t)M * K * 2)) return fail(DIT_ERR_INVALID_ARG, "out overlaps x");
     if ((st = check_device()) != DIT_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t cb = ((size_t)M * K / 2 + 255) & ~(size_t)255, sb = (size_t)M * K / 32;
+    const size_t cb = ((size_t)M * K / 2 + 255) & ~(size_t)255, sb = dit::mx_scale_bytes(M, K);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, cb + sb, s) != hipSuccess) {
         (void)hipGetLastError();

@@ -7,10 +7,17 @@
 // along the reduction axis), and runs them as an activation quantisation
 // kernel plus an A4W4 matrix-core GEMM (section "MXFP4 Kernel").
 //
-// Formats (row-major, shared by the quantiser and the GEMM):
-//   codes  [R, K/2] bytes: element k of a row in byte k/2, low nibble for even
-//          k; E2M1 = sign, 2 exponent bits (bias 1), 1 mantissa bit.
-//   scales [R, K/32] bytes: E8M0 biased exponent of each 32-element block.
+// Formats (shared by the quantiser and the GEMM):
+//   codes  [R, K/2] bytes, row-major: element k of a row in byte k/2, low
+//          nibble for even k; E2M1 = sign, 2 exponent bits (bias 1), 1 mantissa bit.
+//   scales E8M0 biased exponent of each 32-element block, in tiles of 32 rows
+//          x 8 blocks (256 contiguous bytes, row-major inside the tile):
+//          block b of row r at byte ((r / 32) * G + b / 8) * 256 + (r % 32) * 8
+//          + b % 8, with G = ceil(K / 256) tiles per row of tiles
+//          (mx_scale_index).  A GEMM step (256 of K) of a 256-row operand tile
+//          then reads eight whole 256-byte tiles instead of 8 bytes from each of
+//          256 rows 96 bytes apart; bytes of rows past R or blocks past K/32 are
+//          never read.
 //
 // Quantisation of a block V (the MX rule): X = floor(log2 max|V|) - 2 (the
 // largest E2M1 exponent), clamped to [-127, 127] (an all-zero block takes
@@ -42,13 +49,22 @@ namespace dit {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// Byte of block b of row r in the tiled scale layout (G tiles per row of tiles).
+__host__ __device__ __forceinline__ int64_t mx_scale_index(int64_t r, int b, int G) {
+    return ((r >> 5) * G + (b >> 3)) * 256 + (r & 31) * 8 + (b & 7);
+}
+__host__ __device__ __forceinline__ int64_t mx_scale_size(int64_t rows, int K) {
+    return ((rows + 31) / 32) * ((K + 255) / 256) * 256;
+}
+size_t mx_scale_bytes(int64_t rows, int K) { return (size_t)mx_scale_size(rows, K); }
+
 // ---------------------------------------------------------------- quantiser
 
 // Thread t: elements 8t .. 8t+7 of the flattened [R, K] input (K % 32 == 0, so
 // 4 consecutive lanes hold one block).  Grid-stride.
 __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint4* __restrict__ x,
                                                              uint32_t* __restrict__ codes,
-                                                             uint8_t* __restrict__ scales, int64_t groups) {
+                                                             uint8_t* __restrict__ scales, int64_t groups, int K) {
     // groups is a multiple of 4 and t steps in multiples of 4, so the 4 lanes of
     // a block enter and leave the loop together (the shuffles need all four)
     for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < groups; t += (int64_t)gridDim.x * 256) {
@@ -72,7 +88,11 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint4* __rest
             packed |= c << (4 * i);
         }
         codes[t] = packed;
-        if ((t & 3) == 0) scales[t >> 2] = (uint8_t)(X + 127);
+        if ((t & 3) == 0) {
+            const int64_t blk = t >> 2, per_row = K / 32;
+            const int64_t r = blk / per_row;
+            scales[mx_scale_index(r, (int)(blk - r * per_row), (K + 255) / 256)] = (uint8_t)(X + 127);
+        }
     }
 }
 
@@ -82,7 +102,7 @@ hipError_t launch_mxfp4_quantize(const void* x, void* codes, void* scales, int64
     const int64_t blocks = std::min<int64_t>((groups + 255) / 256, (int64_t)MI355X_CUS * 32);
     mxfp4_quantize_kernel<<<(int)blocks, 256, 0, stream>>>(static_cast<const uint4*>(x),
                                                            static_cast<uint32_t*>(codes),
-                                                           static_cast<uint8_t*>(scales), groups);
+                                                           static_cast<uint8_t*>(scales), groups, K);
     return hipGetLastError();
 }
 
@@ -94,8 +114,10 @@ constexpr int GK = 256;      // K per pipeline step: four 64-deep MFMA steps, 12
 constexpr int GWAVES = 8;    // wave (wm, wn) = (w & 3, w >> 2): 64 rows x 128 columns each
 constexpr int G_GROUP = 8;   // column tiles per group of the workgroup order
 constexpr int G_CODE_PIECES = (GM + GN) * (GK / 2) / 1024 / GWAVES;   // 1 KiB code pieces per wave and step (8)
-constexpr int G_SCALE_PIECES = (GM + GN) * (GK / 128) / 64 / GWAVES;  // 64-word scale pieces per wave and step (2)
-static_assert(G_SCALE_PIECES * GWAVES == 16 && G_CODE_PIECES * GWAVES == 64, "pieces are spread evenly");
+static_assert(G_CODE_PIECES * GWAVES == 64, "pieces are spread evenly");
+// Scales of a step: 8 whole scale tiles (256 rows x 8 bytes) per operand, two
+// 1 KiB pieces each, copied by waves 0..3 (A: waves 0-1, W: waves 2-3).
+static_assert(GM == 256 && GN == 256 && GK == 256, "one scale tile column per step and 32-row tile");
 
 // LDS image of a tile: rows of GK/2 = 128 bytes = eight 16-byte chunks; chunk c
 // of row r sits at position c ^ ((r >> 1) & 7), so the 16 lanes of an LDS read
@@ -127,13 +149,12 @@ __device__ __forceinline__ f32x16 mfma_fp4(const uint4& a, const uint4& b, const
 }
 
 // One pipeline stage: the A tile (GM rows) and the W tile (GN rows) of a K
-// step, and the step's eight block scales of every row (two 32-bit words per
-// row), ordered so each lane's words are contiguous: sa[wm][n_lane][mb][word]
-// for row 64 wm + 32 mb + n_lane of A, sw[wn][n_lane][nb][word] for row
-// 128 wn + 32 nb + n_lane of W.  A lane reads its A words with one 16-byte
-// and its W words with two 16-byte LDS reads (4-byte reads would be merged into
-// ds_read2 instructions that lose the LDS alias information, and the compiler
-// would then make them wait for every copy in flight).
+// step, and the step's eight block scales of every row (8 bytes per row, row
+// r at byte 8 r: the step's eight scale tiles as they are in memory).  A lane
+// reads the 8 bytes of each of its rows with a 16-byte LDS read of the row
+// pair (8-byte reads would be merged into ds_read2 instructions that lose the
+// LDS alias information, and the compiler would then make them wait for
+// every copy in flight).
 struct GStage {
     uint4 a[GM * 8];
     uint4 w[GN * 8];
@@ -169,42 +190,37 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
     const int r = logical - g * G_GROUP * m_tiles;
     const int m0 = (r / gw) * GM;
     const int n0 = (g * G_GROUP + r % gw) * GN;
-    const int rowbytes = K / 2, srow = K / 32;
+    const int rowbytes = K / 2, G = (K + 255) / 256;  // G: scale tiles per row of tiles
     const int nk = (K + GK - 1) / GK;      // the last step is a half step when K % 256 == 128
     const bool half_last = (K % GK) != 0;
 
     const __amdgpu_buffer_rsrc_t ra = raw_rsrc(a_codes, (uint32_t)((int64_t)M * rowbytes));
     const __amdgpu_buffer_rsrc_t rw = raw_rsrc(w_codes, (uint32_t)((int64_t)N * rowbytes));
-    const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(a_scales, (uint32_t)((int64_t)M * srow));
-    const __amdgpu_buffer_rsrc_t rsw = raw_rsrc(w_scales, (uint32_t)((int64_t)N * srow));
+    const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(a_scales, (uint32_t)mx_scale_size(M, K));
+    const __amdgpu_buffer_rsrc_t rsw = raw_rsrc(w_scales, (uint32_t)mx_scale_size(N, K));
 
     // code pieces of this wave: pieces wave + 8 j of the 64 per step (A: 0..31, W: 32..63);
     // their per-lane offsets are recomputed at each step (a few integer ops) to spare registers
-    // scale pieces of this wave: pieces 2 wave, 2 wave + 1 of the 16 (A: 0..7, W: 8..15); lane l of
-    // piece q fills word 64 q' + l of sa / sw, gathered from the row and word the order above puts there
-    const bool scale_of_a = wave < GWAVES / 2;
-    int soff[G_SCALE_PIECES];
-#pragma unroll
-    for (int j = 0; j < G_SCALE_PIECES; ++j) {
-        const int wd = 64 * (2 * (scale_of_a ? wave : wave - GWAVES / 2) + j) + lane;
-        const int word = wd & 1;
-        const int row = scale_of_a ? 64 * (wd >> 7) + 32 * ((wd >> 1) & 1) + ((wd >> 2) & 31)
-                                   : 128 * (wd >> 8) + 32 * ((wd >> 1) & 3) + ((wd >> 3) & 31);
-        soff[j] = min((scale_of_a ? m0 : n0) + row, (scale_of_a ? M : N) - 1) * srow + 4 * word;
+    // scale piece of waves 0..3: piece q = wave & 1 of A (waves 0, 1) or W
+    // (waves 2, 3) covers the operand's row tiles 4 q .. 4 q + 3; lane l brings
+    // 16-byte chunk l % 16 of tile 4 q + l / 16 (row tiles past the matrix
+    // repeat its last one, never stored).  The step adds kk * 256 bytes.
+    const bool scale_copier = wave < 4, scale_of_a = wave < 2;
+    int soff = 0;
+    {
+        const int q = wave & 1, t = 4 * q + (lane >> 4);
+        const int rt0 = (scale_of_a ? m0 : n0) / 32, nrt = ((scale_of_a ? M : N) + 31) / 32;
+        soff = min(rt0 + t, nrt - 1) * G * 256 + (lane & 15) * 16;
     }
-    const int sbase = 64 * 2 * (scale_of_a ? wave : wave - GWAVES / 2);   // first word of this wave's pieces
 
     auto copy_stage = [&](int kk, GStage& d) {
-#pragma unroll
-        for (int j = 0; j < G_SCALE_PIECES; ++j) {
-            if (scale_of_a)  // wave-uniform
+        if (scale_copier) {  // wave-uniform
+            if (scale_of_a)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsa, (__attribute__((address_space(3))) void*)(reinterpret_cast<uint32_t*>(d.sa) + sbase + 64 * j),
-                    4, soff[j], kk * (GK / 32), 0, 0);
+                    rsa, (__attribute__((address_space(3))) void*)(d.sa + 64 * (wave & 1)), 16, soff, kk * 256, 0, 0);
             else
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsw, (__attribute__((address_space(3))) void*)(reinterpret_cast<uint32_t*>(d.sw) + sbase + 64 * j),
-                    4, soff[j], kk * (GK / 32), 0, 0);
+                    rsw, (__attribute__((address_space(3))) void*)(d.sw + 64 * (wave & 1)), 16, soff, kk * 256, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < G_CODE_PIECES; ++j) {
@@ -235,11 +251,22 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
         constexpr int NSUB = decltype(nsub_c)::value;
         __builtin_amdgcn_sched_barrier(0);
         // scale words: A rows (mb, word) and W rows (nb, word) of this lane
-        const uint4 wa = t.sa[32 * wm + n_lane];
-        const uint4 wwlo = t.sw[2 * (32 * wn + n_lane)];
-        const uint4 wwhi = t.sw[2 * (32 * wn + n_lane) + 1];
-        const uint32_t sa_w[2][2] = {{wa.x, wa.y}, {wa.z, wa.w}};
-        const uint32_t sw_w[4][2] = {{wwlo.x, wwlo.y}, {wwlo.z, wwlo.w}, {wwhi.x, wwhi.y}, {wwhi.z, wwhi.w}};
+        // row r's 8 bytes are half (r & 1) of 16-byte chunk r / 2; every row of
+        // this lane has the parity of n_lane
+        const bool odd = n_lane & 1;
+        uint32_t sa_w[2][2], sw_w[4][2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const uint4 v = t.sa[(64 * wm + 32 * mb + n_lane) >> 1];
+            sa_w[mb][0] = odd ? v.z : v.x;
+            sa_w[mb][1] = odd ? v.w : v.y;
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const uint4 v = t.sw[(128 * wn + 32 * nb + n_lane) >> 1];
+            sw_w[nb][0] = odd ? v.z : v.x;
+            sw_w[nb][1] = odd ? v.w : v.y;
+        }
         // operand fragments of MFMA step s, read just before its MFMAs (fenced,
         // so the compiler cannot hoist every read of the stage and run out of
         // registers; the other wave of the SIMD covers the read latency)

@@ -230,9 +230,16 @@ dit_status_t dit_attn_forward_fp8(const void* q8, const void* k8, const void* v8
  * weights are quantised once, activations per call, and the product is an
  * A4W4 matrix-core GEMM ("MXFP4 Quantization" and "MXFP4 Kernel" sections).
  *
- * Layouts (device memory, row-major):
- *   codes  [rows, K/2] bytes: element k in byte k/2, low nibble for even k.
- *   scales [rows, K/32] bytes: E8M0 (2^(s - 127)) of each 32-element block.
+ * Layouts (device memory):
+ *   codes  [rows, K/2] bytes, row-major: element k in byte k/2, low nibble for
+ *          even k.
+ *   scales E8M0 (2^(s - 127)) of each 32-element block, in tiles of 32 rows x
+ *          8 blocks: block b of row r is byte ((r / 32) * G + b / 8) * 256 +
+ *          (r % 32) * 8 + b % 8, with G = ceil(K / 256); the tiles of one
+ *          256-deep slice of K are contiguous per 32 rows, which is what one
+ *          GEMM step reads.  dit_mxfp4_scale_bytes(rows, K) = ceil(rows / 32)
+ *          * G * 256 bytes (0 on invalid sizes); bytes of rows past `rows` or
+ *          blocks past K/32 are neither written nor used.
  *
  * dit_mxfp4_quantize  x: bf16 [rows, K], 16-byte aligned, K a multiple of 32,
  *   finite values.  Per block: X = floor(log2 max|x|) - 2 clamped to
@@ -251,6 +258,8 @@ dit_status_t dit_attn_forward_fp8(const void* q8, const void* k8, const void* v8
  * dit_mxfp4_linear  quantise x (bf16 [M, K]) into a stream-ordered workspace
  *   (hipMallocAsync / hipFreeAsync on stream), then dit_mxfp4_gemm.
  */
+size_t dit_mxfp4_scale_bytes(int rows, int K);
+
 dit_status_t dit_mxfp4_quantize(const void* x, void* codes, void* scales, int rows, int K, void* stream);
 
 dit_status_t dit_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,

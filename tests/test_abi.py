@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     lib = dj.lib()
     for name in dj.EXPORTED_SYMBOLS:
         assert getattr(lib, name) is not None
-    assert dj.dit_abi_version() == 5
+    assert dj.dit_abi_version() == 6
 
 
 def _expected_workspace(B, H, S):
@@ -241,6 +241,11 @@ def test_lse_entry_points_reject_bad_arguments():
 def test_mxfp4_entry_points_reject_bad_arguments():
     L = dj.lib()
     x, c, s, o = 0x30000000, 0x40000000, 0x50000000, 0x60000000
+    # tiled scales: ceil(rows / 32) x ceil(K / 256) tiles of 256 bytes
+    assert L.dit_mxfp4_scale_bytes(16896, 3072) == 528 * 12 * 256
+    assert L.dit_mxfp4_scale_bytes(33, 288) == 2 * 2 * 256
+    assert L.dit_mxfp4_scale_bytes(1, 32) == 256
+    assert L.dit_mxfp4_scale_bytes(0, 64) == 0 and L.dit_mxfp4_scale_bytes(4, 48) == 0
     q = L.dit_mxfp4_quantize
     assert q(None, c, s, 4, 64, None) == dj.DIT_ERR_INVALID_ARG
     assert q(x, c, s, 0, 64, None) == dj.DIT_ERR_INVALID_ARG

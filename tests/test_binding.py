@@ -112,9 +112,11 @@ def test_mxfp4_and_dbcache_reject_bad_arguments():
         dj.dit_mxfp4_quantize(torch.zeros((4, 48), dtype=BF))
     with pytest.raises(ValueError, match="shape"):
         dj.dit_mxfp4_quantize(x, codes=torch.zeros((4, 31), dtype=torch.uint8))
-    wc, wsc = torch.zeros((8, 32), dtype=torch.uint8), torch.zeros((8, 2), dtype=torch.uint8)
+    wc, wsc = torch.zeros((8, 32), dtype=torch.uint8), torch.zeros(dj.mxfp4_scale_shape(8, 64), dtype=torch.uint8)
     with pytest.raises(ValueError, match="shape"):
         dj.dit_mxfp4_linear(x, wc, torch.zeros((8, 3), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="shape"):   # row-major scales are not the library's layout
+        dj.dit_mxfp4_linear(x, wc, torch.zeros((8, 2), dtype=torch.uint8))
     with pytest.raises(ValueError, match="dtype"):
         dj.dit_mxfp4_linear(x.float(), wc, wsc)
     with pytest.raises(ValueError, match="shape"):
@@ -143,3 +145,19 @@ def test_rope_tables_reject_bad_arguments():
         dj.dit_rope_tables(pos, (16, 56, 56), 1e4, rope_cos=torch.zeros((8, 32)))
     with pytest.raises(ValueError, match="GPU"):
         dj.dit_rope_tables(pos, (16, 56, 56), 1e4)
+
+
+def test_mxfp4_scale_tiles_round_trip():
+    """The tiled scale layout is a permutation: block b of row r sits at byte
+    ((r // 32) * G + b // 8) * 256 + (r % 32) * 8 + b % 8, G = ceil(K / 256)."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    for rows, K in [(1, 32), (33, 288), (64, 256), (70, 3072)]:
+        s = rng.integers(0, 256, size=(rows, K // 32), dtype=np.uint8)
+        t = dj.mxfp4_scales_to_tiles(s)
+        assert t.shape == dj.mxfp4_scale_shape(rows, K)
+        assert t.size == -(-rows // 32) * -(-K // 256) * 256
+        flat, G = t.reshape(-1), -(-K // 256)
+        for r, b in [(0, 0), (rows - 1, K // 32 - 1), (rows // 2, (K // 32) // 2)]:
+            assert flat[((r // 32) * G + b // 8) * 256 + (r % 32) * 8 + b % 8] == s[r, b]
+        assert np.array_equal(dj.mxfp4_scales_from_tiles(t, rows, K), s)

@@ -93,7 +93,7 @@ def test_quantize_bit_exact(case):
     torch.cuda.synchronize()
     want_c, want_s = mxfp4_quantize(bf16_f64(bits))
     got_c = _unpack(codes.cpu().numpy())
-    assert np.array_equal(scales.cpu().numpy(), want_s), case
+    assert np.array_equal(dj.mxfp4_scales_from_tiles(scales.cpu().numpy(), *bits.shape), want_s), case
     bad = np.argwhere(got_c != want_c)
     assert len(bad) == 0, (case, bad[:5], got_c[tuple(bad[0])], want_c[tuple(bad[0])])
 
@@ -109,11 +109,13 @@ def test_gemm_random_codes(M, N, K):
     asc = rng.integers(120, 134, size=(M, K // 32), dtype=np.uint8)
     wsc = rng.integers(120, 134, size=(N, K // 32), dtype=np.uint8)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
-    out = dj.dit_mxfp4_gemm(dev(_pack(ac)), dev(asc), dev(_pack(wc)), dev(wsc))
+    tiles = lambda sc: dev(dj.mxfp4_scales_to_tiles(sc))   # the library's scale layout (a permutation)
+    out = dj.dit_mxfp4_gemm(dev(_pack(ac)), tiles(asc), dev(_pack(wc)), tiles(wsc))
     torch.cuda.synchronize()
     got = from_device_bf16(out)
     _gate(got, mxfp4_dequantize(ac, asc), mxfp4_dequantize(wc, wsc), f"M={M} N={N} K={K}")
-    assert np.array_equal(got, from_device_bf16(dj.dit_mxfp4_gemm(dev(_pack(ac)), dev(asc), dev(_pack(wc)), dev(wsc))))
+    assert np.array_equal(got, from_device_bf16(dj.dit_mxfp4_gemm(dev(_pack(ac)), tiles(asc), dev(_pack(wc)),
+                                                                  tiles(wsc))))
 
 
 @pytest.mark.parametrize("case", ["small_ragged", "flux1024x768_qkv"])
