@@ -44,7 +44,7 @@ MEASURED_TRAFFIC = {
     ("5b720b2b819d28e1", "flux2048_fp8"): {"read_bytes": 711.7e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
-    ("68292c3f8fd19d45", "flux2048_qkv"): {"read_bytes": 435.7e6, "write_bytes": 331.1e6,
+    ("904ecb6377cb4ce4", "flux2048_qkv"): {"read_bytes": 428.2e6, "write_bytes": 311.4e6,
                                            "profile": "profiles/mxfp4_gemm_flux2048_qkv.md"},
     # residual_diff_partials + residual_diff_finish (hash over RESIDUAL_SOURCES)
     ("ab5d6a5aa3060f98", "flux2048_residual"): {"read_bytes": 207.80e6, "write_bytes": 0.26e6,
