@@ -50,13 +50,21 @@ __device__ __forceinline__ i32x8 lds_read32(const uint4* p) {
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+// Registers whose previous content does not matter: the packing below
+// overwrites both halves of every word (no instruction is emitted).
+__device__ __forceinline__ i32x8 unset_i32x8() {
+    i32x8 v;
+    asm("" : "=v"(v));
+    return v;
+}
+
 // exp2 of a lane's 32 scores (two key blocks), packed to e4m3 in the PV B
 // operand order (byte j = key block j/16, register j%16); fp32 sum of p'.
 // No clamp to 448: a weight above it makes the lane's sum exceed
 // F8_SUM_LIMIT, and the tile is then redone with a moved offset (p' <= 16).
 // cvt_pk replaces one half of its destination register and keeps the other,
 // so the packing needs no cleared register: the second call overwrites the
-// half the first one kept.
+// half the first one kept (the caller passes unset registers).
 __device__ __forceinline__ void f8_weights(const f32x16 (&s)[2], i32x8& pf, float& sum) {
     float t0 = 0.0f, t1 = 0.0f;
 #pragma unroll
@@ -105,7 +113,7 @@ __device__ __forceinline__ i32x8 f8_scores_weights(const uint4* kt, int j, bool 
                 if (base + 32 * kb + 16 * (r >> 3) + (r & 7) >= S) s[kb][r] = -INFINITY;
     }
 
-    i32x8 pf = i32x8{};
+    i32x8 pf = unset_i32x8();
     float tsum = 0.0f;
     bool slow = first;
     if (!slow) {
