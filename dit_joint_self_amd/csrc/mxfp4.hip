@@ -113,10 +113,9 @@ constexpr int GN = 256;      // rows of W (output columns) per workgroup
 constexpr int GK = 256;      // K per pipeline step: four 64-deep MFMA steps, 128 bytes of each row
 constexpr int GWAVES = 8;    // wave (wm, wn) = (w & 3, w >> 2): 64 rows x 128 columns each
 constexpr int G_GROUP = 8;   // column tiles per group of the workgroup order
-constexpr int G_CODE_PIECES = (GM + GN) * (GK / 2) / 1024 / GWAVES;   // 1 KiB code pieces per wave and step (8)
-static_assert(G_CODE_PIECES * GWAVES == 64, "pieces are spread evenly");
 // Scales of a step: 8 whole scale tiles (256 rows x 8 bytes) per operand, two
-// 1 KiB pieces each, copied by waves 0..3 (A: waves 0-1, W: waves 2-3).
+// 1 KiB pieces each, copied by waves 0..3 (A: waves 0-1, W: waves 2-3; the W
+// part of a 128-wide tile is one piece, wave 2).
 static_assert(GM == 256 && GN == 256 && GK == 256, "one scale tile column per step and 32-row tile");
 
 // LDS image of a tile: rows of GK/2 = 128 bytes = eight 16-byte chunks; chunk c
@@ -162,34 +161,25 @@ struct GStage {
     uint4 sw[GN / 2];
 };
 
-// Workgroup: 8 waves over a 256 x 256 output tile; accumulators acc[nb][mb]
-// of C^T (wave columns 128 wn + 32 nb, rows 64 wm + 32 mb).
-__global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* __restrict__ a_codes,
-                                                                const uint8_t* __restrict__ a_scales,
-                                                                const uint8_t* __restrict__ w_codes,
-                                                                const uint8_t* __restrict__ w_scales,
-                                                                uint2* __restrict__ out, int M, int N, int K) {
-    // two distinct stage objects, statically indexed (the loop is unrolled by
-    // two), so the compiler never makes an LDS read wait for the copy in flight
-    __shared__ GStage st0, st1;
-
+// One output tile of GM rows x TN columns (TN = 256, or 128 for the tiles
+// of a last partial round), 8 waves; accumulators acc[nb][mb] of C^T (wave
+// columns (TN / 2) wn + 32 nb, rows 64 wm + 32 mb).  Both tile widths use the
+// kernel's two stage objects (a 128-wide tile fills the first half of their
+// W parts).
+template <int TN>
+__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+                                          const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
+                                          uint2* __restrict__ out, int M, int N, int K, int m0, int n0, GStage& st0,
+                                          GStage& st1) {
+    static_assert(TN == 256 || TN == 128, "tile widths");
+    constexpr int NB = TN / 64;                          // 32-column blocks per wave
+    constexpr int WCOLS = TN / 2;                        // columns per wave
+    constexpr int CODE_PIECES = (GM + TN) / 8 / GWAVES;  // 1 KiB code pieces per wave and step (8 or 6)
+    static_assert(CODE_PIECES * GWAVES * 8 == GM + TN, "pieces are spread evenly");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave & 3, wn = wave >> 2;
     const int n_lane = lane & 31, hh = lane >> 5;
-
-    // Tile order: groups of G_GROUP column tiles, row tiles fastest-but-one
-    // inside a group (logical r -> row tile r / gw, column tile r % gw), and
-    // each XCD a contiguous range of the order.  The ~32 workgroups an XCD
-    // runs at once then cover 4 row tiles x 8 column tiles: the group's W
-    // tiles stay in that XCD's L2 while it sweeps down the rows.
-    const int m_tiles = (M + GM - 1) / GM, n_tiles = (N + GN - 1) / GN;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int g = logical / (G_GROUP * m_tiles);
-    const int gw = min(G_GROUP, n_tiles - g * G_GROUP);
-    const int r = logical - g * G_GROUP * m_tiles;
-    const int m0 = (r / gw) * GM;
-    const int n0 = (g * G_GROUP + r % gw) * GN;
     const int rowbytes = K / 2, G = (K + 255) / 256;  // G: scale tiles per row of tiles
     const int nk = (K + GK - 1) / GK;      // the last step is a half step when K % 256 == 128
     const bool half_last = (K % GK) != 0;
@@ -199,13 +189,15 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
     const __amdgpu_buffer_rsrc_t rsa = raw_rsrc(a_scales, (uint32_t)mx_scale_size(M, K));
     const __amdgpu_buffer_rsrc_t rsw = raw_rsrc(w_scales, (uint32_t)mx_scale_size(N, K));
 
-    // code pieces of this wave: pieces wave + 8 j of the 64 per step (A: 0..31, W: 32..63);
-    // their per-lane offsets are recomputed at each step (a few integer ops) to spare registers
-    // scale piece of waves 0..3: piece q = wave & 1 of A (waves 0, 1) or W
-    // (waves 2, 3) covers the operand's row tiles 4 q .. 4 q + 3; lane l brings
-    // 16-byte chunk l % 16 of tile 4 q + l / 16 (row tiles past the matrix
-    // repeat its last one, never stored).  The step adds kk * 256 bytes.
-    const bool scale_copier = wave < 4, scale_of_a = wave < 2;
+    // code pieces of this wave: pieces wave + 8 j of the step's (GM + TN) / 8
+    // (A: 0..31, then W); their per-lane offsets are recomputed at each step
+    // (a few integer ops) to spare registers.
+    // Scale pieces (four 32-row scale tiles, 1 KiB): waves 0 and 1 copy piece
+    // q = wave & 1 of A, waves 2 .. 2 + TN / 128 - 1 piece q of W; piece q
+    // covers the operand's row tiles 4 q .. 4 q + 3 and lane l brings 16-byte
+    // chunk l % 16 of tile 4 q + l / 16 (row tiles past the matrix repeat its
+    // last one, never stored).  The step adds kk * 256 bytes.
+    const bool scale_copier = wave < 2 + TN / 128, scale_of_a = wave < 2;
     int soff = 0;
     {
         const int q = wave & 1, t = 4 * q + (lane >> 4);
@@ -223,7 +215,7 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
                     rsw, (__attribute__((address_space(3))) void*)(d.sw + 64 * (wave & 1)), 16, soff, kk * 256, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < G_CODE_PIECES; ++j) {
+        for (int j = 0; j < CODE_PIECES; ++j) {
             const int p = wave + GWAVES * j;
             if (p < GM / 8)  // wave-uniform
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(d.a + p * 64),
@@ -236,9 +228,9 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
         }
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[NB][2];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x16{};
 
@@ -254,7 +246,7 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
         // row r's 8 bytes are half (r & 1) of 16-byte chunk r / 2; every row of
         // this lane has the parity of n_lane
         const bool odd = n_lane & 1;
-        uint32_t sa_w[2][2], sw_w[4][2];
+        uint32_t sa_w[2][2], sw_w[NB][2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             const uint4 v = t.sa[(64 * wm + 32 * mb + n_lane) >> 1];
@@ -262,41 +254,42 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
             sa_w[mb][1] = odd ? v.w : v.y;
         }
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const uint4 v = t.sw[(128 * wn + 32 * nb + n_lane) >> 1];
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint4 v = t.sw[(WCOLS * wn + 32 * nb + n_lane) >> 1];
             sw_w[nb][0] = odd ? v.z : v.x;
             sw_w[nb][1] = odd ? v.w : v.y;
         }
         // operand fragments of MFMA step s, read just before its MFMAs (fenced,
         // so the compiler cannot hoist every read of the stage and run out of
-        // registers; the other wave of the SIMD covers the read latency)
-        uint4 fa[2][2], fw[2][4];
-        auto read_frags = [&](int s, uint4 (&a)[2], uint4 (&w)[4]) {
+        // registers; the other wave of the SIMD covers the read latency.  Reading
+        // the next step's fragments ahead of the MFMAs measured slower.)
+        uint4 fa[2][2], fw[2][NB];
+        auto read_frags = [&](int s, uint4 (&a)[2], uint4 (&w)[NB]) {
             const int c = 2 * s + hh;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) a[mb] = t.a[swz(64 * wm + 32 * mb + n_lane, c)];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) w[nb] = t.w[swz(128 * wn + 32 * nb + n_lane, c)];
+            for (int nb = 0; nb < NB; ++nb) w[nb] = t.w[swz(WCOLS * wn + 32 * nb + n_lane, c)];
         };
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
             read_frags(s, fa[s & 1], fw[s & 1]);
             __builtin_amdgcn_sched_barrier(0);
             // MFMA step s covers blocks 2 s and 2 s + 1: word s >> 1, bytes 2 (s & 1) + hh
-            int sca[2], scw[4];
+            int sca[2], scw[NB];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) sca[mb] = (int)(sa_w[mb][s >> 1] >> (8 * hh));
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) scw[nb] = (int)(sw_w[nb][s >> 1] >> (8 * hh));
+            for (int nb = 0; nb < NB; ++nb) scw[nb] = (int)(sw_w[nb][s >> 1] >> (8 * hh));
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
                     acc[nb][mb] = mfma_fp4(fw[s & 1][nb], fa[s & 1][mb], acc[nb][mb], scw[nb], sca[mb], 2 * (s & 1));
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) settle(acc[nb][mb]);
         __builtin_amdgcn_sched_barrier(0);
@@ -335,47 +328,99 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
             step(i, st0, st1, half_step);
     }
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) settle(acc[nb][mb]);
 
     // acc[nb][mb]: lane (n_lane, hh), register r holds C[m][n .. n+3] with
-    // m = m0 + 64 wm + 32 mb + n_lane, n = n0 + 128 wn + 32 nb + 8 (r >> 2) + 4 hh + (r & 3).
-    // The wave's 64 x 128 block leaves through LDS (16 KiB per wave in the
-    // stages, free once every wave is past its last step), so each 8-byte
-    // store instruction covers two whole 256-byte row segments instead of
-    // 32 rows: row rho keeps 8-byte piece p (columns 4p..4p+3) in slot p ^ (rho % 32),
-    // which spreads both the writes (32 rows per lane group) and the reads
-    // (32 pieces of one row) over all LDS banks.
+    // m = m0 + 64 wm + 32 mb + n_lane, n = n0 + WCOLS wn + 32 nb + 8 (r >> 2) + 4 hh + (r & 3).
+    // The wave's 64 x WCOLS block (rows of TN bytes = PPR 8-byte pieces) leaves
+    // through LDS (64 TN bytes per wave in the stages, free once every wave is
+    // past its last step), so each 8-byte store instruction covers whole row
+    // segments instead of 32 rows: row rho keeps piece p (columns 4p..4p+3) in
+    // slot p ^ (rho % PPR), which spreads both the writes (32 rows per lane
+    // group) and the reads (the pieces of a row) over the LDS banks.
+    constexpr int PPR = TN / 8;         // 8-byte pieces per row
+    constexpr int RPI = 64 / PPR;       // rows per store instruction
     __syncthreads();
-    char* const blk = reinterpret_cast<char*>(wave < 4 ? &st0 : &st1) + (wave & 3) * 16384;
+    char* const blk = reinterpret_cast<char*>(wave < 4 ? &st0 : &st1) + (wave & 3) * (64 * TN);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int rho = 32 * mb + n_lane, piece = 8 * nb + 2 * gq + hh;
                 const f32x16& c = acc[nb][mb];
-                *reinterpret_cast<uint2*>(blk + rho * 256 + ((piece ^ (rho & 31)) << 3)) =
+                *reinterpret_cast<uint2*>(blk + rho * TN + ((piece ^ (rho & (PPR - 1))) << 3)) =
                     make_uint2(pack_bf16x2(c[4 * gq], c[4 * gq + 1]), pack_bf16x2(c[4 * gq + 2], c[4 * gq + 3]));
             }
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int rho = 2 * i + (lane >> 5), piece = lane & 31;
-        const int m = m0 + 64 * wm + rho, n = n0 + 128 * wn + 4 * piece;
-        const uint2 v = *reinterpret_cast<const uint2*>(blk + rho * 256 + ((piece ^ (rho & 31)) << 3));
+    for (int i = 0; i < PPR; ++i) {
+        const int rho = RPI * i + lane / PPR, piece = lane & (PPR - 1);
+        const int m = m0 + 64 * wm + rho, n = n0 + WCOLS * wn + 4 * piece;
+        const uint2 v = *reinterpret_cast<const uint2*>(blk + rho * TN + ((piece ^ (rho & (PPR - 1))) << 3));
         if (m < M && n < N) out[(int64_t)m * (N / 4) + n / 4] = v;
+    }
+}
+
+// The launch: tiles of 256 x 256 in full rounds of the 256 CUs, and when the
+// last round would be at most half full (rem <= 128 tiles) its tiles run as
+// 2 rem tiles of 256 x 128 instead, which end in about half the time: the
+// first nbig workgroups take whole tiles, the rest half tiles.
+struct GemmPlan {
+    int tiles, nbig, halves;
+};
+inline GemmPlan gemm_plan(int M, int N) {
+    GemmPlan g;
+    g.tiles = ((M + GM - 1) / GM) * ((N + GN - 1) / GN);
+    const int rem = g.tiles % MI355X_CUS;
+    const bool split = rem > 0 && rem <= MI355X_CUS / 2;
+    g.nbig = split ? g.tiles - rem : g.tiles;
+    g.halves = split ? 2 * rem : 0;
+    return g;
+}
+
+// Tile order: groups of G_GROUP column tiles, row tiles fastest-but-one
+// inside a group (logical r -> row tile r / gw, column tile r % gw), and
+// each XCD a contiguous range of the order.  The ~32 workgroups an XCD runs
+// at once then cover 4 row tiles x 8 column tiles: the group's W tiles stay
+// in that XCD's L2 while it sweeps down the rows.  Logical tiles from nbig
+// on are the half-tile ones (two workgroups each).
+__global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* __restrict__ a_codes,
+                                                                const uint8_t* __restrict__ a_scales,
+                                                                const uint8_t* __restrict__ w_codes,
+                                                                const uint8_t* __restrict__ w_scales,
+                                                                uint2* __restrict__ out, int M, int N, int K,
+                                                                int nbig) {
+    // two distinct stage objects, statically indexed (the loop is unrolled by
+    // two), so the compiler never makes an LDS read wait for the copy in flight
+    __shared__ GStage st0, st1;
+    const int m_tiles = (M + GM - 1) / GM, n_tiles = (N + GN - 1) / GN;
+    const bool big = (int)blockIdx.x < nbig;
+    const int h = (int)blockIdx.x - nbig;
+    const int logical = big ? xcd_remap(blockIdx.x, nbig) : nbig + (h >> 1);
+    const int g = logical / (G_GROUP * m_tiles);
+    const int gw = min(G_GROUP, n_tiles - g * G_GROUP);
+    const int r = logical - g * G_GROUP * m_tiles;
+    const int m0 = (r / gw) * GM;
+    const int n0 = (g * G_GROUP + r % gw) * GN;
+    if (big) {
+        gemm_tile<256>(a_codes, a_scales, w_codes, w_scales, out, M, N, K, m0, n0, st0, st1);
+    } else {
+        const int n0h = n0 + 128 * (h & 1);
+        if (n0h >= N) return;  // the whole workgroup: a half past the matrix
+        gemm_tile<128>(a_codes, a_scales, w_codes, w_scales, out, M, N, K, m0, n0h, st0, st1);
     }
 }
 
 hipError_t launch_mxfp4_gemm(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
                              void* out, int M, int N, int K, hipStream_t stream) {
-    const int64_t grid = (int64_t)((M + GM - 1) / GM) * ((N + GN - 1) / GN);
-    mxfp4_gemm_kernel<<<(int)grid, GWAVES * 64, 0, stream>>>(
+    const GemmPlan g = gemm_plan(M, N);
+    mxfp4_gemm_kernel<<<g.nbig + g.halves, GWAVES * 64, 0, stream>>>(
         static_cast<const uint8_t*>(a_codes), static_cast<const uint8_t*>(a_scales),
         static_cast<const uint8_t*>(w_codes), static_cast<const uint8_t*>(w_scales), static_cast<uint2*>(out), M,
-        N, K);
+        N, K, g.nbig);
     return hipGetLastError();
 }
 
