@@ -25,14 +25,14 @@ run bench_line 600 python -u bench.py --gpus 1 --steps 20 --warmup 5
 run trace_flux2048 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/trace_flux2048 -o run -- $B --workload flux2048 --steps 20 --warmup 5
 pmc fetch_flux2048 FETCH_SIZE -- $B --workload flux2048 $P
 pmc write_flux2048 WRITE_SIZE -- $B --workload flux2048 $P
-pmc sq_flux2048 "SQ_BUSY_CYCLES SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE" -- $B --workload flux2048 $P
+pmc sq_flux2048 "SQ_BUSY_CYCLES SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE" -- $B --workload flux2048 $P
 pmc fetch_copy FETCH_SIZE -- python -u bench.py --copy-mib 1024 --steps 2 --warmup 1
 pmc write_copy WRITE_SIZE -- python -u bench.py --copy-mib 1024 --steps 2 --warmup 1
 run bench_fp8 300 $B --workload flux2048_fp8 --steps 20 --warmup 5
 run trace_fp8 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/trace_fp8 -o run -- $B --workload flux2048_fp8 --steps 20 --warmup 5
 pmc fetch_fp8 FETCH_SIZE -- $B --workload flux2048_fp8 $P
 pmc write_fp8 WRITE_SIZE -- $B --workload flux2048_fp8 $P
-pmc sq_fp8 "SQ_BUSY_CYCLES SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE" -- $B --workload flux2048_fp8 $P
+pmc sq_fp8 "SQ_BUSY_CYCLES SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE" -- $B --workload flux2048_fp8 $P
 run bench_ring2 300 python -u bench.py --workload flux2048 --ring 2 --steps 20 --warmup 5
 run trace_ring2 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/trace_ring2 -o run -- python -u bench.py --workload flux2048 --ring 2 --steps 20 --warmup 5
 run bench_qkv 300 python -u bench.py --workload flux2048_qkv --steps 20 --warmup 5 --cpu-seconds 10
