@@ -181,29 +181,31 @@ __global__ __launch_bounds__(256) void prepare_kv_fp8_kernel(
 
     __syncthreads();
 
-    // V^T part: chunk (d, c) holds bytes 16c..16c+15 of row d, i.e. keys
-    // f8_vkey(hh, j) for byte 32 hh + j; c = 4 is padding.  Lanes run over d.
+    // V^T part, stored in order: chunk x = (row d = x / 5, c = x % 5) holds
+    // bytes 16c..16c+15 of row d, i.e. keys f8_vkey(hh, j) for byte 32 hh + j;
+    // c = 4 is padding.  Consecutive threads build and store consecutive
+    // chunks, so every store instruction writes whole lines (with lanes over d
+    // instead, 80 bytes apart, each store touched about 40 lines).
     const uint8_t* vt8 = reinterpret_cast<const uint8_t*>(vtile);
     uint4* vdst = dst + F8_K_PART_CHUNKS;
+    for (int x = tid; x < F8_V_PART_CHUNKS; x += 256) {
+        const int d = x / F8_V_ROW_CHUNKS;
+        const int c = x - d * F8_V_ROW_CHUNKS;
+        uint32_t w[4] = {0, 0, 0, 0};
+        if (c < 4) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int y = tid + i * 256;
-        const int d = y & 127;
-        const int c = y >> 7;
-        uint32_t w[4];
+            for (int e = 0; e < 4; ++e) {
+                uint32_t acc = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int p = 16 * c + 4 * e + b;
-                acc |= (uint32_t)vt8[f8_vkey(p >> 5, p & 31) * 128 + d] << (8 * b);
+                for (int b = 0; b < 4; ++b) {
+                    const int p = 16 * c + 4 * e + b;
+                    acc |= (uint32_t)vt8[f8_vkey(p >> 5, p & 31) * 128 + d] << (8 * b);
+                }
+                w[e] = acc;
             }
-            w[e] = acc;
         }
-        vdst[d * F8_V_ROW_CHUNKS + c] = make_uint4(w[0], w[1], w[2], w[3]);
+        vdst[x] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    if (tid < HEAD_DIM) vdst[tid * F8_V_ROW_CHUNKS + 4] = make_uint4(0, 0, 0, 0);
 }
 
 hipError_t launch_prepare_kv_fp8(const void* k, const void* v, const float* cos_t, const float* sin_t, void* ws,
