@@ -227,13 +227,18 @@ hipError_t launch_prepare_k(const void* k, const float* cos_t, const float* sin_
     const float4* ss = reinterpret_cast<const float4*>(sin_t);
     uint4* w = static_cast<uint4*>(ws);
     const int rope = cos_t != nullptr;
-    // While the two tables (S x 64 x 8 bytes) stay cache resident across the
-    // heads, one head per workgroup is fastest (16896 tokens: 32 us against 35
-    // with two heads); beyond that the per-head table re-reads go to HBM and
-    // four heads per workgroup pay (76112 tokens, 39 MB of tables: 110 -> 80 us).
+    // Heads per workgroup (the tile's table rows are loaded once for all of
+    // them), timed inside the step, after an attention call has displaced the
+    // caches: with tables (S x 64 x 8 bytes) of up to 16 MB two heads are
+    // fastest (16896 tokens: 44.9 us with one, 40.6 with two, 43.5 with four;
+    // 3584 tokens: the same 12 us for all three), beyond that four (76112
+    // tokens, 39 MB of tables: 79.9 us with one, 89.3 with two, 78.9 with four).
     if (rope && (int64_t)S * HEAD_DIM * 4 > ((int64_t)16 << 20) && BH > 1) {
         dim3 grid(ntiles, (BH + 3) / 4);
         prepare_k_kernel<4><<<grid, 256, 0, stream>>>(kk, cc, ss, w, ctl, S, ntiles, BH, rope);
+    } else if (rope && BH > 1) {
+        dim3 grid(ntiles, (BH + 1) / 2);
+        prepare_k_kernel<2><<<grid, 256, 0, stream>>>(kk, cc, ss, w, ctl, S, ntiles, BH, rope);
     } else {
         dim3 grid(ntiles, BH);
         prepare_k_kernel<1><<<grid, 256, 0, stream>>>(kk, cc, ss, w, ctl, S, ntiles, BH, rope);

@@ -216,18 +216,20 @@ def test_whole_ranges_and_key_range_pieces_in_one_launch(B, H, split_ranges):
         _assert_close(got, want, f"S={w.S} H={w.H} split={split}")
 
 
-def test_rotated_keys_round_like_plain_fp32():
+@pytest.mark.parametrize("H", [2, 3])
+def test_rotated_keys_round_like_plain_fp32(H):
     """The tile preparation rotates K in plain fp32 arithmetic (each product
     rounded, then the sum; no fused multiply-add) and rounds to bf16 to nearest
     even.  With fp32 tables made on the host, the prepared K' rows equal that
     evaluation bit for bit.  The tile image is private to the library; the test
-    reads it as documented in tile_layout.h: per (batch, head), 35840-byte
-    tiles of 64 keys whose first 17408 bytes are 64 rows of 272 bytes, row rho
-    holding key (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1) of the tile,
-    dims 0..127 first."""
+    reads it as documented in tile_layout.h: per (batch, head), 17408-byte
+    tiles of 64 keys, 64 rows of 272 bytes, row rho holding key
+    (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1) of the tile, dims 0..127
+    first.  Two heads share a workgroup of the preparation at this size, so
+    H = 3 also covers a group with one head."""
     torch = _torch()
     dj = _dj()
-    w = _small(0, (10, 30), B=1, H=2, seed=300)          # S = 300: a ragged last tile
+    w = _small(0, (10, 30), B=1, H=H, seed=300)          # S = 300: a ragged last tile
     qb, kb, vb = W.make_bf16_inputs(w)
     ang = rope_angles(W.positions(w), w.axes_dim, w.theta)
     cos32, sin32 = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
