@@ -23,8 +23,9 @@
 // largest E2M1 exponent), clamped to [-127, 127] (an all-zero block takes
 // -127); P_i = V_i * 2^-X rounded to the nearest E2M1 value, ties to the even
 // code, magnitudes above 6 saturated to 6, sign bit kept.  Every step is
-// exact in fp32 (bf16 inputs, power-of-two scaling, comparisons against the
-// midpoints), so the codes do not depend on evaluation order.
+// exact (bf16 inputs, power-of-two scaling, then the hardware conversion's
+// rounding, which follows that rule), so the codes do not depend on
+// evaluation order.
 //
 // GEMM: C[M, N] (bf16) = deq(A)[M, K] deq(W)[N, K]^T on
 // v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands.  In that instruction
@@ -77,16 +78,19 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint4* __rest
         a = fmaxf(a, __shfl_xor(a, 2, 4));
         // floor(log2 a) from the exponent field; zero and subnormal maxima clamp to -127
         const int X = max((int)((__float_as_uint(a) >> 23) & 0xff) - 127 - 2, -127);
+        // v_cvt_scalef32_pk_fp4_f32 rounds two values divided by the scale to
+        // E2M1 exactly as the MX rule does (nearest, ties to the even code,
+        // magnitudes above 6 to 6, the sign kept, -0 included), for every
+        // power-of-two scale 2^-127 .. 2^127 (checked against the rule on the
+        // GPU value by value, at every rounding midpoint and either side of
+        // it); the first value goes to the low nibble of the selected byte.
+        // The scale's bits are built directly: 2^-127 is an fp32 subnormal.
+        const float scale = __uint_as_float(X >= -126 ? (uint32_t)(X + 127) << 23 : 0x00400000u);
         uint32_t packed = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float y = fabsf(ldexpf(v[i], -X));
-            // number of rounding midpoints passed; a tie goes to the even code
-            uint32_t c = (y > 0.25f) + (y >= 0.75f) + (y > 1.25f) + (y >= 1.75f) + (y > 2.5f) + (y >= 3.5f) +
-                         (y > 5.0f);
-            c |= (__float_as_uint(v[i]) >> 28) & 8u;   // sign bit
-            packed |= c << (4 * i);
-        }
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[0], v[1], scale, 0);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[2], v[3], scale, 1);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[4], v[5], scale, 2);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[6], v[7], scale, 3);
         codes[t] = packed;
         if ((t & 3) == 0) {
             const int64_t blk = t >> 2, per_row = K / 32;
