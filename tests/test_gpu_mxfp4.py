@@ -70,6 +70,8 @@ def _quantize_edge_rows():
     rows.append(np.zeros(32, np.float32))                                  # zero block
     rows.append(np.array([-0.0] * 32, np.float32))                         # all -0
     rows.append(np.array([2.0 ** -130] + [2.0 ** -133] * 31, np.float32))  # subnormal maxima: X clamps to -127
+    rows.append(np.array(mids * 2, np.float32) * np.float32(2.0 ** -127))  # max 2^-125: X = -127 with every
+    #                                                                        midpoint (bf16 subnormals, exact)
     rows.append(np.array([3.0e38, -1.0e38] + [1.0] * 30, np.float32))      # largest exponents
     rows.append(np.array([1.5 * 2.0 ** 20, 2.0 ** 18] + [2.0 ** 15] * 30, np.float32))
     x = np.concatenate(rows)
