@@ -102,6 +102,8 @@ def parse():
     ap.add_argument("--prewarm-s", type=float, default=0.5,
                     help="seconds of untimed back-to-back steps before the warmup steps (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-library-baseline", action="store_true",
+                    help="skip timing the library's own kernel on the same shape (PyTorch SDPA / _scaled_mm)")
     ap.add_argument("--single-config", action="store_true",
                     help="time only --workload (by default an attention run also times every other attention "
                          "workload and reports them under `configs`)")
@@ -369,6 +371,8 @@ def gemm_bench(args, lw, torch, dj):
         "stages_ms": {"mxfp4_quantize": q_avg, "mxfp4_gemm": g_avg,
                       "quantize_GBps": quant_bytes / (q_avg * 1e-3) / 1e9},
     }
+    if not args.no_library_baseline:
+        rec["library_baseline"] = library_gemm(lw, torch, K, ac, wc, g_avg)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         from oracle.mx import mx_linear, mxfp4_quantize
@@ -549,6 +553,8 @@ def main():
     out_host = run.out.cpu()
     f64_head = run.f64_head
     run.release()
+    if not args.no_library_baseline:
+        rec["library_baseline"] = library_attention(w, torch, args.steps, core_avg)
     if not args.single_config:
         rec["configs"] = other_configs(w, args, torch, dj)
     if not args.no_cpu_baseline:
@@ -664,6 +670,69 @@ class AttentionRun:
         self.out = None
         self.torch.cuda.synchronize()
         self.torch.cuda.empty_cache()
+
+
+def _event_ms(torch, fn, K, prewarm_s=0.3):
+    """Mean ms of fn over K back-to-back calls between HIP events (after a
+    short clock warm-up)."""
+    fn()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + prewarm_s
+    while time.perf_counter() < t_end:
+        fn()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def library_attention(w, torch, K, core_ms):
+    """PyTorch's own fused attention on the same shape, for comparison:
+    scaled_dot_product_attention restricted to its FLASH_ATTENTION backend
+    (AOTriton on ROCm), bf16 Q, K, V of [B, H, S, D] drawn at random, no RoPE
+    (the library has none), non-causal, scale 1/sqrt(D).  Timing only; bf16
+    workloads up to 20000 tokens (the library call takes seconds beyond)."""
+    if w.dtype != "bf16" or w.S > 20000:
+        return None
+    try:
+        import torch.nn.functional as F
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        g = torch.Generator(device="cuda").manual_seed(0)
+        q, k, v = (torch.randn((w.B, w.H, w.S, w.D), device="cuda", dtype=torch.bfloat16, generator=g)
+                   for _ in range(3))
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ms = _event_ms(torch, lambda: F.scaled_dot_product_attention(q, k, v, scale=1.0 / math.sqrt(w.D)), K)
+        del q, k, v
+    except Exception as ex:  # a library without this backend: report, do not fail the bench
+        return {"error": f"{type(ex).__name__}: {str(ex)[:200]}"}
+    tf = w.flops / (ms * 1e-3) / 1e12
+    return {"what": "torch.nn.functional.scaled_dot_product_attention, FLASH_ATTENTION backend, same B/H/S/D in "
+                    "bf16, no RoPE, timing only",
+            "torch": torch.__version__, "ms": ms, "TFLOPs": tf, "frac": tf / BF16_PEAK_TFLOPS,
+            "attn_core_speedup": ms / core_ms}
+
+
+def library_gemm(lw, torch, K, ac, wc, gemm_ms):
+    """The library's MXFP4 GEMM on the same shape, for comparison: torch._scaled_mm
+    on the same E2M1 codes viewed as float4_e2m1fn_x2 with E8M0 scales of
+    [rows, K/32] (hipBLASLt on ROCm), bf16 output.  Timing only (the scales are
+    all 2^0: their layout is the library's, not this one's)."""
+    try:
+        a4 = ac.view(torch.float4_e2m1fn_x2)
+        w4 = wc.view(torch.float4_e2m1fn_x2)
+        sa = torch.full((lw.M, lw.K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+        sw = torch.full((lw.N, lw.K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+        ms = _event_ms(torch, lambda: torch._scaled_mm(a4, w4.t(), sa, sw, out_dtype=torch.bfloat16), K)
+    except Exception as ex:
+        return {"error": f"{type(ex).__name__}: {str(ex)[:200]}"}
+    tf = lw.flops / (ms * 1e-3) / 1e12
+    return {"what": "torch._scaled_mm on MXFP4 operands (float4_e2m1fn_x2 codes, e8m0 scales per 1x32), same "
+                    "M/N/K, bf16 out, timing only", "torch": torch.__version__, "ms": ms, "TFLOPs": tf,
+            "frac": tf / FP4_PEAK_TFLOPS, "gemm_speedup": ms / gemm_ms}
 
 
 def other_configs(headline, args, torch, dj):

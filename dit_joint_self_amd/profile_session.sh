@@ -19,7 +19,7 @@ pmc() {  # pmc <name> <counters> -- <cmd...>
     timeout -s KILL 180 rocprofv3 --pmc $ctr --output-format csv -d "$O/$name" -o run -- "$@" > "$O/$name.log" 2>&1 \
         || { echo "FAILED: pmc $name"; tail -20 "$O/$name.log"; exit 1; }
 }
-B="python -u bench.py --no-cpu-baseline --single-config"
+B="python -u bench.py --no-cpu-baseline --no-library-baseline --single-config"
 P="--steps 2 --warmup 1 --prewarm-s 0"
 run bench_line 600 python -u bench.py --gpus 1 --steps 20 --warmup 5
 run trace_flux2048 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/trace_flux2048 -o run -- $B --workload flux2048 --steps 20 --warmup 5
