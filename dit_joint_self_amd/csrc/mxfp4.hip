@@ -369,8 +369,11 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes, c
 
 // The launch: tiles of 256 x 256 in full rounds of the 256 CUs, and when the
 // last round would be at most half full (rem <= 128 tiles) its tiles run as
-// 2 rem tiles of 256 x 128 instead, which end in about half the time: the
-// first nbig workgroups take whole tiles, the rest half tiles.
+// 2 rem tiles of 256 x 128 instead, which end in about half the time.  The
+// half tiles are dispatched first: the CUs that take one then run half a tile
+// out of phase with the others for the rest of the launch, so the tiles'
+// output stores and first copies come in two waves instead of one burst per
+// round (267 -> 261 us at 16896 x 9216 x 3072).
 struct GemmPlan {
     int tiles, nbig, halves;
 };
@@ -389,7 +392,8 @@ inline GemmPlan gemm_plan(int M, int N) {
 // each XCD a contiguous range of the order.  The ~32 workgroups an XCD runs
 // at once then cover 4 row tiles x 8 column tiles: the group's W tiles stay
 // in that XCD's L2 while it sweeps down the rows.  Logical tiles from nbig
-// on are the half-tile ones (two workgroups each).
+// on are the half-tile ones (two workgroups each, the first gridDim - nbig
+// workgroups of the launch).
 __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* __restrict__ a_codes,
                                                                 const uint8_t* __restrict__ a_scales,
                                                                 const uint8_t* __restrict__ w_codes,
@@ -400,9 +404,10 @@ __global__ __launch_bounds__(GWAVES * 64) void mxfp4_gemm_kernel(const uint8_t* 
     // two), so the compiler never makes an LDS read wait for the copy in flight
     __shared__ GStage st0, st1;
     const int m_tiles = (M + GM - 1) / GM, n_tiles = (N + GN - 1) / GN;
-    const bool big = (int)blockIdx.x < nbig;
-    const int h = (int)blockIdx.x - nbig;
-    const int logical = big ? xcd_remap(blockIdx.x, nbig) : nbig + (h >> 1);
+    const int halves = (int)gridDim.x - nbig;
+    const bool big = (int)blockIdx.x >= halves;
+    const int h = (int)blockIdx.x;
+    const int logical = big ? xcd_remap((int)blockIdx.x - halves, nbig) : nbig + (h >> 1);
     const int g = logical / (G_GROUP * m_tiles);
     const int gw = min(G_GROUP, n_tiles - g * G_GROUP);
     const int r = logical - g * G_GROUP * m_tiles;
