@@ -44,7 +44,7 @@ MEASURED_TRAFFIC = {
     ("6ee80bfcaa00a0bb", "flux2048_fp8"): {"read_bytes": 706.5e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
-    ("a16c007fb165d4ea", "flux2048_qkv"): {"read_bytes": 430.5e6, "write_bytes": 311.4e6,
+    ("302d7d079501f519", "flux2048_qkv"): {"read_bytes": 580.8e6, "write_bytes": 311.4e6,
                                            "profile": "profiles/mxfp4_gemm_flux2048_qkv.md"},
     # residual_diff_partials + residual_diff_finish (hash over RESIDUAL_SOURCES)
     ("ab5d6a5aa3060f98", "flux2048_residual"): {"read_bytes": 207.80e6, "write_bytes": 0.26e6,
