@@ -101,12 +101,14 @@ def test_quantize_bit_exact(case):
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 256, 128), (1, 4, 128), (200, 100, 384), (1000, 1028, 1024),
-                                   (257, 260, 640), (2048, 9116, 384)])
+                                   (257, 260, 640), (2048, 9116, 384), (2304, 7424, 256)])
 def test_gemm_random_codes(M, N, K):
     """Random codes (all 16 nibbles) and scales in 2^-7 .. 2^6: exact products.
     Up to 128 tiles run as 256 x 128 half tiles only (some wholly past N);
     2048 x 9116 has 288 tiles: 256 whole ones, then the last 32 as 64 half
-    tiles, with a ragged last column tile and a half K step."""
+    tiles (dispatched first), with a ragged last column tile and a half K
+    step; 2304 x 7424 has 261 tiles: 256 whole ones and 5 tiles as 10 half
+    tiles, a count that does not fill the XCDs evenly."""
     torch = _torch()
     dj = _dj()
     rng = np.random.default_rng(M * 7 + N * 3 + K)
