@@ -32,7 +32,9 @@ METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=16896,H=24,D=128 (1 GPU
 BF16_SOURCES = ["dit_joint_self_amd/csrc/attn_core.hip", "dit_joint_self_amd/csrc/attn_common.h",
                 "dit_joint_self_amd/csrc/gfx950.h", "dit_joint_self_amd/csrc/tile_layout.h",
                 "dit_joint_self_amd/csrc/bf16_util.h"]
-FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/csrc/attn_common.h",
+# (the fp8 call's merge kernel lives in attn_core.hip)
+FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/csrc/attn_core.hip",
+               "dit_joint_self_amd/csrc/attn_common.h",
                "dit_joint_self_amd/csrc/gfx950.h", "dit_joint_self_amd/csrc/tile_layout.h",
                "dit_joint_self_amd/csrc/bf16_util.h", "dit_joint_self_amd/csrc/fp8_util.h"]
 KERNEL_SOURCES = BF16_SOURCES

@@ -562,7 +562,9 @@ __global__ __launch_bounds__(NW * 64) void attn_core_kernel(
 
 // Combine the nsplit key-range partials of each split item (the same streaming
 // softmax merge, exact): M = max m_f, O = sum 2^(m_f - M) O_f / sum 2^(m_f - M) l_f.
-// One workgroup per 16 rows of an item; 16 threads per row, 8 dims each.
+// One workgroup per 16 rows of an item; 16 threads per row, 8 dims each.  A
+// thread issues the loads of all nsplit (at most 8) partials before any
+// arithmetic (1024x768: 150.5 -> 149.3 us for the call, bit-identical).
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part, uint4* __restrict__ out,
                                                          float* __restrict__ lse, int S, int nqt, int item0,
                                                          int nsplit) {
@@ -574,18 +576,34 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     const int row = (item - (int)bh * nqt) * BM + rloc;
     if (row >= S) return;
     const float* p0 = part + (int64_t)item_local * nsplit * PART_FLOATS;
+    float mv[8], lv[8];
+    float4 va[8], vb[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        if (f < nsplit) {
+            const float* pf = p0 + (int64_t)f * PART_FLOATS;
+            mv[f] = pf[BM * HEAD_DIM + rloc];
+            lv[f] = pf[BM * HEAD_DIM + BM + rloc];
+            const float4* src = reinterpret_cast<const float4*>(pf + (int64_t)rloc * HEAD_DIM + seg * 8);
+            va[f] = src[0];
+            vb[f] = src[1];
+        }
+    }
     float M = -INFINITY;
-    for (int f = 0; f < nsplit; ++f) M = fmaxf(M, p0[(int64_t)f * PART_FLOATS + BM * HEAD_DIM + rloc]);
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+        if (f < nsplit) M = fmaxf(M, mv[f]);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float L = 0.0f;
-    for (int f = 0; f < nsplit; ++f) {
-        const float* pf = p0 + (int64_t)f * PART_FLOATS;
-        const float w = __builtin_amdgcn_exp2f(pf[BM * HEAD_DIM + rloc] - M);
-        L += w * pf[BM * HEAD_DIM + BM + rloc];
-        const float4* src = reinterpret_cast<const float4*>(pf + (int64_t)rloc * HEAD_DIM + seg * 8);
-        const float4 a = src[0], b = src[1];
-        acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
-        acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        if (f < nsplit) {
+            const float w = __builtin_amdgcn_exp2f(mv[f] - M);
+            L += w * lv[f];
+            const float4 a = va[f], b = vb[f];
+            acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+            acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+        }
     }
     const float inv = 1.0f / L;
 #pragma unroll
