@@ -66,15 +66,15 @@ __device__ __forceinline__ i32x8 unset_i32x8() {
 // so the packing needs no cleared register: the second call overwrites the
 // half the first one kept (the caller passes unset registers).
 __device__ __forceinline__ void f8_weights(const f32x16 (&s)[2], i32x8& pf, float& sum) {
-    float t0 = 0.0f, t1 = 0.0f;
+    float t0, t1;  // started by the first pair: 0 + x would cost an add (it is not folded, for -0)
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         const f32x16& sc = s[w >> 2];
         const int r = (w & 3) * 4;
         const float a = __builtin_amdgcn_exp2f(sc[r]), b = __builtin_amdgcn_exp2f(sc[r + 1]);
         const float c = __builtin_amdgcn_exp2f(sc[r + 2]), d = __builtin_amdgcn_exp2f(sc[r + 3]);
-        t0 += a + b;
-        t1 += c + d;
+        t0 = w == 0 ? a + b : t0 + (a + b);
+        t1 = w == 0 ? c + d : t1 + (c + d);
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, pf[w], false);
         pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
     }
