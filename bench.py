@@ -40,13 +40,13 @@ FP8_SOURCES = ["dit_joint_self_amd/csrc/attn_core_fp8.hip", "dit_joint_self_amd/
 KERNEL_SOURCES = BF16_SOURCES
 MEASURED_TRAFFIC = {
     # dit_attn_core (attn_core_kernel + attn_merge_kernel), hash over BF16_SOURCES
-    ("f26581d5c5880a72", "flux2048"): {"read_bytes": 1047.2e6, "write_bytes": 135.8e6,
+    ("fa548de7e9f15bb5", "flux2048"): {"read_bytes": 1051.6e6, "write_bytes": 135.8e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
     # dit_attn_core_fp8 (attn_core_fp8_kernel + attn_merge_kernel), hash over FP8_SOURCES
-    ("38ca761fa3fe4451", "flux2048_fp8"): {"read_bytes": 705.3e6, "write_bytes": 135.8e6,
+    ("1314fbfe7141ea8b", "flux2048_fp8"): {"read_bytes": 716.8e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
-    ("302d7d079501f519", "flux2048_qkv"): {"read_bytes": 585.1e6, "write_bytes": 311.4e6,
+    ("302d7d079501f519", "flux2048_qkv"): {"read_bytes": 575.7e6, "write_bytes": 311.4e6,
                                            "profile": "profiles/mxfp4_gemm_flux2048_qkv.md"},
     # residual_diff_partials + residual_diff_finish (hash over RESIDUAL_SOURCES)
     ("ab5d6a5aa3060f98", "flux2048_residual"): {"read_bytes": 207.80e6, "write_bytes": 0.26e6,
