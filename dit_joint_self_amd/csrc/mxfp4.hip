@@ -262,10 +262,16 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes, c
             sw_w[nb][0] = v.x;
             sw_w[nb][1] = v.y;
         }
-        // operand fragments of MFMA step s, read just before its MFMAs (fenced,
-        // so the compiler cannot hoist every read of the stage and run out of
-        // registers; the other wave of the SIMD covers the read latency.  Reading
-        // the next step's fragments ahead of the MFMAs measured slower.)
+        // Operand fragments: two sets, MFMA step s uses set s & 1.  Step s
+        // issues half of its MFMAs, then the reads of step s + 1's fragments,
+        // then its other half, so a read has half a step of MFMAs (and the
+        // other wave of the SIMD) to land, and the reads into a set issue after
+        // half a step of this wave's MFMAs (four; two in a 128-wide tile)
+        // behind the last MFMA that reads that set (fenced: the compiler may
+        // not hoist the reads further).  Reading them right before their own
+        // MFMAs was 2.4-3.5% slower; placing the reads after a quarter or
+        // three quarters of the MFMAs, or spreading them over the step, 7-22%
+        // slower.
         uint4 fa[2][2], fw[2][NB];
         auto read_frags = [&](int s, uint4 (&a)[2], uint4 (&w)[NB]) {
             const int c = 2 * s + hh;
@@ -274,9 +280,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes, c
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) w[nb] = t.w[swz(WCOLS * wn + 32 * nb + n_lane, c)];
         };
+        read_frags(0, fa[0], fw[0]);
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
-            read_frags(s, fa[s & 1], fw[s & 1]);
             __builtin_amdgcn_sched_barrier(0);
             // MFMA step s covers blocks 2 s and 2 s + 1: word s >> 1, bytes 2 (s & 1) + hh
             int sca[2], scw[NB];
@@ -285,7 +291,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes, c
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) scw[nb] = (int)(sw_w[nb][s >> 1] >> (8 * hh));
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < NB / 2; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+                    acc[nb][mb] = mfma_fp4(fw[s & 1][nb], fa[s & 1][mb], acc[nb][mb], scw[nb], sca[mb], 2 * (s & 1));
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < NSUB) read_frags(s + 1, fa[(s + 1) & 1], fw[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int nb = NB / 2; nb < NB; ++nb)
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
                     acc[nb][mb] = mfma_fp4(fw[s & 1][nb], fa[s & 1][mb], acc[nb][mb], scw[nb], sca[mb], 2 * (s & 1));
