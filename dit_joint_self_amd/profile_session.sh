@@ -39,7 +39,7 @@ run bench_qkv 300 python -u bench.py --workload flux2048_qkv --steps 20 --warmup
 run trace_qkv 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/trace_qkv -o run -- $B --workload flux2048_qkv --steps 20 --warmup 5
 pmc fetch_qkv FETCH_SIZE -- $B --workload flux2048_qkv $P
 pmc write_qkv WRITE_SIZE -- $B --workload flux2048_qkv $P
-pmc sq_qkv "SQ_BUSY_CYCLES SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_LDS GRBM_GUI_ACTIVE" -- $B --workload flux2048_qkv $P
+pmc sq_qkv "SQ_BUSY_CYCLES SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE" -- $B --workload flux2048_qkv $P
 run bench_residual 300 python -u bench.py --workload flux2048_residual --steps 20 --warmup 5 --cpu-seconds 10
 run trace_residual 300 rocprofv3 --kernel-trace --stats --output-format csv -d $O/trace_residual -o run -- $B --workload flux2048_residual --steps 20 --warmup 5
 pmc fetch_residual FETCH_SIZE -- $B --workload flux2048_residual $P
