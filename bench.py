@@ -43,7 +43,7 @@ MEASURED_TRAFFIC = {
     ("fa548de7e9f15bb5", "flux2048"): {"read_bytes": 1051.6e6, "write_bytes": 135.8e6,
                                        "profile": "profiles/attn_core_flux2048.md"},
     # dit_attn_core_fp8 (attn_core_fp8_kernel + attn_merge_kernel), hash over FP8_SOURCES
-    ("1314fbfe7141ea8b", "flux2048_fp8"): {"read_bytes": 716.8e6, "write_bytes": 135.8e6,
+    ("65b1ca7361f29fcd", "flux2048_fp8"): {"read_bytes": 707.0e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
     ("51deeab8a221c83f", "flux2048_qkv"): {"read_bytes": 511.3e6, "write_bytes": 330.3e6,
