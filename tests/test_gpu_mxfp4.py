@@ -177,3 +177,30 @@ def test_linear_full_size_bitwise_repeatable():
     b = dj.dit_mxfp4_linear(x, wc, ws)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 512, 256), (1, 8, 128)])
+def test_gemm_out_only_8byte_aligned(M, N, K):
+    """An output that starts 8 bytes past a 16-byte boundary (the interface
+    asks for 8-byte alignment) takes the 8-byte store path; N % 8 == 0, so an
+    aligned output of the same call takes the 16-byte one: both bit-identical
+    and within the gate."""
+    torch = _torch()
+    dj = _dj()
+    rng = np.random.default_rng(M + N + K)
+    ac, wc = rng.integers(0, 16, size=(M, K), dtype=np.uint8), rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    asc = rng.integers(120, 134, size=(M, K // 32), dtype=np.uint8)
+    wsc = rng.integers(120, 134, size=(N, K // 32), dtype=np.uint8)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    tiles = lambda sc: dev(dj.mxfp4_scales_to_tiles(sc))
+    args = (dev(_pack(ac)), tiles(asc), dev(_pack(wc)), tiles(wsc))
+    aligned = dj.dit_mxfp4_gemm(*args)
+    buf = torch.full((M * N + 8,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    assert buf.data_ptr() % 16 == 0
+    out8 = buf[4:4 + M * N].view(M, N)
+    assert out8.data_ptr() % 16 == 8
+    dj.dit_mxfp4_gemm(*args, out=out8)
+    torch.cuda.synchronize()
+    assert torch.equal(aligned.view(torch.int16), out8.view(torch.int16))
+    assert torch.isnan(buf[:4]).all() and torch.isnan(buf[4 + M * N:]).all()   # nothing written outside
+    _gate(from_device_bf16(aligned), mxfp4_dequantize(ac, asc), mxfp4_dequantize(wc, wsc), f"M={M} N={N} K={K}")
