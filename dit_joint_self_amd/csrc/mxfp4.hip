@@ -253,9 +253,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes, c
     auto compute = [&](const GStage& t, auto nsub_c, auto&& issue_copies) {
         constexpr int NSUB = decltype(nsub_c)::value;
         __builtin_amdgcn_sched_barrier(0);
-        // scale words: A rows (mb, word) and W rows (nb, word) of this lane
-        // row r's 8 bytes are half (r & 1) of 16-byte chunk r / 2; every row of
-        // this lane has the parity of n_lane
+        // scale words (mb, word) of this lane's A rows and (nb, word) of its W
+        // rows: the row's 8 scale bytes of the step, one 8-byte LDS read each
         uint32_t sa_w[2][2], sw_w[NB][2];
         const uint2* const sa8 = reinterpret_cast<const uint2*>(t.sa);
         const uint2* const sw8 = reinterpret_cast<const uint2*>(t.sw);
