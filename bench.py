@@ -46,7 +46,7 @@ MEASURED_TRAFFIC = {
     ("65b1ca7361f29fcd", "flux2048_fp8"): {"read_bytes": 707.0e6, "write_bytes": 135.8e6,
                                            "profile": "profiles/attn_core_fp8_flux2048.md"},
     # mxfp4_gemm_kernel alone (hash over MXFP4_SOURCES)
-    ("97884e7d7749a1ea", "flux2048_qkv"): {"read_bytes": 547.2e6, "write_bytes": 349.2e6,
+    ("3f50413424c15d89", "flux2048_qkv"): {"read_bytes": 547.2e6, "write_bytes": 349.2e6,
                                            "profile": "profiles/mxfp4_gemm_flux2048_qkv.md"},
     # residual_diff_partials + residual_diff_finish (hash over RESIDUAL_SOURCES)
     ("ab5d6a5aa3060f98", "flux2048_residual"): {"read_bytes": 207.80e6, "write_bytes": 0.26e6,

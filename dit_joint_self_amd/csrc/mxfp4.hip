@@ -118,8 +118,8 @@ constexpr int GK = 256;      // K per pipeline step: four 64-deep MFMA steps, 12
 constexpr int GWAVES = 8;    // wave (wm, wn) = (w & 3, w >> 2): 64 rows x 128 columns each
 constexpr int G_GROUP = 8;   // column tiles per group of the workgroup order
 // Scales of a step: 8 whole scale tiles (256 rows x 8 bytes) per operand, two
-// 1 KiB pieces each, copied by waves 0..3 (A: waves 0-1, W: waves 2-3; the W
-// part of a 128-wide tile is one piece, wave 2).
+// 1 KiB pieces each, copied by the step's four copying waves (A: the first
+// two, W: the other two; the W part of a 128-wide tile is one piece, the third).
 static_assert(GM == 256 && GN == 256 && GK == 256, "one scale tile column per step and 32-row tile");
 
 // LDS image of a tile: rows of GK/2 = 128 bytes = eight 16-byte chunks; chunk c
